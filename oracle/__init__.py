@@ -1,0 +1,154 @@
+"""CPU oracle for the top-k routed MoE SwiGLU FFN forward (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP path
+(``grouped_gemm_permute_amd``) and never imports it; both are fed by
+``moe_inputs``.
+
+Two independent evaluations are offered:
+
+* ``moe_oracle.c`` (through ctypes): fp64 loops.  ``forward_dense`` is the
+  brute force over every (token, choice); ``forward_permuted`` takes the
+  pages' order (counting sort, per-expert loop over sorted rows, unpermute,
+  combine in j order) and also returns the sorted-row intermediates h and Y.
+  ``permute`` is the stable counting sort with per-expert counts, offsets and
+  row-tile offsets.
+* ``brute.py``: a separate numpy fp64 brute force for tiny inputs.
+
+Definitions followed are cited in ``moe_oracle.c`` ("Triton MoE Kernels &
+Memory Checkpointing", Part A sections 2, 10.2, 10.3; "Chinchilla scaling,
+MoE, and fused Triton kernels", section "PyTorch MoE implementation").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-ffp-contract=off", "-pthread",
+                               "-std=c11", "-Wall", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        ci = ctypes.c_int
+        lib.moe_oracle_permute.restype = i64
+        lib.moe_oracle_permute.argtypes = [P, i64, ci, ci, i64, P, P, P, P, P]
+        lib.moe_oracle_forward_dense.restype = ci
+        lib.moe_oracle_forward_dense.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i64, ci, ci,
+                                                 P, i64, P, ci]
+        lib.moe_oracle_forward_permuted.restype = i64
+        lib.moe_oracle_forward_permuted.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i64, ci,
+                                                    ci, P, P, P, P, P, P, P, ci]
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def permute(topk_idx: np.ndarray, E: int, tile_rows: int = 1, shared_rows: int = 0) -> dict:
+    """Stable counting sort of slots s = t*k + j by expert id.
+
+    Returns counts [E], offsets [E+1], tile_off [E+2], perm [S], inv [S]
+    (int32) and ``bad``, the number of slots whose id is outside [0, E)."""
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32).reshape(-1)
+    S = idx.size
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    tile_off = np.empty(E + 2, np.int32)
+    perm = np.empty(max(S, 1), np.int32)
+    inv = np.empty(max(S, 1), np.int32)
+    bad = _load().moe_oracle_permute(_ptr(idx), S, E, tile_rows, shared_rows, _ptr(counts),
+                                     _ptr(offsets), _ptr(tile_off), _ptr(perm), _ptr(inv))
+    return dict(counts=counts, offsets=offsets, tile_off=tile_off, perm=perm[:S], inv=inv[:S],
+                bad=int(bad))
+
+
+def _shared(shared):
+    if shared is None:
+        return None, None, None
+    return tuple(_f64(a) for a in shared)
+
+
+def forward_dense(x, topk_idx, topk_w, W1, W3, W2, shared=None, tokens=None, nthreads=1):
+    """Path (i): y rows for ``tokens`` (all tokens when None), fp64."""
+    x = _f64(x)
+    T, D = x.shape
+    E, _, F = W1.shape
+    k = topk_idx.shape[1]
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    w = _f64(topk_w)
+    W1, W3, W2 = _f64(W1), _f64(W3), _f64(W2)
+    Ws1, Ws3, Ws2 = _shared(shared)
+    tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
+    n = T if tok is None else tok.size
+    y = np.empty((n, D), np.float64)
+    rc = _load().moe_oracle_forward_dense(_ptr(x), _ptr(idx), _ptr(w), _ptr(W1), _ptr(W3),
+                                          _ptr(W2), _ptr(Ws1), _ptr(Ws3), _ptr(Ws2), T, D, F, E,
+                                          k, _ptr(tok), n, _ptr(y), nthreads)
+    if rc != 0:
+        raise MemoryError("oracle allocation failed")
+    return y
+
+
+def forward_permuted(x, topk_idx, topk_w, W1, W3, W2, shared=None, nthreads=1) -> dict:
+    """Path (ii): returns y [T,D], the sorted-row intermediates h [R,F] and
+    Y [R,D] (R = T*k plus T shared rows), and counts/offsets/perm/inv."""
+    x = _f64(x)
+    T, D = x.shape
+    E, _, F = W1.shape
+    k = topk_idx.shape[1]
+    S = T * k
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    w = _f64(topk_w)
+    W1, W3, W2 = _f64(W1), _f64(W3), _f64(W2)
+    Ws1, Ws3, Ws2 = _shared(shared)
+    R = S + (T if Ws1 is not None else 0)
+    y = np.empty((T, D), np.float64)
+    h = np.empty((max(R, 1), F), np.float64)
+    Y = np.empty((max(R, 1), D), np.float64)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    perm = np.empty(max(S, 1), np.int32)
+    inv = np.empty(max(S, 1), np.int32)
+    bad = _load().moe_oracle_forward_permuted(
+        _ptr(x), _ptr(idx), _ptr(w), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1), _ptr(Ws3),
+        _ptr(Ws2), T, D, F, E, k, _ptr(y), _ptr(h), _ptr(Y), _ptr(counts), _ptr(offsets),
+        _ptr(perm), _ptr(inv), nthreads)
+    if bad < 0:
+        raise MemoryError("oracle allocation failed")
+    return dict(y=y, h=h[:R], Y=Y[:R], counts=counts, offsets=offsets, perm=perm[:S],
+                inv=inv[:S], bad=int(bad))
+
+
+def flops(T: int, D: int, F: int, k: int, shared: bool) -> int:
+    """Algorithmic FLOPs of one forward: 2 per multiply-add of the three
+    GEMMs (W1, W3: D x F each; W2: F x D) for every routed slot and, with a
+    shared expert, every token once more."""
+    return 6 * D * F * (T * k + (T if shared else 0))

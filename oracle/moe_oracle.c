@@ -1,0 +1,302 @@
+/*
+ * moe_oracle.c -- plain, slow, fp64 CPU oracle for the forward pass of a
+ * top-k routed mixture-of-experts SwiGLU feed-forward layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  It shares no
+ * code, header, table or constant with the HIP path, and the HIP path never
+ * calls it.
+ *
+ * What it computes (the plain definition; every sum runs in fp64 in
+ * ascending index order, no blocking, no fusion):
+ *
+ *   SwiGLU_e(v) = (silu(v . W1[e]) * (v . W3[e])) . W2[e],  silu(z) = z / (1 + exp(-z))
+ *   y[t] = [shared] SwiGLU_sh(x[t]) + sum_{j=0}^{k-1} w[t,j] * SwiGLU_{idx[t,j]}(x[t])
+ *
+ * Sources (pages as published on the web):
+ *  - "Triton MoE Kernels & Memory Checkpointing", Part A section 2: each
+ *    expert is the SwiGLU block W2(silu(W1 x) * W3 x), every token goes to its
+ *    top-2 of 8 routed experts plus one shared expert.
+ *  - same page, section 10.2 (the CPU reference): a loop over experts that
+ *    skips empty experts and evaluates each expert on its contiguous chunk
+ *    of sorted rows.
+ *  - same page, section 10.3 (the dispatch): flatten (token, choice) pairs
+ *    to slots, stable-argsort the slots by expert id, per-expert counts by
+ *    bincount and start offsets by cumulative sum; W2 per expert; scale by
+ *    the routing weight after W2 and add back into the token's row.
+ *  - "Chinchilla scaling, MoE, and fused Triton kernels", section "PyTorch
+ *    MoE implementation": slot order t*k + j (reshape(-1)), stable argsort,
+ *    bincount with minlength E, the inverse permutation inv[perm[p]] = p,
+ *    and the weighted sum over the k choices of each token.
+ *
+ * Readings where the pages are silent or garbled:
+ *  - weights are stored [E,D,F] for W1/W3 and [E,F,D] for W2, so the gate
+ *    pre-activation is the row vector x times W1[e];
+ *  - the activation is SwiGLU (silu of the W1 product times the W3 product);
+ *    the second page's "silu(h) * h" is taken as a garbled single-matrix form;
+ *  - the shared expert has weight 1 and the routing weights are used as given
+ *    (no renormalisation);
+ *  - combine order: start from the shared expert's row (or 0), then add
+ *    w[t,j] * Y_j for j = 0 .. k-1;
+ *  - an expert id outside [0, E) marks its slot invalid: the slot gets no
+ *    sorted position (inv = -1), is not counted and contributes nothing; the
+ *    function returns how many such slots it saw.
+ *
+ * Build: gcc -O2 -fPIC -shared -ffp-contract=off -pthread (no -ffast-math).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * Counting sort of the flattened slots by expert id (stable).
+ *   idx      [S]     expert id of slot s = t*k + j
+ *   counts   [E]     number of valid slots per expert
+ *   offsets  [E+1]   exclusive prefix sum of counts; offsets[E] = valid slots
+ *   tile_off [E+2]   prefix sum of ceil(count/BM) over the E routed groups
+ *                    followed by one shared group of shared_rows rows
+ *   perm     [S]     sorted position -> slot, ascending (expert, slot);
+ *                    positions >= offsets[E] are set to -1
+ *   inv      [S]     slot -> sorted position, -1 for invalid slots
+ * Returns the number of invalid slots.
+ */
+int64_t moe_oracle_permute(const int32_t *idx, int64_t S, int E, int BM, int64_t shared_rows,
+                           int32_t *counts, int32_t *offsets, int32_t *tile_off,
+                           int32_t *perm, int32_t *inv)
+{
+    int64_t bad = 0;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t s = 0; s < S; ++s) {
+        int32_t e = idx[s];
+        if (e >= 0 && e < E) counts[e] += 1;
+        else bad += 1;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+
+    tile_off[0] = 0;
+    for (int e = 0; e < E; ++e)
+        tile_off[e + 1] = tile_off[e] + (int32_t)((counts[e] + BM - 1) / BM);
+    tile_off[E + 1] = tile_off[E] + (int32_t)((shared_rows + BM - 1) / BM);
+
+    /* Stable by construction: experts in ascending order, and within one
+     * expert the slots in ascending order. */
+    for (int64_t s = 0; s < S; ++s) inv[s] = -1;
+    for (int64_t p = 0; p < S; ++p) perm[p] = -1;
+    int64_t pos = 0;
+    for (int e = 0; e < E; ++e)
+        for (int64_t s = 0; s < S; ++s)
+            if (idx[s] == e) {
+                perm[pos] = (int32_t)s;
+                inv[s] = (int32_t)pos;
+                ++pos;
+            }
+    return bad;
+}
+
+/*
+ * One expert on one row: out[D] = SwiGLU(xr) with W1,W3 [D,F] and W2 [F,D].
+ * h[F] receives silu(g)*u.  g and u are scratch of length F.
+ */
+static void swiglu_row(const double *xr, const double *W1, const double *W3, const double *W2,
+                       int64_t D, int64_t F, double *g, double *u, double *h, double *out)
+{
+    for (int64_t f = 0; f < F; ++f) { g[f] = 0.0; u[f] = 0.0; }
+    for (int64_t d = 0; d < D; ++d) {          /* g[f] = sum_d x[d] W1[d][f], d ascending */
+        const double xd = xr[d];
+        const double *w1 = W1 + d * F, *w3 = W3 + d * F;
+        for (int64_t f = 0; f < F; ++f) {
+            g[f] += xd * w1[f];
+            u[f] += xd * w3[f];
+        }
+    }
+    for (int64_t f = 0; f < F; ++f) h[f] = silu(g[f]) * u[f];
+    for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+    for (int64_t f = 0; f < F; ++f) {          /* out[d] = sum_f h[f] W2[f][d], f ascending */
+        const double hf = h[f];
+        const double *w2 = W2 + f * D;
+        for (int64_t d = 0; d < D; ++d) out[d] += hf * w2[d];
+    }
+}
+
+typedef struct {
+    /* problem */
+    const double *x, *w, *W1, *W3, *W2, *Ws1, *Ws3, *Ws2;
+    const int32_t *idx;
+    int64_t T, D, F;
+    int E, k;
+    /* dense path */
+    const int64_t *tokens;
+    int64_t ntok;
+    double *y;
+    /* permuted path */
+    const int32_t *perm, *offsets;
+    int64_t S;
+    double *h_out, *Y_out;     /* sorted-row results [S(+T), F] and [S(+T), D] */
+    /* work split */
+    int64_t lo, hi;
+    int status;
+} job_t;
+
+/* Path (i): every listed token evaluated directly through its experts. */
+static void *dense_worker(void *arg)
+{
+    job_t *J = (job_t *)arg;
+    const int64_t D = J->D, F = J->F;
+    double *g = malloc(sizeof(double) * F), *u = malloc(sizeof(double) * F);
+    double *h = malloc(sizeof(double) * F), *o = malloc(sizeof(double) * D);
+    if (!g || !u || !h || !o) { J->status = -1; goto done; }
+    for (int64_t i = J->lo; i < J->hi; ++i) {
+        const int64_t t = J->tokens ? J->tokens[i] : i;
+        const double *xr = J->x + t * D;
+        double *yr = J->y + i * D;
+        for (int64_t d = 0; d < D; ++d) yr[d] = 0.0;
+        if (J->Ws1) {
+            swiglu_row(xr, J->Ws1, J->Ws3, J->Ws2, D, F, g, u, h, o);
+            for (int64_t d = 0; d < D; ++d) yr[d] = o[d];
+        }
+        for (int j = 0; j < J->k; ++j) {
+            const int32_t e = J->idx[t * J->k + j];
+            if (e < 0 || e >= J->E) continue;
+            const double wt = J->w[t * J->k + j];
+            swiglu_row(xr, J->W1 + (int64_t)e * D * F, J->W3 + (int64_t)e * D * F,
+                       J->W2 + (int64_t)e * F * D, D, F, g, u, h, o);
+            for (int64_t d = 0; d < D; ++d) yr[d] = yr[d] + wt * o[d];
+        }
+    }
+done:
+    free(g); free(u); free(h); free(o);
+    return NULL;
+}
+
+static int run_jobs(job_t *base, int64_t n, int nthreads, void *(*fn)(void *))
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > n) nthreads = (int)(n > 0 ? n : 1);
+    job_t *jobs = calloc((size_t)nthreads, sizeof(job_t));
+    pthread_t *th = calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return -1; }
+    int status = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = *base;
+        jobs[i].lo = n * i / nthreads;
+        jobs[i].hi = n * (i + 1) / nthreads;
+        jobs[i].status = 0;
+        if (nthreads > 1) pthread_create(&th[i], NULL, fn, &jobs[i]);
+        else fn(&jobs[i]);
+    }
+    for (int i = 0; i < nthreads; ++i) {
+        if (nthreads > 1) pthread_join(th[i], NULL);
+        if (jobs[i].status) status = jobs[i].status;
+    }
+    free(jobs); free(th);
+    return status;
+}
+
+/*
+ * Path (i), dense brute force.  For each of the ntok listed tokens (or all T
+ * when tokens == NULL, ntok = T) y[i] = shared + sum_j w * SwiGLU_e(x[t]).
+ * Ws1/Ws3/Ws2 NULL means no shared expert.  Returns 0, or -1 on allocation
+ * failure.
+ */
+int moe_oracle_forward_dense(const double *x, const int32_t *idx, const double *w,
+                             const double *W1, const double *W3, const double *W2,
+                             const double *Ws1, const double *Ws3, const double *Ws2,
+                             int64_t T, int64_t D, int64_t F, int E, int k,
+                             const int64_t *tokens, int64_t ntok, double *y, int nthreads)
+{
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.x = x; J.idx = idx; J.w = w; J.W1 = W1; J.W3 = W3; J.W2 = W2;
+    J.Ws1 = Ws1; J.Ws3 = Ws3; J.Ws2 = Ws2;
+    J.T = T; J.D = D; J.F = F; J.E = E; J.k = k;
+    J.tokens = tokens; J.ntok = tokens ? ntok : T; J.y = y;
+    return run_jobs(&J, J.ntok, nthreads, dense_worker);
+}
+
+/* Path (ii) stage: evaluate sorted rows [lo, hi) of the routed-plus-shared
+ * row space.  Row p < S belongs to expert e with offsets[e] <= p <
+ * offsets[e+1] and reads token perm[p] / k; row S + t is the shared expert on
+ * token t. */
+static void *sorted_worker(void *arg)
+{
+    job_t *J = (job_t *)arg;
+    const int64_t D = J->D, F = J->F;
+    double *g = malloc(sizeof(double) * F), *u = malloc(sizeof(double) * F);
+    if (!g || !u) { J->status = -1; goto done; }
+    for (int64_t p = J->lo; p < J->hi; ++p) {
+        const double *A1, *A3, *A2;
+        int64_t t;
+        if (p < J->S) {
+            if (p >= J->offsets[J->E]) continue;          /* unused (invalid slots) */
+            int e = 0;
+            while (!(p < J->offsets[e + 1])) ++e;          /* the expert whose chunk holds p */
+            A1 = J->W1 + (int64_t)e * D * F;
+            A3 = J->W3 + (int64_t)e * D * F;
+            A2 = J->W2 + (int64_t)e * F * D;
+            t = J->perm[p] / J->k;
+        } else {
+            A1 = J->Ws1; A3 = J->Ws3; A2 = J->Ws2;
+            t = p - J->S;
+        }
+        swiglu_row(J->x + t * D, A1, A3, A2, D, F, g, u, J->h_out + p * F, J->Y_out + p * D);
+    }
+done:
+    free(g); free(u);
+    return NULL;
+}
+
+/*
+ * Path (ii), the permuted evaluation in the pages' order: counting sort,
+ * per-expert loop over sorted rows (empty experts do nothing), shared rows
+ * appended after the S routed rows, then unpermute through inv and combine
+ * in j order.  h_out [S + T*sh, F] and Y_out [S + T*sh, D] receive every
+ * sorted row's h and W2 output (rows of invalid slots are left as zero).
+ * perm/inv/counts/offsets are written to the caller's arrays
+ * (sizes S, S, E, E+1).  Returns the number of invalid slots, or -1 on
+ * allocation failure.
+ */
+int64_t moe_oracle_forward_permuted(const double *x, const int32_t *idx, const double *w,
+                                    const double *W1, const double *W3, const double *W2,
+                                    const double *Ws1, const double *Ws3, const double *Ws2,
+                                    int64_t T, int64_t D, int64_t F, int E, int k,
+                                    double *y, double *h_out, double *Y_out,
+                                    int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                                    int nthreads)
+{
+    const int64_t S = T * k;
+    const int has_sh = Ws1 != NULL;
+    const int64_t rows = S + (has_sh ? T : 0);
+    int32_t *tile_off = malloc(sizeof(int32_t) * (size_t)(E + 2));
+    if (!tile_off) return -1;
+    const int64_t bad = moe_oracle_permute(idx, S, E, 1, has_sh ? T : 0, counts, offsets,
+                                           tile_off, perm, inv);
+    free(tile_off);
+    memset(h_out, 0, sizeof(double) * (size_t)(rows * F));
+    memset(Y_out, 0, sizeof(double) * (size_t)(rows * D));
+
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.x = x; J.idx = idx; J.w = w; J.W1 = W1; J.W3 = W3; J.W2 = W2;
+    J.Ws1 = Ws1; J.Ws3 = Ws3; J.Ws2 = Ws2;
+    J.T = T; J.D = D; J.F = F; J.E = E; J.k = k;
+    J.perm = perm; J.offsets = offsets; J.S = S; J.h_out = h_out; J.Y_out = Y_out;
+    if (run_jobs(&J, rows, nthreads, sorted_worker)) return -1;
+
+    /* Unpermute and combine: y[t] = Ysh[t] + sum_j w[t,j] * Y[inv[t*k+j]]. */
+    for (int64_t t = 0; t < T; ++t) {
+        double *yr = y + t * D;
+        for (int64_t d = 0; d < D; ++d) yr[d] = has_sh ? Y_out[(S + t) * D + d] : 0.0;
+        for (int j = 0; j < k; ++j) {
+            const int32_t p = inv[t * k + j];
+            if (p < 0) continue;
+            const double wt = w[t * k + j];
+            for (int64_t d = 0; d < D; ++d) yr[d] = yr[d] + wt * Y_out[(int64_t)p * D + d];
+        }
+    }
+    return bad;
+}
