@@ -1,0 +1,274 @@
+#!/usr/bin/env python
+"""Benchmark of the MoE SwiGLU FFN forward on one MI355X.
+
+One step = one moe_ffn_forward call (permute, up+SwiGLU grouped GEMM, down
+grouped GEMM, combine) over one batch of seeded synthetic input already
+resident in HBM.  The default workload is the full-step layer: T = 32768
+tokens (8 x 4096), d_model 768, d_ff 1536, 8 routed experts top-2 with
+Zipf(1.2)-skewed routing, plus a shared expert, bf16 storage with fp32
+accumulation.  Inputs and weights are rotated over enough copies that the
+working set exceeds the on-die caches (MALL + L2), so each step streams from
+HBM.
+
+Prints one JSON line:
+  value       whole-forward TFLOP/s (algorithmic FLOPs 6*D*F*(T*k + T) / time)
+  roofline    the dominant kernel's achieved rate vs the MI355X peak, from
+              HIP events recorded between the kernels on their stream during
+              the timed loop (traffic: HBM bytes from rocprofv3 counters,
+              when a counter summary for the current kernel source exists)
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE FFN fwd TFLOP/s + % bf16 MFMA peak, 32k tok D768 F1536 E8 top-2"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+STAGES = ("permute", "up_swiglu", "down", "combine")
+KERNEL_SOURCES = {             # the source each stage's kernel is built from
+    "permute": "grouped_gemm_permute_amd/csrc/permute.hip",
+    "up_swiglu": "grouped_gemm_permute_amd/csrc/gemm_bf16.hip",
+    "down": "grouped_gemm_permute_amd/csrc/gemm_bf16.hip",
+    "combine": "grouped_gemm_permute_amd/csrc/combine.hip",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(stage: str) -> str:
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[stage], "grouped_gemm_permute_amd/csrc/moe_internal.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = ev.value
+        return arr
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, arr):
+        for ev in arr:
+            self.hip.hipEventDestroy(ev)
+
+
+def stage_work(w, counts):
+    """Algorithmic FLOPs and compulsory bytes (each operand read once, each
+    result written once) of one launch of every stage.  b = 2 (bf16)."""
+    b = 2 if w.dtype == "bf16" else 4
+    rows = w.T * w.k + (w.T if w.shared else 0)
+    groups = int(sum(1 for c in counts if c > 0)) + (1 if w.shared else 0)
+    wbytes = w.D * w.F * b
+    return {
+        "permute": {"flop": 0, "bytes": w.T * w.k * 4 * 3 + 4 * (3 * w.E + 3)},
+        "up_swiglu": {"flop": 4 * w.D * w.F * rows,
+                      "bytes": w.T * w.D * b + 2 * wbytes * groups + rows * w.F * b},
+        "down": {"flop": 2 * w.D * w.F * rows,
+                 "bytes": rows * w.F * b + wbytes * groups + rows * w.D * 4},
+        "combine": {"flop": 2 * w.k * w.D * w.T,
+                    "bytes": rows * w.D * 4 + w.T * w.k * 8 + w.T * w.D * b},
+    }
+
+
+def path_bytes(w, counts):
+    """Bytes the whole forward must move: x, y, routing, and the three weight
+    matrices of every active expert (intermediates excluded)."""
+    b = 2 if w.dtype == "bf16" else 4
+    groups = int(sum(1 for c in counts if c > 0)) + (1 if w.shared else 0)
+    return 2 * w.T * w.D * b + w.T * w.k * 8 + 3 * w.D * w.F * b * groups
+
+
+def load_traffic(workload_name, stage):
+    """Counter-derived HBM bytes per launch, if profiles/ holds a summary
+    taken from the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(workload_name, {}).get(stage)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_hash(stage):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, w, target_s):
+    import numpy as np
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    shared = (inp["Ws1"], inp["Ws3"], inp["Ws2"]) if w.shared else None
+    W = [np.ascontiguousarray(inp[n], np.float64) for n in ("W1", "W3", "W2")]
+    sh = tuple(np.ascontiguousarray(a, np.float64) for a in shared) if shared else None
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.forward_permuted(inp["x"][:n], inp["topk_idx"][:n], inp["topk_w"][:n], *W, sh,
+                                nthreads=threads)
+        return time.perf_counter() - t0
+
+    n0 = min(w.T, 8 * threads)
+    t0 = run(n0)
+    n = int(min(w.T, max(n0, target_s / max(t0, 1e-6) * n0)))
+    t = run(n)
+    flop = 6 * w.D * w.F * (n * w.k + (n if w.shared else 0))
+    return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(t, 3),
+            "sample": f"first {n} of {w.T} tokens of the same workload (same weights and routing), "
+                      f"fp64 permuted oracle path, {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, help="index into moe_inputs.WORKLOADS")
+    ap.add_argument("--variant", default="unfused", choices=("unfused", "fused"))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target length of the CPU-oracle baseline sample; 0 skips it")
+    ap.add_argument("--rotate-bytes", type=float, default=512e6,
+                    help="rotate input copies until their total exceeds this many bytes")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this path has no multi-GPU implementation); "
+              f"got --gpus {args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import grouped_gemm_permute_amd as gg
+    import moe_inputs
+
+    w = moe_inputs.WORKLOADS[args.workload]
+    log(f"workload {w.name}: drawing inputs")
+    inp = moe_inputs.make_inputs(args.workload)
+    counts = np.bincount(inp["topk_idx"].reshape(-1), minlength=w.E)
+    torch.cuda.set_device(0)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(inp[name]).cuda()
+
+    base = {n: dev(n) for n in ("x", "W1", "W3", "W2")}
+    if w.shared:
+        base.update({n: dev(n) for n in ("Ws1", "Ws3", "Ws2")})
+    base["idx"] = torch.from_numpy(inp["topk_idx"]).cuda()
+    base["w"] = torch.from_numpy(inp["topk_w"]).cuda()
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    R = max(2, math.ceil(args.rotate_bytes / set_bytes))
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(R - 1)]
+    ws = gg.alloc_workspace(w.T, w.D, w.F, w.E, w.k, w.shared, dt, args.variant)
+    y = torch.empty((w.T, w.D), dtype=dt, device="cuda")
+    log(f"{R} rotated input sets of {set_bytes / 1e6:.1f} MB; workspace {ws.numel() / 1e6:.1f} MB")
+
+    def step(i, events=None):
+        s = sets[i % R]
+        sh = (s["Ws1"], s["Ws3"], s["Ws2"]) if w.shared else None
+        gg.forward(s["x"], s["idx"], s["w"], s["W1"], s["W3"], s["W2"], sh, y=y,
+                   variant=args.variant, workspace=ws, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    hip = HipEvents()
+    evs = [hip.create(5) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {st: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs]))
+                for j, st in enumerate(STAGES)}
+    fwd_ms = float(np.mean([hip.elapsed_ms(e[0], e[4]) for e in evs]))
+    for e in evs:
+        hip.destroy(e)
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (host clock), "
+        f"{fwd_ms:.4f} ms/step (events); stages {stage_ms}")
+
+    flop = w.flops()
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    work = stage_work(w, counts)
+    dom = max(("up_swiglu", "down"), key=lambda s: stage_ms[s])
+    sec = stage_ms[dom] * 1e-3
+    mfma_bound = work[dom]["flop"] / work[dom]["bytes"] > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3
+    if mfma_bound:
+        ach = work[dom]["flop"] / sec / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    else:
+        ach = work[dom]["bytes"] / sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = load_traffic(w.name, dom)
+    roof["kernel"] = dom
+    roof["launch_ms"] = round(stage_ms[dom], 5)
+    roof["algorithmic"] = work[dom]["flop"] if mfma_bound else work[dom]["bytes"]
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("timing the CPU oracle baseline")
+        cpu = cpu_baseline(inp, w, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "F": w.F, "E": w.E, "k": w.k,
+                   "shared_expert": w.shared, "routing": w.routing, "variant": args.variant,
+                   "rotated_sets": R},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "hbm_gbs_path": round(path_bytes(w, counts) / (ms_per_step * 1e-3) / 1e9, 1),
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "expert_rows": counts.tolist(),
+        "input_sha256": moe_inputs.input_digest(inp),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,94 @@
+// gemm_f32.hip -- fp32 grouped expert GEMMs (plain fp32 FMA, one thread per
+// output element).  The fp32 dtype exists for exact-arithmetic checks on
+// small problems; fp32 inputs are never rounded to a lower precision (the
+// same rule as the IEEE-fp32 dot of "Triton MoE Kernels & Memory
+// Checkpointing", Part A section 5.1).
+//
+//   up:   h[p][n] = silu(sum_d x[tok(p)][d] W1[g][d][n]) * sum_d x[tok(p)][d] W3[g][d][n]
+//   down: Y[p][n] = sum_f h[p][f] W2[g][f][n]
+//
+// Row p < offsets[E] belongs to routed expert g (offsets[g] <= p <
+// offsets[g+1]) and reads token perm[p] / k; row S + t is the shared expert
+// on token t; rows in [offsets[E], S) (left by invalid ids) are skipped.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int NT = 128;
+
+// Group of row p, or -1 for an unused row.  Shared rows return E.
+__device__ __forceinline__ int row_group(const GroupArgs& g, int64_t p) {
+    if (p >= g.S) return g.E;
+    if (p >= g.offsets[g.E]) return -1;
+    int lo = 0, hi = g.E - 1;
+    while (lo < hi) {                   // largest e with offsets[e] <= p
+        const int mid = (lo + hi + 1) >> 1;
+        if (g.offsets[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(NT) void up_swiglu_f32_kernel(GroupArgs g, const float* __restrict__ x,
+                                                          const float* __restrict__ W1,
+                                                          const float* __restrict__ W3,
+                                                          const float* __restrict__ Ws1,
+                                                          const float* __restrict__ Ws3,
+                                                          float* __restrict__ h, int D, int F) {
+    const int64_t p = blockIdx.x;
+    const int n = blockIdx.y * NT + threadIdx.x;
+    if (n >= F) return;
+    const int grp = row_group(g, p);
+    if (grp < 0) return;
+    const float *w1, *w3;
+    int64_t tok;
+    if (grp == g.E) {
+        w1 = Ws1; w3 = Ws3; tok = p - g.S;
+    } else {
+        w1 = W1 + (int64_t)grp * D * F; w3 = W3 + (int64_t)grp * D * F; tok = g.perm[p] / g.k;
+    }
+    const float* xr = x + tok * D;
+    float gs = 0.f, us = 0.f;
+    for (int d = 0; d < D; ++d) {
+        gs = fmaf(xr[d], w1[(int64_t)d * F + n], gs);
+        us = fmaf(xr[d], w3[(int64_t)d * F + n], us);
+    }
+    h[p * F + n] = gs / (1.0f + expf(-gs)) * us;
+}
+
+__global__ __launch_bounds__(NT) void down_f32_kernel(GroupArgs g, const float* __restrict__ h,
+                                                     const float* __restrict__ W2,
+                                                     const float* __restrict__ Ws2,
+                                                     float* __restrict__ Y, int D, int F) {
+    const int64_t p = blockIdx.x;
+    const int n = blockIdx.y * NT + threadIdx.x;
+    if (n >= D) return;
+    const int grp = row_group(g, p);
+    if (grp < 0) return;
+    const float* w2 = grp == g.E ? Ws2 : W2 + (int64_t)grp * F * D;
+    const float* hr = h + p * F;
+    float acc = 0.f;
+    for (int f = 0; f < F; ++f) acc = fmaf(hr[f], w2[(int64_t)f * D + n], acc);
+    Y[p * D + n] = acc;
+}
+
+int64_t rows_of(const GroupArgs& g) { return g.S + (g.G > g.E ? g.T : 0); }
+
+}  // namespace
+
+hipError_t launch_up_swiglu_f32(const GroupArgs& g, const float* x, const float* W1,
+                                const float* W3, const float* Ws1, const float* Ws3, float* h,
+                                int D, int F, hipStream_t s) {
+    const dim3 grid((unsigned)rows_of(g), (unsigned)((F + NT - 1) / NT));
+    up_swiglu_f32_kernel<<<grid, NT, 0, s>>>(g, x, W1, W3, Ws1, Ws3, h, D, F);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_f32(const GroupArgs& g, const float* h, const float* W2, const float* Ws2,
+                           float* Y, int D, int F, hipStream_t s) {
+    const dim3 grid((unsigned)rows_of(g), (unsigned)((D + NT - 1) / NT));
+    down_f32_kernel<<<grid, NT, 0, s>>>(g, h, W2, Ws2, Y, D, F);
+    return hipGetLastError();
+}
+
+}  // namespace moe

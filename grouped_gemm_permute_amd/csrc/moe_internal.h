@@ -1,0 +1,58 @@
+// moe_internal.h -- launchers shared between the translation units of
+// libmoe_ffn.so.  Not part of the public ABI (include/moe_ffn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Slot blocks of the multi-block permute; a single workgroup handles
+// T*k <= kPermuteSingleMax.
+constexpr int kPermuteBlockSlots = 2048;
+constexpr int64_t kPermuteSingleMax = 4096;
+constexpr int kMaxExperts = 1024;
+
+inline int permute_hist_blocks(int64_t S) {
+    return S <= kPermuteSingleMax ? 0 : (int)((S + kPermuteBlockSlots - 1) / kPermuteBlockSlots);
+}
+
+// Stable counting sort of slots by expert (see moe_expert_permute).
+// hist: int32 [(E+1) * nblocks] when nblocks > 0.
+hipError_t launch_permute(const int32_t* idx, int64_t S, int E, int tile_rows, int64_t shared_rows,
+                          int32_t* counts, int32_t* offsets, int32_t* tile_off, int32_t* perm,
+                          int32_t* inv, int32_t* err, int32_t* hist, int nblocks, hipStream_t s);
+
+// Everything the grouped GEMMs read about the routed groups.
+struct GroupArgs {
+    const int32_t* offsets;   // [E+1] routed row starts
+    const int32_t* tile_off;  // [G+1] row-tile prefix, G = E + has_shared
+    const int32_t* perm;      // [S] sorted row -> slot
+    int64_t S;                // T*k: first shared row
+    int64_t T;
+    int E;
+    int k;
+    int G;                    // E + has_shared
+};
+
+// bf16 MFMA grouped GEMMs.
+constexpr int kBf16TileRows = 256;
+hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
+                                 const void* Ws1, const void* Ws3, void* h, int D, int F,
+                                 hipStream_t s);
+hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
+                            float* Y, int D, int F, hipStream_t s);
+
+// fp32 grouped GEMMs (plain fp32 FMA; correctness-first path).
+constexpr int kF32TileRows = 64;
+hipError_t launch_up_swiglu_f32(const GroupArgs& g, const float* x, const float* W1,
+                                const float* W3, const float* Ws1, const float* Ws3, float* h,
+                                int D, int F, hipStream_t s);
+hipError_t launch_down_f32(const GroupArgs& g, const float* h, const float* W2, const float* Ws2,
+                           float* Y, int D, int F, hipStream_t s);
+
+// y[t] = Ysh[t] + sum_j w[t,j] * Y[inv[t*k+j]], rounded once.
+hipError_t launch_combine(const float* Y, const int32_t* inv, const float* w, void* y, int64_t T,
+                          int D, int k, bool has_shared, bool out_bf16, hipStream_t s);
+
+}  // namespace moe

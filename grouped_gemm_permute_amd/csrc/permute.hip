@@ -1,0 +1,210 @@
+// permute.hip -- expert_permute: stable counting sort of the flattened
+// (token, choice) slots by expert id.
+//
+// The dispatch of "Triton MoE Kernels & Memory Checkpointing" (Part A,
+// section 10.3, steps 1-2) flattens the router's top-k ids to slots,
+// stable-argsorts them by expert so each expert's rows are contiguous, and
+// takes per-expert counts (bincount) and start offsets (cumulative sum);
+// "Chinchilla scaling, MoE, and fused Triton kernels" (section "PyTorch MoE
+// implementation") adds the inverse permutation used by the combine.  Here
+// the argsort is a counting sort, which yields the same unique stable order:
+//
+//   histogram   counts[e] = #{s : idx[s] == e}      (order-free, LDS atomics)
+//   scan        offsets = exclusive prefix of counts; tile_off = prefix of
+//               ceil(counts/tile_rows) plus one shared group
+//   scatter     perm[offsets[e] + #{s' < s : idx[s'] == e}] = s, inv[s] = that
+//
+// The in-order rank #{s' < s : idx[s'] == e} never depends on atomic timing:
+// inside a wavefront it is the popcount of the lanes below with the same key
+// (found with one ballot per key bit), across wavefronts and slot blocks it
+// is a prefix sum in (expert, block) order.
+//
+// Small problems run as one workgroup; larger ones as three launches
+// (per-block histograms, one scan workgroup, per-block scatter).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kSingleThreads = 512;
+constexpr int kScatterThreads = 256;
+constexpr int kScanThreads = 1024;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Lanes of this wavefront whose key equals this lane's key.  Every lane of
+// the wavefront must call it.  Keys are in [0, 2^nbits).
+__device__ __forceinline__ uint64_t match_peers(int key, int nbits) {
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+        const int bit = (key >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    return peers;
+}
+
+__device__ __forceinline__ int key_of(const int32_t* idx, int64_t s, int64_t S, int E) {
+    if (s >= S) return E + 1;                        // past the end: no slot
+    const int32_t e = idx[s];
+    return (e >= 0 && e < E) ? e : E;                // E: invalid id
+}
+
+// Serial prefix sums by one thread: counts/offsets/tile_off/err from cnt[0..E].
+__device__ void finish_scan(const int32_t* cnt, int E, int tile_rows, int64_t shared_rows,
+                            int32_t* counts, int32_t* offsets, int32_t* tile_off, int32_t* err,
+                            int32_t* run) {
+    int32_t acc = 0, tiles = 0;
+    for (int e = 0; e < E; ++e) {
+        const int32_t c = cnt[e];
+        counts[e] = c;
+        offsets[e] = acc;
+        tile_off[e] = tiles;
+        if (run) run[e] = acc;
+        acc += c;
+        tiles += (c + tile_rows - 1) / tile_rows;
+    }
+    offsets[E] = acc;
+    tile_off[E] = tiles;
+    tile_off[E + 1] = tiles + (int32_t)((shared_rows + tile_rows - 1) / tile_rows);
+    err[0] = cnt[E];
+}
+
+// Rank the slots [c0, c0 + blockDim) of one chunk and scatter them.
+// run[e]: next free position of expert e; wcnt [nwaves][E] zeroed on entry
+// and on exit.
+// Slots at or past `end` are not part of this chunk; S bounds every write.
+template <int NT>
+__device__ void scatter_chunk(const int32_t* idx, int64_t c0, int64_t end, int64_t S, int E,
+                              int nbits, int32_t* run, int32_t* wcnt, int32_t* perm, int32_t* inv) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
+    const int64_t s = c0 + tid;
+    const int key = key_of(idx, s, end, E);
+    const uint64_t peers = match_peers(key, nbits);
+    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    if (rank == 0 && key < E) wcnt[wave * E + key] = __popcll(peers);
+    __syncthreads();
+    if (key < E) {
+        int32_t pos = run[key] + rank;
+        for (int w = 0; w < wave; ++w) pos += wcnt[w * E + key];
+        if (pos >= 0 && pos < S) {     // always true for a consistent histogram
+            perm[pos] = (int32_t)s;
+            inv[s] = pos;
+        }
+    } else if (s < end) {
+        inv[s] = -1;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += NT) {
+        int32_t tot = 0;
+        for (int w = 0; w < NW; ++w) {
+            tot += wcnt[w * E + e];
+            wcnt[w * E + e] = 0;
+        }
+        run[e] += tot;
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ int key_bits(int E) { return 32 - __clz(E + 1); }
+
+__global__ __launch_bounds__(kSingleThreads) void permute_single_kernel(
+    const int32_t* __restrict__ idx, int64_t S, int E, int tile_rows, int64_t shared_rows,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ err) {
+    __shared__ int32_t cnt[kMaxExperts + 1];
+    __shared__ int32_t run[kMaxExperts];
+    __shared__ int32_t wcnt[(kSingleThreads / 64) * kMaxExperts];
+    const int tid = threadIdx.x;
+    for (int e = tid; e <= E; e += kSingleThreads) cnt[e] = 0;
+    for (int i = tid; i < (kSingleThreads / 64) * E; i += kSingleThreads) wcnt[i] = 0;
+    __syncthreads();
+    for (int64_t s = tid; s < S; s += kSingleThreads) atomicAdd(&cnt[key_of(idx, s, S, E)], 1);
+    __syncthreads();
+    if (tid == 0) finish_scan(cnt, E, tile_rows, shared_rows, counts, offsets, tile_off, err, run);
+    __syncthreads();
+    const int nbits = key_bits(E);
+    for (int64_t c0 = 0; c0 < S; c0 += kSingleThreads)
+        scatter_chunk<kSingleThreads>(idx, c0, S, S, E, nbits, run, wcnt, perm, inv);
+    const int32_t valid = (int32_t)(S - cnt[E]);
+    for (int64_t p = valid + tid; p < S; p += kSingleThreads) perm[p] = -1;
+}
+
+// hist[e * nb + b] = slots of block b with key e (e == E: invalid ids).
+__global__ __launch_bounds__(kScatterThreads) void permute_hist_kernel(
+    const int32_t* __restrict__ idx, int64_t S, int E, int32_t* __restrict__ hist) {
+    __shared__ int32_t cnt[kMaxExperts + 1];
+    const int tid = threadIdx.x, b = blockIdx.x, nb = gridDim.x;
+    for (int e = tid; e <= E; e += kScatterThreads) cnt[e] = 0;
+    __syncthreads();
+    const int64_t lo = (int64_t)b * kPermuteBlockSlots;
+    const int64_t hi = min(S, lo + kPermuteBlockSlots);
+    for (int64_t s = lo + tid; s < hi; s += kScatterThreads) atomicAdd(&cnt[key_of(idx, s, S, E)], 1);
+    __syncthreads();
+    for (int e = tid; e <= E; e += kScatterThreads) hist[(int64_t)e * nb + b] = cnt[e];
+}
+
+// Turns hist into per-(expert, block) start positions and writes the
+// per-expert results.
+__global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
+    int32_t* __restrict__ hist, int nb, int64_t S, int E, int tile_rows, int64_t shared_rows,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ perm, int32_t* __restrict__ err) {
+    __shared__ int32_t cnt[kMaxExperts + 1];
+    __shared__ int32_t start[kMaxExperts];
+    const int tid = threadIdx.x;
+    for (int e = tid; e <= E; e += kScanThreads) {
+        int32_t sum = 0;
+        for (int b = 0; b < nb; ++b) {
+            const int32_t v = hist[(int64_t)e * nb + b];
+            hist[(int64_t)e * nb + b] = sum;
+            sum += v;
+        }
+        cnt[e] = sum;
+    }
+    __syncthreads();
+    if (tid == 0) finish_scan(cnt, E, tile_rows, shared_rows, counts, offsets, tile_off, err, start);
+    __syncthreads();
+    for (int e = tid; e < E; e += kScanThreads) {
+        const int32_t base = start[e];
+        for (int b = 0; b < nb; ++b) hist[(int64_t)e * nb + b] += base;
+    }
+    const int32_t valid = (int32_t)(S - cnt[E]);
+    for (int64_t p = valid + tid; p < S; p += kScanThreads) perm[p] = -1;
+}
+
+__global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
+    const int32_t* __restrict__ idx, int64_t S, int E, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    __shared__ int32_t run[kMaxExperts];
+    __shared__ int32_t wcnt[(kScatterThreads / 64) * kMaxExperts];
+    const int tid = threadIdx.x, b = blockIdx.x, nb = gridDim.x;
+    for (int e = tid; e < E; e += kScatterThreads) run[e] = hist[(int64_t)e * nb + b];
+    for (int i = tid; i < (kScatterThreads / 64) * E; i += kScatterThreads) wcnt[i] = 0;
+    __syncthreads();
+    const int nbits = key_bits(E);
+    const int64_t lo = (int64_t)b * kPermuteBlockSlots;
+    const int64_t hi = min(S, lo + kPermuteBlockSlots);
+    for (int64_t c0 = lo; c0 < hi; c0 += kScatterThreads)
+        scatter_chunk<kScatterThreads>(idx, c0, hi, S, E, nbits, run, wcnt, perm, inv);
+}
+
+}  // namespace
+
+hipError_t launch_permute(const int32_t* idx, int64_t S, int E, int tile_rows, int64_t shared_rows,
+                          int32_t* counts, int32_t* offsets, int32_t* tile_off, int32_t* perm,
+                          int32_t* inv, int32_t* err, int32_t* hist, int nblocks, hipStream_t s) {
+    if (nblocks == 0) {
+        permute_single_kernel<<<1, kSingleThreads, 0, s>>>(idx, S, E, tile_rows, shared_rows, counts,
+                                                           offsets, tile_off, perm, inv, err);
+        return hipGetLastError();
+    }
+    permute_hist_kernel<<<nblocks, kScatterThreads, 0, s>>>(idx, S, E, hist);
+    permute_scan_kernel<<<1, kScanThreads, 0, s>>>(hist, nblocks, S, E, tile_rows, shared_rows,
+                                                   counts, offsets, tile_off, perm, err);
+    permute_scatter_kernel<<<nblocks, kScatterThreads, 0, s>>>(idx, S, E, hist, perm, inv);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,192 @@
+/*
+ * moe_ffn.h -- C ABI of the MI355X (gfx950) top-k routed mixture-of-experts
+ * SwiGLU feed-forward forward pass.
+ *
+ * The layer (one token t, k routed choices, optional always-on shared expert):
+ *
+ *   SwiGLU_e(v) = (silu(v . W1[e]) * (v . W3[e])) . W2[e],   silu(z) = z / (1 + exp(-z))
+ *   y[t] = [shared] SwiGLU_sh(x[t]) + sum_{j=0}^{k-1} topk_w[t,j] * SwiGLU_{topk_idx[t,j]}(x[t])
+ *
+ * The expert is the SwiGLU block W2(silu(W1 x) * W3 x) with top-2-of-8
+ * routing plus a shared expert ("Triton MoE Kernels & Memory
+ * Checkpointing", Part A section 2); tokens are grouped by expert through a
+ * stable sort of the flattened (token, choice) slots with per-expert counts
+ * and start offsets (same page, section 10.3; "Chinchilla scaling, MoE, and
+ * fused Triton kernels", section "PyTorch MoE implementation"), the experts
+ * run as grouped matrix products, and the outputs are unpermuted and summed
+ * with the routing weights (both pages, same sections).
+ *
+ * Conventions shared by every entry point:
+ *  - The caller owns every buffer.  All data pointers are device pointers
+ *    (HIP device memory of the current device); the library never allocates
+ *    or frees memory.
+ *  - Tensors are dense, row-major, with no padding between rows.
+ *  - Work is enqueued on `stream` in order and returns without waiting for
+ *    the device (no host synchronisation), except moe_ffn_get_device_error.
+ *  - Argument errors are detected on the host before anything is enqueued;
+ *    in that case nothing is launched and the outputs are untouched.
+ *  - The library never falls back to a different algorithm or precision: a
+ *    shape or variant it does not implement returns MOE_ERR_UNSUPPORTED.
+ *  - Expert ids outside [0, E) are detected on the device: such a slot takes
+ *    no sorted position (inv = -1), contributes nothing to y, and is counted
+ *    in a flag that moe_ffn_get_device_error reads back.
+ *  - Calls that share a workspace must not overlap in time (same stream, or
+ *    ordered by events).
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, k > E, unknown enum */
+    MOE_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. D % 64 != 0 for bf16) */
+    MOE_ERR_WORKSPACE = 3,     /* ws_bytes smaller than moe_ffn_workspace_size() */
+    MOE_ERR_HIP = 4            /* a HIP launch or copy reported an error */
+} moe_status;
+
+typedef enum moe_dtype {
+    MOE_F32 = 0,               /* x, weights, y in fp32; fp32 arithmetic throughout */
+    MOE_BF16 = 1               /* x, weights, y in bf16; fp32 accumulation, h stored as bf16 */
+} moe_dtype;
+
+typedef enum moe_variant {
+    MOE_VARIANT_UNFUSED = 0,   /* permute -> up+SwiGLU GEMM -> down GEMM -> combine */
+    MOE_VARIANT_FUSED = 1      /* permute -> fused up-act-down (h kept on chip) -> combine */
+} moe_variant;
+
+/* Byte offsets of the pieces of a forward workspace (all 256-byte aligned).
+ * Row space: R = T*k + (has_shared ? T : 0); sorted routed rows come first,
+ * shared-expert row of token t is row T*k + t. */
+typedef struct moe_ws_layout {
+    size_t total;       /* bytes the workspace must hold */
+    size_t err;         /* int32: number of slots with an out-of-range expert id (always 0) */
+    size_t counts;      /* int32 [E] rows per expert */
+    size_t offsets;     /* int32 [E+1] exclusive prefix sum of counts */
+    size_t tile_off;    /* int32 [E+2] prefix sum of ceil(rows/tile_rows), shared group last */
+    size_t perm;        /* int32 [T*k] sorted position -> slot t*k+j (-1 past the valid rows) */
+    size_t inv;         /* int32 [T*k] slot -> sorted position (-1 for an invalid slot) */
+    size_t hist;        /* int32 scratch of the multi-block permute */
+    size_t h;           /* [R, F] silu(g)*u, dtype of the call (unfused variant only) */
+    size_t Y;           /* fp32 [R, D] per-row expert outputs before weighting */
+    int32_t tile_rows;  /* row-tile height of the grouped GEMMs (tile_off's divisor) */
+    int32_t hist_blocks;/* number of slot blocks of the multi-block permute (0: single block) */
+} moe_ws_layout;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *moe_status_string(moe_status status);
+
+/* Row-tile height the grouped GEMMs of (dtype, variant) use; tile_off[] of
+ * moe_expert_permute must be computed with this value to drive them. */
+int moe_ffn_tile_rows(moe_dtype dtype, moe_variant variant);
+
+/*
+ * Fill *layout for a forward call of these sizes.  Returns MOE_OK,
+ * MOE_ERR_INVALID_ARG (layout NULL, T < 0, D/F/E <= 0, k < 1, k > E,
+ * E > 1024, T*k + T >= 2^31, unknown enum) or MOE_ERR_UNSUPPORTED (see
+ * moe_ffn_forward).
+ */
+moe_status moe_ffn_workspace_layout(int64_t T, int D, int F, int E, int k, int has_shared,
+                                    moe_dtype dtype, moe_variant variant, moe_ws_layout *layout);
+
+/* Workspace bytes a forward call of these sizes needs; 0 if the sizes are
+ * invalid or unsupported. */
+size_t moe_ffn_workspace_size(int64_t T, int D, int F, int E, int k, int has_shared,
+                              moe_dtype dtype, moe_variant variant);
+
+/*
+ * Forward pass of the routed SwiGLU MoE layer.
+ *
+ *   x         [T, D]     dtype; token activations, 16-byte aligned
+ *   topk_idx  [T, k]     int32; expert id of choice j of token t
+ *   topk_w    [T, k]     fp32;  routing weight of that choice (used as given)
+ *   W1, W3    [E, D, F]  dtype; gate and up projections (v . W1[e] is v's gate row)
+ *   W2        [E, F, D]  dtype; down projection
+ *   Ws1, Ws3  [D, F], Ws2 [F, D]  dtype; shared expert, all three NULL for none
+ *   y         [T, D]     dtype; output, fully overwritten
+ *   workspace device buffer of ws_bytes >= moe_ffn_workspace_size(), 256-byte aligned
+ *
+ * Stored results (bf16): per row, the gate and up products accumulate in
+ * fp32, silu(g)*u is formed in fp32 and rounded once to bf16 (h); the down
+ * product accumulates in fp32 (Y, kept fp32); the combine starts from the
+ * shared row (or 0), adds w[t,j]*Y for j = 0..k-1 in that order in fp32 and
+ * rounds once to the output dtype.  The summation order does not depend on
+ * timing, so repeated calls give bitwise-identical y.
+ *
+ * Returns MOE_OK; MOE_ERR_INVALID_ARG (null pointer, pointer misaligned,
+ * sizes as in moe_ffn_workspace_layout, only some of Ws1/Ws3/Ws2 given);
+ * MOE_ERR_UNSUPPORTED (bf16 with D or F not a multiple of 64; the fused
+ * variant for a shape it does not cover); MOE_ERR_WORKSPACE; MOE_ERR_HIP.
+ * T == 0 returns MOE_OK and launches nothing.
+ */
+moe_status moe_ffn_forward(const void *x, const int32_t *topk_idx, const float *topk_w,
+                           const void *W1, const void *W3, const void *W2,
+                           const void *Ws1, const void *Ws3, const void *Ws2,
+                           void *y, int64_t T, int D, int F, int E, int k,
+                           moe_dtype dtype, moe_variant variant,
+                           void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_ffn_forward plus per-stage timing: the same call, which also records
+ * events[0] before the permute, events[1] after it, events[2] after the
+ * up+SwiGLU GEMM, events[3] after the down GEMM and events[4] after the
+ * combine, all on `stream` (five caller-created hipEvent_t).  For measuring
+ * each kernel's duration inside a timed loop; results are identical to
+ * moe_ffn_forward.  events == NULL behaves exactly like moe_ffn_forward.
+ */
+moe_status moe_ffn_forward_timed(const void *x, const int32_t *topk_idx, const float *topk_w,
+                                 const void *W1, const void *W3, const void *W2,
+                                 const void *Ws1, const void *Ws3, const void *Ws2,
+                                 void *y, int64_t T, int D, int F, int E, int k,
+                                 moe_dtype dtype, moe_variant variant,
+                                 void *workspace, size_t ws_bytes, hipStream_t stream,
+                                 hipEvent_t events[5]);
+
+/*
+ * Expert permute alone: the stable counting sort of the T*k slots
+ * s = t*k + j by expert id ("Triton MoE Kernels & Memory Checkpointing",
+ * Part A section 10.3 steps 1-2: flatten, stable argsort, bincount and
+ * cumulative sum), plus row-tile offsets for the grouped GEMMs.
+ *
+ *   topk_idx [T*k] int32 in; counts [E]; offsets [E+1] (exclusive starts,
+ *   offsets[E] = number of valid slots); tile_off [E+2] (prefix sum of
+ *   ceil(counts[e]/tile_rows), then one group of shared_rows rows);
+ *   perm [T*k] sorted position -> slot, ascending by (expert, slot), -1 at
+ *   positions >= offsets[E]; inv [T*k] slot -> position, -1 for invalid
+ *   slots; err [1] number of invalid slots.  scratch: scratch_bytes >=
+ *   moe_expert_permute_scratch_size(T, k, E) bytes, 4-byte aligned (may be
+ *   NULL when that size is 0).
+ *
+ * Returns MOE_OK, MOE_ERR_INVALID_ARG (null outputs, T < 0, k < 1, E < 1,
+ * E > 1024, tile_rows < 1, shared_rows < 0, T*k >= 2^31), MOE_ERR_WORKSPACE,
+ * MOE_ERR_HIP.  T == 0 writes counts/offsets/tile_off/err and nothing else.
+ */
+moe_status moe_expert_permute(const int32_t *topk_idx, int64_t T, int k, int E, int tile_rows,
+                              int64_t shared_rows, int32_t *counts, int32_t *offsets,
+                              int32_t *tile_off, int32_t *perm, int32_t *inv, int32_t *err,
+                              void *scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* Scratch bytes moe_expert_permute needs for these sizes (0 when it runs as
+ * a single workgroup). */
+size_t moe_expert_permute_scratch_size(int64_t T, int k, int E);
+
+/*
+ * Read the invalid-slot count of the last forward that used `workspace`.
+ * Waits for `stream` to finish (the one synchronising call).  Returns
+ * MOE_OK, MOE_ERR_INVALID_ARG (null argument) or MOE_ERR_HIP.
+ */
+moe_status moe_ffn_get_device_error(const void *workspace, hipStream_t stream, int32_t *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

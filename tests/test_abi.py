@@ -1,0 +1,109 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/moe_ffn.h declares, sizes its workspace, and rejects bad arguments on
+the host before enqueueing anything (no pointer here is ever dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
+
+gg = pytest.importorskip("grouped_gemm_permute_amd")
+from grouped_gemm_permute_amd import _lib as L  # noqa: E402
+
+FAKE = 0x7F0000000000          # 256-byte aligned, never dereferenced by host validation
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    names = declared_functions()
+    assert names, "no declarations found"
+    assert sorted(L.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_status_strings_and_tile_rows():
+    for s in range(5):
+        assert L.status_string(s).startswith("MOE_")
+    assert L.lib().moe_ffn_tile_rows(L.MOE_BF16, 0) == 256
+    assert L.lib().moe_ffn_tile_rows(L.MOE_F32, 0) > 0
+
+
+def test_workspace_layout_is_aligned_and_sized():
+    import torch
+    lay = L.workspace_layout(32768, 768, 1536, 8, 2, True, torch.bfloat16)
+    R = 32768 * 3
+    for key in ("err", "counts", "offsets", "tile_off", "perm", "inv", "hist", "h", "Y"):
+        assert lay[key] % 256 == 0
+    assert lay["err"] == 0
+    assert lay["Y"] + R * 768 * 4 <= lay["total"]
+    assert lay["h"] + R * 1536 * 2 <= lay["Y"]
+    assert lay["hist_blocks"] == (65536 + 2047) // 2048
+    assert L.workspace_size(32768, 768, 1536, 8, 2, True, torch.bfloat16) == lay["total"]
+    small = L.workspace_layout(512, 768, 1536, 8, 2, False, torch.bfloat16)
+    assert small["hist_blocks"] == 0
+
+
+def _fwd(**over):
+    a = dict(x=FAKE, idx=FAKE, w=FAKE, W1=FAKE, W3=FAKE, W2=FAKE, Ws1=None, Ws3=None, Ws2=None,
+             y=FAKE, T=16, D=64, F=128, E=4, k=2, dt=L.MOE_BF16, v=0, ws=FAKE, nbytes=1 << 40)
+    a.update(over)
+    return L.lib().moe_ffn_forward(a["x"], a["idx"], a["w"], a["W1"], a["W3"], a["W2"], a["Ws1"],
+                                   a["Ws3"], a["Ws2"], a["y"], a["T"], a["D"], a["F"], a["E"],
+                                   a["k"], a["dt"], a["v"], a["ws"], a["nbytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k=5), L.MOE_ERR_INVALID_ARG),                 # k > E
+    (dict(k=0), L.MOE_ERR_INVALID_ARG),
+    (dict(E=0, k=1), L.MOE_ERR_INVALID_ARG),
+    (dict(E=1025, k=2), L.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), L.MOE_ERR_INVALID_ARG),
+    (dict(D=0), L.MOE_ERR_INVALID_ARG),
+    (dict(dt=7), L.MOE_ERR_INVALID_ARG),
+    (dict(v=9), L.MOE_ERR_INVALID_ARG),
+    (dict(x=None), L.MOE_ERR_INVALID_ARG),
+    (dict(W2=None), L.MOE_ERR_INVALID_ARG),
+    (dict(ws=None), L.MOE_ERR_INVALID_ARG),
+    (dict(x=FAKE + 8), L.MOE_ERR_INVALID_ARG),          # misaligned activations
+    (dict(idx=FAKE + 2), L.MOE_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 64), L.MOE_ERR_INVALID_ARG),         # workspace must be 256-byte aligned
+    (dict(Ws1=FAKE), L.MOE_ERR_INVALID_ARG),             # only part of the shared expert
+    (dict(D=96), L.MOE_ERR_UNSUPPORTED),                 # bf16 needs D % 64 == 0
+    (dict(F=200), L.MOE_ERR_UNSUPPORTED),
+    (dict(v=1), L.MOE_ERR_UNSUPPORTED),                  # fused variant not built yet
+    (dict(nbytes=1024), L.MOE_ERR_WORKSPACE),
+    (dict(T=1 << 30, k=2), L.MOE_ERR_INVALID_ARG),       # T*k + T >= 2^31
+    (dict(T=0, x=None, idx=None, w=None, y=None), L.MOE_OK),   # nothing to do, nothing launched
+])
+def test_forward_rejects_bad_arguments_on_host(over, status):
+    assert _fwd(**over) == status
+
+
+def test_permute_rejects_bad_arguments_on_host():
+    lib = L.lib()
+    args = [FAKE, 10, 2, 4, 256, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None]
+    bad = list(args); bad[3] = 0
+    assert lib.moe_expert_permute(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(args); bad[4] = 0
+    assert lib.moe_expert_permute(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(args); bad[6] = None
+    assert lib.moe_expert_permute(*bad) == L.MOE_ERR_INVALID_ARG
+    big = list(args); big[1] = 10000                     # needs scratch for the multi-block path
+    assert lib.moe_ffn_forward is not None
+    assert lib.moe_expert_permute(*big) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_expert_permute_scratch_size(10000, 2, 4) == 5 * ((20000 + 2047) // 2048) * 4
+    assert lib.moe_expert_permute_scratch_size(100, 2, 4) == 0
+
+
+def test_device_error_rejects_null():
+    v = ctypes.c_int32()
+    assert L.lib().moe_ffn_get_device_error(None, None, ctypes.byref(v)) == L.MOE_ERR_INVALID_ARG

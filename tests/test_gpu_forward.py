@@ -1,0 +1,162 @@
+"""moe_ffn_forward on the GPU against the fp64 oracle.
+
+* full element-by-element parity at sizes the oracle finishes in seconds,
+  spanning several 256-row tiles, ragged tails, column tails, the
+  multi-block permute, Zipf skew and empty experts;
+* the five workload shapes at full size in the launch configuration the
+  benchmark times, on sampled tokens the oracle computes one by one;
+* the sorted-row intermediates h and Y on sampled rows;
+* run-to-run bitwise determinism with garbage-filled workspaces;
+* edge cases: T = 1, all tokens on one expert, zero routing weights,
+  out-of-range expert ids (flagged and skipped), T = 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import oracle
+from oracle import brute
+from gpu_util import check_close, device_inputs, host_shared, make_case, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = 16
+
+
+def gpu_forward(inp, variant="unfused", workspace=None):
+    import grouped_gemm_permute_amd as gg
+    d = device_inputs(inp)
+    y = gg.forward(d["x"], d["topk_idx"], d["topk_w"], d["W1"], d["W3"], d["W2"], d["shared"],
+                   variant=variant, workspace=workspace)
+    torch.cuda.synchronize()
+    return y, d
+
+
+def oracle_y(inp, tokens=None):
+    return oracle.forward_dense(inp["x"], inp["topk_idx"], inp["topk_w"], inp["W1"], inp["W3"],
+                                inp["W2"], host_shared(inp), tokens=tokens, nthreads=NTHREADS)
+
+
+FULL_CASES = [
+    # T, D, F, E, k, shared, dtype, routing
+    (64, 64, 128, 4, 2, False, "f32", "uniform"),
+    (97, 64, 192, 3, 2, True, "f32", "uniform"),
+    (700, 256, 512, 8, 2, True, "bf16", "uniform"),
+    (2500, 128, 192, 8, 2, True, "bf16", "uniform"),     # multi-block permute, column tails
+    (300, 64, 64, 1, 1, False, "bf16", "uniform"),
+    (1500, 192, 320, 6, 3, True, "bf16", "zipf"),
+    (1111, 320, 128, 16, 4, False, "bf16", "zipf"),      # empty / tiny experts
+]
+
+
+@pytest.mark.parametrize("case", FULL_CASES, ids=lambda c: "T{}_D{}_F{}_E{}_k{}_{}_{}_{}".format(*c))
+def test_forward_full_parity(case):
+    T, D, F, E, k, sh, dt, routing = case
+    inp = make_case(T, D, F, E, k, sh, dt, routing)
+    say(f"forward full parity {case}")
+    y, _ = gpu_forward(inp)
+    check_close(to_f64(y), oracle_y(inp), dt, str(case))
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_forward_workload_sampled(cfg):
+    w = moe_inputs.WORKLOADS[cfg]
+    inp = moe_inputs.make_inputs(cfg)
+    say(f"forward workload {w.name}")
+    y, _ = gpu_forward(inp)
+    rng = np.random.default_rng(cfg)
+    n = min(w.T, 48)
+    tokens = np.unique(np.concatenate([np.arange(8), np.arange(w.T - 8, w.T),
+                                       rng.choice(w.T, n - 16, replace=False)]))
+    tokens = tokens[tokens < w.T]
+    ref = oracle_y(inp, tokens)
+    check_close(to_f64(y)[tokens], ref, w.dtype, w.name)
+
+
+def test_forward_intermediates_sampled_rows():
+    import grouped_gemm_permute_amd as gg
+    inp = make_case(900, 192, 256, 5, 2, True, "bf16", "zipf", seed=21)
+    T, D, F, E, k = 900, 192, 256, 5, 2
+    lay = gg.workspace_layout(T, D, F, E, k, True, torch.bfloat16)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device="cuda")
+    say("forward intermediates T900 D192 F256 E5 k2 shared")
+    gpu_forward(inp, workspace=ws)
+    R = T * k + T
+    h = ws[lay["h"]:lay["h"] + R * F * 2].view(torch.bfloat16).view(R, F)
+    Y = ws[lay["Y"]:lay["Y"] + R * D * 4].view(torch.float32).view(R, D)
+    ref = oracle.permute(inp["topk_idx"], E)
+    rows = np.concatenate([np.arange(0, T * k, 37), np.arange(T * k - 5, T * k),
+                           np.arange(T * k, R, 41), [R - 1]])
+    flat = inp["topk_idx"].reshape(-1)
+    hs = to_f64(h[torch.from_numpy(rows).cuda()])
+    Ys = to_f64(Y[torch.from_numpy(rows).cuda()])
+    for i, p in enumerate(rows):
+        if p < T * k:
+            s = ref["perm"][p]
+            t, e = s // k, flat[s]
+            w1, w3, w2 = inp["W1"][e], inp["W3"][e], inp["W2"][e]
+        else:
+            t = p - T * k
+            w1, w3, w2 = inp["Ws1"], inp["Ws3"], inp["Ws2"]
+        xv = inp["x"][t].astype(np.float64)
+        g, u = xv @ w1, xv @ w3
+        hh = brute.silu(g) * u
+        check_close(hs[i], hh, "bf16", f"h row {p}")
+        check_close(Ys[i], hh @ w2.astype(np.float64), "bf16", f"Y row {p}")
+
+
+def test_forward_is_bitwise_deterministic():
+    import grouped_gemm_permute_amd as gg
+    inp = make_case(3000, 256, 384, 8, 2, True, "bf16", "zipf", seed=5)
+    d = device_inputs(inp)
+    lay = gg.workspace_layout(3000, 256, 384, 8, 2, True, torch.bfloat16)
+    say("determinism T3000 D256 F384 E8 k2 shared")
+    outs = []
+    for fill in (0, 255, 77):
+        ws = torch.full((lay["total"],), fill, dtype=torch.uint8, device="cuda")
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            y = gg.forward(d["x"], d["topk_idx"], d["topk_w"], d["W1"], d["W3"], d["W2"], d["shared"],
+                           workspace=ws)
+        s.synchronize()
+        outs.append(y.view(torch.int16).cpu())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_forward_edge_cases():
+    import grouped_gemm_permute_amd as gg
+    # one token
+    inp = make_case(1, 128, 128, 4, 2, True, "bf16")
+    say("edge T1")
+    y, _ = gpu_forward(inp)
+    check_close(to_f64(y), oracle_y(inp), "bf16", "T=1")
+    # every token on the same two experts, the others empty
+    inp = make_case(600, 128, 256, 8, 2, False, "bf16")
+    inp["topk_idx"][:, 0] = 3
+    inp["topk_idx"][:, 1] = 7
+    say("edge all tokens on experts 3 and 7")
+    y, _ = gpu_forward(inp)
+    check_close(to_f64(y), oracle_y(inp), "bf16", "two experts")
+    # zero routing weights leave the shared expert
+    inp = make_case(200, 128, 128, 4, 2, True, "bf16")
+    inp["topk_w"][:] = 0.0
+    say("edge zero weights")
+    y, _ = gpu_forward(inp)
+    check_close(to_f64(y), oracle_y(inp), "bf16", "zero weights")
+    # out-of-range ids: flagged, skipped
+    inp = make_case(500, 128, 192, 6, 2, True, "bf16")
+    inp["topk_idx"][10, 1] = 6
+    inp["topk_idx"][11, 0] = -1
+    inp["topk_idx"][499, 1] = 1000
+    lay = gg.workspace_layout(500, 128, 192, 6, 2, True, torch.bfloat16)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device="cuda")
+    say("edge invalid ids")
+    y, _ = gpu_forward(inp, workspace=ws)
+    assert gg.device_error(ws) == 3
+    check_close(to_f64(y), oracle_y(inp), "bf16", "invalid ids")
+    # T = 0: nothing launched, empty output
+    inp = make_case(0, 64, 64, 2, 1, False, "bf16")
+    y, _ = gpu_forward(inp)
+    assert y.shape == (0, 64)
