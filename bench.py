@@ -152,6 +152,23 @@ def cpu_baseline(inp, w, target_s):
                       f"fp64 permuted oracle path, {threads} threads"}
 
 
+def copy_calibration(nbytes, steps):
+    """A plain copy of known size: reads and writes nbytes per launch."""
+    import torch
+    n = nbytes // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes": n * 4, "launches": steps + 1, "ms_per_copy": round(dt * 1e3, 4),
+                      "gbs_read_plus_write": round(2 * n * 4 / dt / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,7 +180,13 @@ def main():
                     help="target length of the CPU-oracle baseline sample; 0 skips it")
     ap.add_argument("--rotate-bytes", type=float, default=512e6,
                     help="rotate input copies until their total exceeds this many bytes")
+    ap.add_argument("--copy-bytes", type=float, default=0,
+                    help="only run a plain device-to-device copy of this many bytes --steps times "
+                         "(the reference kernel for scaling HBM byte counters); prints its timing")
     args = ap.parse_args()
+    if args.copy_bytes > 0:
+        copy_calibration(int(args.copy_bytes), args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path has no multi-GPU implementation); "
               f"got --gpus {args.gpus}", file=sys.stderr)

@@ -1,16 +1,19 @@
 // combine.hip -- unpermute and weighted combine.
 //
-//   y[t] = Ysh[t] + sum_{j=0}^{k-1} w[t,j] * Y[inv[t*k + j]]
+//   y[t] = Yw[S + t] + sum_{j=0}^{k-1} Yw[inv[t*k + j]]
 //
+// where Yw holds every row's expert output already multiplied by its
+// routing weight (the down GEMM's epilogue applies it) and row S + t is the
+// shared expert's output for token t (absent without a shared expert).
 // "Chinchilla scaling, MoE, and fused Triton kernels" (section "PyTorch MoE
 // implementation") gathers each token's k expert rows through the inverse
 // permutation and sums them weighted; "Triton MoE Kernels & Memory
 // Checkpointing" (Part A, section 10.3 step 4) scales by the routing weight
-// after W2 and adds the result back into the token's row.  Here the k terms
-// are added in j order, starting from the shared expert's row (or 0), in
-// fp32, and rounded once to the output type, so the result does not depend
-// on scheduling (no scatter atomics).  Slots with inv = -1 (invalid ids)
-// add nothing.
+// after W2 and adds the result back into the token's row.  Here the terms
+// are added in fp32 in j order, starting from the shared row (or 0), and
+// rounded once to the output type, so the result does not depend on
+// scheduling (no scatter atomics).  Slots with inv = -1 (invalid ids) add
+// nothing.
 #include "moe_internal.h"
 
 namespace moe {
@@ -18,76 +21,79 @@ namespace {
 
 constexpr int NT = 256;
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-// One thread per (token, 4 consecutive columns).
-template <bool BF16>
-__global__ __launch_bounds__(NT) void combine_kernel(const float* __restrict__ Y,
-                                                    const int32_t* __restrict__ inv,
-                                                    const float* __restrict__ w, void* __restrict__ y,
-                                                    int64_t T, int D, int k, int has_shared) {
-    const int cg = (D + 3) / 4;
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// bf16: one thread per (token, 8 consecutive columns); D % 8 == 0 (the bf16
+// path requires D % 64 == 0), all accesses 16 bytes.
+__global__ __launch_bounds__(NT) void combine_bf16_kernel(const uint16_t* __restrict__ Yw,
+                                                         const int32_t* __restrict__ inv,
+                                                         uint16_t* __restrict__ y, int64_t T, int D,
+                                                         int k, int has_shared) {
+    const int cg = D / 8;
     const int64_t gid = (int64_t)blockIdx.x * NT + threadIdx.x;
     if (gid >= T * cg) return;
     const int64_t t = gid / cg;
-    const int c = (int)(gid - t * cg) * 4;
+    const int c = (int)(gid - t * cg) * 8;
     const int64_t S = T * k;
-    const bool vec = (c + 4 <= D) && (D % 4 == 0);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (has_shared) {
-        const float* ys = Y + (S + t) * D + c;
-        if (vec) {
-            const float4 v = *(const float4*)ys;
-            acc[0] = v.x; acc[1] = v.y; acc[2] = v.z; acc[3] = v.w;
-        } else {
-            for (int i = 0; i < 4 && c + i < D; ++i) acc[i] = ys[i];
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto add = [&](const uint16_t* src) {
+        const uint4 v = *(const uint4*)src;
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += bf16_lo(w[i]);
+            acc[2 * i + 1] += bf16_hi(w[i]);
         }
-    }
+    };
+    if (has_shared) add(Yw + (S + t) * D + c);
     for (int j = 0; j < k; ++j) {
         const int32_t p = inv[t * k + j];
         if (p < 0 || p >= S) continue;      // invalid slot (p == -1)
-        const float wt = w[t * k + j];
-        const float* yr = Y + (int64_t)p * D + c;
-        if (vec) {
-            const float4 v = *(const float4*)yr;
-            acc[0] = fmaf(wt, v.x, acc[0]);
-            acc[1] = fmaf(wt, v.y, acc[1]);
-            acc[2] = fmaf(wt, v.z, acc[2]);
-            acc[3] = fmaf(wt, v.w, acc[3]);
-        } else {
-            for (int i = 0; i < 4 && c + i < D; ++i) acc[i] = fmaf(wt, yr[i], acc[i]);
-        }
+        add(Yw + (int64_t)p * D + c);
     }
-    if (BF16) {
-        uint16_t* out = (uint16_t*)y + t * D + c;
-        if (vec) {
-            const uint32_t lo = bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);
-            const uint32_t hi = bf16_rne(acc[2]) | ((uint32_t)bf16_rne(acc[3]) << 16);
-            *(uint2*)out = make_uint2(lo, hi);
-        } else {
-            for (int i = 0; i < 4 && c + i < D; ++i) out[i] = bf16_rne(acc[i]);
-        }
-    } else {
-        float* out = (float*)y + t * D + c;
-        for (int i = 0; i < 4 && c + i < D; ++i) out[i] = acc[i];
+    *(uint4*)(y + t * D + c) = make_uint4(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
+                                          pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7]));
+}
+
+// fp32: one thread per (token, column).
+__global__ __launch_bounds__(NT) void combine_f32_kernel(const float* __restrict__ Yw,
+                                                        const int32_t* __restrict__ inv,
+                                                        float* __restrict__ y, int64_t T, int D,
+                                                        int k, int has_shared) {
+    const int64_t gid = (int64_t)blockIdx.x * NT + threadIdx.x;
+    if (gid >= T * D) return;
+    const int64_t t = gid / D;
+    const int c = (int)(gid - t * D);
+    const int64_t S = T * k;
+    float acc = has_shared ? Yw[(S + t) * D + c] : 0.f;
+    for (int j = 0; j < k; ++j) {
+        const int32_t p = inv[t * k + j];
+        if (p < 0 || p >= S) continue;
+        acc += Yw[(int64_t)p * D + c];
     }
+    y[t * D + c] = acc;
 }
 
 }  // namespace
 
-hipError_t launch_combine(const float* Y, const int32_t* inv, const float* w, void* y, int64_t T,
-                          int D, int k, bool has_shared, bool out_bf16, hipStream_t s) {
-    const int64_t threads = T * ((D + 3) / 4);
-    const unsigned blocks = (unsigned)((threads + NT - 1) / NT);
-    if (out_bf16)
-        combine_kernel<true><<<blocks, NT, 0, s>>>(Y, inv, w, y, T, D, k, has_shared);
-    else
-        combine_kernel<false><<<blocks, NT, 0, s>>>(Y, inv, w, y, T, D, k, has_shared);
+hipError_t launch_combine(const void* Yw, const int32_t* inv, void* y, int64_t T, int D, int k,
+                          bool has_shared, bool bf16, hipStream_t s) {
+    if (bf16) {
+        const int64_t threads = T * (D / 8);
+        combine_bf16_kernel<<<(unsigned)((threads + NT - 1) / NT), NT, 0, s>>>(
+            (const uint16_t*)Yw, inv, (uint16_t*)y, T, D, k, has_shared);
+    } else {
+        const int64_t threads = T * D;
+        combine_f32_kernel<<<(unsigned)((threads + NT - 1) / NT), NT, 0, s>>>(
+            (const float*)Yw, inv, (float*)y, T, D, k, has_shared);
+    }
     return hipGetLastError();
 }
 

@@ -7,24 +7,36 @@
 //                g = x[tok(p)] . W1[grp],  u = x[tok(p)] . W3[grp]   (fp32 accumulate)
 //                h[p] = bf16(silu(g) * u)
 //              x rows are gathered straight from the token matrix while the
-//              A tile is loaded, and W1 and W3 columns of the same output
+//              token tile is loaded, and W1 and W3 columns of the same output
 //              column sit in one workgroup tile, so g and u never leave the
 //              registers.  This is the fused gate/up/SiLU-multiply grouped
 //              GEMM of "Triton MoE Kernels & Memory Checkpointing" (Part A,
 //              sections 6 and 10.1) with fp32 SiLU and a single cast of the
 //              product to the storage type.
-//  down:       Y[p] = h[p] . W2[grp]   (fp32 accumulate, fp32 out), the per
-//              expert W2 product of the same page's section 10.3 step 4.
+//  down:       Yw[p] = bf16(w(p) * (h[p] . W2[grp]))   (fp32 accumulate), the
+//              per-expert W2 product followed by the scaling with the routing
+//              weight of the same page's section 10.3 step 4; w(p) is the
+//              weight of the slot in row p (1 on shared rows).
 //
-// Tile engine: 256 threads (4 wavefronts, 2 x 2), workgroup tile 256 rows x
-// 256 MFMA columns, K step 64, double-buffered LDS (2 x 64 KiB), one wave
-// tile 128 x 128 = 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators.  Global
-// loads of the next K step are issued before the MFMAs of the current one.
-// Weights are stored [K][N] (N contiguous); MFMA wants 8 consecutive K per
-// lane, so each thread loads an 8 x 8 (K x N) block and transposes it in
-// registers before writing K-contiguous rows to LDS.  LDS rows are 128 B;
-// their 16-byte chunks are XOR-swizzled with (row ^ row/8) & 7 so that both
-// the MFMA operand reads and the transposed writes spread over the banks.
+// Tile engine (256 threads = 4 wavefronts, one per SIMD):
+//  * the MFMA computes the transposed tile C^T = W^T . X^T: its A operand is
+//    a 32-feature block of the weights, its B operand a 32-token block of
+//    rows, so each lane ends with 4 consecutive output features of one token
+//    and stores 8 bytes (h, bf16) or 16 bytes (Y, fp32) at a time;
+//  * workgroup tile 256 tokens x 256 MFMA features (up: 128 W1 + 128 W3
+//    columns of the same 128 outputs), K step 64, wave tile 128 x 128 =
+//    4 x 4 v_mfma_f32_32x32x16_bf16 accumulators;
+//  * both tiles go global -> LDS with global_load_lds (16 bytes per lane, no
+//    registers), double-buffered (2 x 64 KiB); the loads of step k+1 are in
+//    flight while step k computes;
+//  * token rows are K-contiguous in memory and in LDS (read with
+//    ds_read_b128); the weights stay [K][N] (N contiguous) in LDS and the
+//    MFMA's K-consecutive operand is produced by ds_read_b64_tr_b16, which
+//    hands each lane 4 consecutive K values of its own column;
+//  * LDS rows are XOR-swizzled in 16-byte chunks (token rows by
+//    (row ^ row/8) & 7, weight rows by 4 (k & 3)); since global_load_lds
+//    writes each wavefront's 1 KiB contiguously, the swizzle is applied by
+//    choosing which global chunk each lane fetches.
 //
 // Row tiles never cross a group: group g owns tiles tile_off[g] ..
 // tile_off[g+1]-1 (computed by the permute on the device), the grid is sized
@@ -37,26 +49,40 @@ namespace moe {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int BM = kBf16TileRows;   // 256 rows per tile
-constexpr int BN = 256;             // MFMA columns per tile (up: 128 g + 128 u)
+constexpr int TT = kBf16TileRows;   // 256 tokens (rows) per tile
+constexpr int TF = 256;             // MFMA features per tile (up: 128 g + 128 u)
 constexpr int BK = 64;
 constexpr int NT = 256;
-constexpr int KCH = BK / 8;         // 16-byte chunks per LDS row
-constexpr int TILE_CHUNKS = BM * KCH;  // chunks of one A (or B) tile in LDS
+constexpr int X_BYTES = TT * BK * 2;                 // 32 KiB token tile
+constexpr int W_BYTES = BK * TF * 2;                 // 32 KiB weight tile
+constexpr int STAGE_BYTES = X_BYTES + W_BYTES;
+constexpr int X_ROW = BK * 2;                        // 128 B per token row
+constexpr int W_ROW = TF * 2;                        // 512 B per k row
 
-static_assert(BM == 256 && BN == 256 && BK == 64 && NT == 256, "index math below assumes these");
+static_assert(TT == 256 && TF == 256 && BK == 64 && NT == 256, "index math below assumes these");
 
-__device__ __forceinline__ int swz(int row, int c) { return row * KCH + (c ^ ((row ^ (row >> 3)) & 7)); }
+// 16-byte-chunk swizzles (chunk index within a row).
+__device__ __forceinline__ int swz_x(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
 
-// Round-to-nearest-even fp32 -> bf16 bits.
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Two fp32 values -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// silu(g) * u in fp32 with the hardware exp2 and reciprocal (about 1 ulp each):
+// g * (1 / (1 + 2^(-g log2 e))) * u.  g -> -inf gives -0, g -> +inf gives g.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
@@ -67,6 +93,13 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
     return x * per + min(x, rem) + i;
 }
 
+__device__ __forceinline__ void load_lds16(const void* g, char* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// Wait until this wavefront's global_load_lds transfers have landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 struct GemmArgs {
     GroupArgs g;
     const uint16_t* a;        // up: x [T, D]; down: h [R, F]
@@ -74,100 +107,145 @@ struct GemmArgs {
     const uint16_t* b1;       // up: W3; down: unused
     const uint16_t* bs0;      // shared expert: up Ws1, down Ws2
     const uint16_t* bs1;      // up Ws3
-    void* out;                // up: h bf16 [R, F]; down: Y fp32 [R, D]
+    void* out;                // up: h bf16 [R, F]; down: Yw bf16 [R, D]
     int D, F;
     int n_tiles;              // column tiles
 };
 
 template <bool UP>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs a) {
-    __shared__ u32x4_t lds[2 * 2 * TILE_CHUNKS];   // [buf][A, B][row][chunk] = 128 KiB
+    // Two stage buffers as separate LDS objects: every access names its buffer
+    // statically, so the compiler knows reads of one buffer do not alias the
+    // asynchronous global_load_lds writes into the other and does not wait
+    // for them.
+    __shared__ __attribute__((aligned(1024))) char lds0[STAGE_BYTES];   // 64 KiB
+    __shared__ __attribute__((aligned(1024))) char lds1[STAGE_BYTES];   // 64 KiB
 
     const int K = UP ? a.D : a.F;      // reduction length
     const int N = UP ? a.F : a.D;      // output columns
-    const int ldb = N;                 // weight row stride (elements)
+    const int ldw = N;                 // weight row stride (elements)
 
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int mt = bid / a.n_tiles, nt = bid - mt * a.n_tiles;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wf = wave >> 1, wt = wave & 1;   // wave's feature half, token half
+
+    // ---- which group owns row tile mt: tile_off is non-decreasing, so the
+    // owner is (number of groups g < G with tile_off[g] <= mt) - 1.  One
+    // vector load of 64 entries per step and a ballot, no dependent chain.
     const int32_t* tile_off = a.g.tile_off;
     if (mt >= tile_off[a.g.G]) return;
-    int grp = 0;
-    {
-        int lo = 0, hi = a.g.G - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (tile_off[mid] <= mt) lo = mid; else hi = mid - 1;
-        }
-        grp = lo;
+    int grp = 0, grp_tile0 = 0, grp_row0_v = 0, grp_end_v = 0;
+    for (int base = 0; base < a.g.G; base += 64) {
+        const int g = base + lane;
+        const bool in = g < a.g.G;
+        const int to = in ? tile_off[g] : 0x7fffffff;
+        const int o0 = (in && g < a.g.E) ? a.g.offsets[g] : 0;
+        const int o1 = (in && g < a.g.E) ? a.g.offsets[g + 1] : 0;
+        const int n = __popcll(__ballot(to <= mt));
+        if (n == 0) break;                  // owner is the last group of the previous block
+        grp = base + n - 1;                 // owner so far: lane n - 1 of this block
+        grp_tile0 = __builtin_amdgcn_readlane(to, n - 1);
+        grp_row0_v = __builtin_amdgcn_readlane(o0, n - 1);
+        grp_end_v = __builtin_amdgcn_readlane(o1, n - 1);
+        if (n < 64) break;
     }
     const bool shared = grp >= a.g.E;
-    const int64_t grp_row0 = shared ? a.g.S : (int64_t)a.g.offsets[grp];
-    const int64_t grp_rows = shared ? a.g.T : (int64_t)(a.g.offsets[grp + 1] - a.g.offsets[grp]);
-    const int64_t tile_r0 = grp_row0 + (int64_t)(mt - tile_off[grp]) * BM;
-    const int valid_rows = (int)min((int64_t)BM, grp_row0 + grp_rows - tile_r0);
+    const int64_t grp_row0 = shared ? a.g.S : (int64_t)grp_row0_v;
+    const int64_t grp_rows = shared ? a.g.T : (int64_t)(grp_end_v - grp_row0_v);
+    const int64_t tile_r0 = grp_row0 + (int64_t)(mt - grp_tile0) * TT;
+    const int valid_rows = (int)min((int64_t)TT, grp_row0 + grp_rows - tile_r0);
     if (valid_rows <= 0) return;       // only if tile_off disagrees with offsets
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    // ---- A rows this thread loads: rows (tid>>3) + 32 i, chunk tid & 7.
-    const int ca = tid & 7;
-    const uint16_t* a_ptr[8];
+    // ---- token tile sources: wave instruction j fills LDS rows 64 wave + 8 j .. +7;
+    // lane -> row 64 wave + 8 j + lane/8, physical chunk lane%8.  Routed rows of
+    // the up GEMM gather token perm[p] / k (all eight index loads in flight at
+    // once); shared rows read token p - S; the down GEMM reads row p of h.
+    int64_t src_row[8];
+    if (UP && !shared) {
+        int32_t slot[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = min((tid >> 3) + 32 * i, valid_rows - 1);
-        const int64_t p = tile_r0 + r;
-        int64_t src_row;
-        if (UP) src_row = p < a.g.S ? (int64_t)(a.g.perm[p] / a.g.k) : p - a.g.S;
-        else src_row = p;
-        a_ptr[i] = a.a + src_row * (int64_t)K + ca * 8;
+        for (int j = 0; j < 8; ++j)
+            slot[j] = a.g.perm[tile_r0 + min(64 * wave + 8 * j + (lane >> 3), valid_rows - 1)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) src_row[j] = slot[j] / a.g.k;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            src_row[j] = tile_r0 + min(64 * wave + 8 * j + (lane >> 3), valid_rows - 1) -
+                         (UP ? a.g.S : 0);
+    }
+    // Down GEMM: routing weight of each of this lane's 4 output rows (1 on shared rows).
+    float row_w[4] = {1.f, 1.f, 1.f, 1.f};
+    if (!UP && !shared) {
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) {
+            const int t = min(128 * wt + 32 * nj + (lane & 31), valid_rows - 1);
+            row_w[nj] = a.g.topk_w[a.g.perm[tile_r0 + t]];
+        }
+    }
+    const char* x_src[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int row = 64 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ swz_x(row);
+        x_src[j] = (const char*)(a.a + src_row[j] * (int64_t)K + 8 * c);
     }
 
-    // ---- B block this thread loads: K rows 8 kb .. 8 kb + 7, 8 columns.
-    const int nb = tid & 31, kb = tid >> 5;
-    const uint16_t* b_ptr;
-    {
+    // ---- weight tile sources: wave instruction j fills k rows 16 wave + 2 j, +1;
+    // lane -> row 16 wave + 2 j + lane/32, physical chunk lane%32.
+    const int64_t gstride = (int64_t)a.D * a.F;
+    const char* w_src[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int kr = 16 * wave + 2 * j + (lane >> 5);
+        const int c = (lane & 31) ^ swz_w(kr);          // logical chunk: 8 feature columns
         int col;
         const uint16_t* base;
-        const int64_t gstride = (int64_t)a.D * a.F;
         if (UP) {
-            // LDS B row R = 8 nb + i: half = R / 128, kind = (R / 64) & 1 (0: W1, 1: W3)
-            const int half = nb >> 4, kind = (nb >> 3) & 1;
-            col = nt * (BN / 2) + half * 64 + (nb & 7) * 8;
-            if (shared) base = kind ? a.bs1 : a.bs0;
-            else base = (kind ? a.b1 : a.b0) + grp * gstride;
+            const int half = c >> 4, kind = (c >> 3) & 1;   // kind 0: W1 (g), 1: W3 (u)
+            col = nt * (TF / 2) + half * 64 + (c & 7) * 8;
+            base = shared ? (kind ? a.bs1 : a.bs0) : (kind ? a.b1 : a.b0) + grp * gstride;
         } else {
-            col = nt * BN + nb * 8;
+            col = nt * TF + c * 8;
             base = shared ? a.bs0 : a.b0 + grp * gstride;
         }
-        if (col >= N) col = 0;                   // past the last column: load a valid one, never stored
-        b_ptr = base + (int64_t)(kb * 8) * ldb + col;
+        if (col >= N) col = 0;                 // past the last column: a valid chunk, never stored
+        w_src[j] = (const char*)(base + (int64_t)kr * ldw + col);
     }
+    const int64_t w_step = (int64_t)BK * ldw * 2;      // bytes per K step in the weights
 
-    u32x4_t ra[8], rb[8];
-    auto load_global = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ra[i] = *(const u32x4_t*)(a_ptr[i] + k0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rb[j] = *(const u32x4_t*)(b_ptr + (int64_t)(k0 + j) * ldb);
+    // One global_load_lds of the stage-kt tiles into buffer xs: instruction
+    // q < 8 is token-tile instruction q, q >= 8 weight-tile instruction q - 8.
+    auto dma = [&](int kt, char* xs, int q) {
+        if (q < 8)
+            load_lds16(x_src[q] + (int64_t)kt * X_ROW, xs + (64 * wave + 8 * q) * X_ROW);
+        else
+            load_lds16(w_src[q - 8] + kt * w_step, xs + X_BYTES + (16 * wave + 2 * (q - 8)) * W_ROW);
     };
-    auto store_lds = [&](int buf) {
-        u32x4_t* As = lds + buf * 2 * TILE_CHUNKS;
-        u32x4_t* Bs = As + TILE_CHUNKS;
+
+    // ---- MFMA operand read offsets (bytes within a stage).
+    // Weight operand (A): lane = 16 G + s reads k = 16 ks + 8 (G>>1) + 4 r + s/4,
+    // feature R = 128 wf + 32 mi + 16 (G&1) + 4 (s&3).
+    const int G = lane >> 4, s = lane & 15;
+    int w_off[4][2];   // [mi][r] for ks = 0; later ks add 16 rows (swizzle repeats every 4 rows)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) As[swz((tid >> 3) + 32 * i, ca)] = ra[i];
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {          // column i of the 8 x 8 block, K ascending
-            const int dw = i >> 1;
-            u32x4_t o;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const uint32_t lo = rb[2 * m][dw], hi = rb[2 * m + 1][dw];
-                o[m] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-            }
-            Bs[swz(8 * nb + i, kb)] = o;
+        for (int r = 0; r < 2; ++r) {
+            const int k = 8 * (G >> 1) + 4 * r + (s >> 2);
+            const int R = 128 * wf + 32 * mi + 16 * (G & 1) + 4 * (s & 3);
+            w_off[mi][r] = X_BYTES + k * W_ROW + (((R >> 3) ^ swz_w(k)) << 4) + 8 * (s & 1);
         }
-    };
+    // Token operand (B): lane reads row 128 wt + 32 nj + lane%32, logical chunk 2 ks + lane/32.
+    int x_row_off[4], x_swz[4];
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj) {
+        const int row = 128 * wt + 32 * nj + (lane & 31);
+        x_row_off[nj] = row * X_ROW;
+        x_swz[nj] = swz_x(row);
+    }
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -175,69 +253,126 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
 #pragma unroll
         for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x16_t{};
 
-    const int KT = K / BK;
-    load_global(0);
-    store_lds(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) load_global((kt + 1) * BK);
-        const u32x4_t* As = lds + buf * 2 * TILE_CHUNKS;
-        const u32x4_t* Bs = As + TILE_CHUNKS;
+    struct Frags {
+        bf16x8_t w[4], x[4];
+    };
+    auto read_frags = [&](const char* st, int ks, Frags& f) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int c = ks * 2 + (lane >> 5);
-            bf16x8_t af[4], bfr[4];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                af[mi] = __builtin_bit_cast(bf16x8_t, As[swz(wm * 128 + mi * 32 + (lane & 31), c)]);
-#pragma unroll
-            for (int nj = 0; nj < 4; ++nj)
-                bfr[nj] = __builtin_bit_cast(bf16x8_t, Bs[swz(wn * 128 + nj * 32 + (lane & 31), c)]);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < 4; ++nj)
-                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[nj],
-                                                                          acc[mi][nj], 0, 0, 0);
+        for (int mi = 0; mi < 4; ++mi) {
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(st + w_off[mi][0] + ks * 16 * W_ROW));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(st + w_off[mi][1] + ks * 16 * W_ROW));
+            const __attribute__((ext_vector_type(8))) short v =
+                __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            f.w[mi] = __builtin_bit_cast(bf16x8_t, v);
         }
-        if (kt + 1 < KT) store_lds(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue.  Accumulator element v of lane l holds column l % 32 and
-    // row 8 (v / 4) + 4 (l / 32) + v % 4 of its 32 x 32 block.
-    const int rbase = wm * 128 + 4 * (lane >> 5);
-    if (UP) {
-        uint16_t* h = (uint16_t*)a.out;
-#pragma unroll
-        for (int nj = 0; nj < 2; ++nj) {
-            const int col = nt * (BN / 2) + wn * 64 + nj * 32 + (lane & 31);
-            if (col >= N) continue;
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int r = rbase + mi * 32 + 8 * (v >> 2) + (v & 3);
-                    if (r < valid_rows) {
-                        const float g = acc[mi][nj][v], u = acc[mi][nj + 2][v];
-                        const float hv = g / (1.0f + __expf(-g)) * u;
-                        h[(tile_r0 + r) * (int64_t)N + col] = bf16_rne(hv);
-                    }
-                }
-        }
-    } else {
-        float* Y = (float*)a.out;
 #pragma unroll
         for (int nj = 0; nj < 4; ++nj) {
-            const int col = nt * BN + wn * 128 + nj * 32 + (lane & 31);
-            if (col >= N) continue;
+            const int c = (2 * ks + (lane >> 5)) ^ x_swz[nj];
+            f.x[nj] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + x_row_off[nj] + (c << 4)));
+        }
+    };
+    auto mfmas = [&](const Frags& f) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj)
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[mi], f.x[nj], acc[mi][nj],
+                                                                      0, 0, 0);
+    };
+    // One K step on stage buffer st (its ks = 0 operands already in fa) while
+    // stage kl streams into nx.  Each k16 slice first issues the next slice's
+    // 12 LDS reads and 4 of the next stage's global_load_lds, then its own 16
+    // independent MFMAs; the scheduling fences keep that order, so every LDS
+    // read has 16 MFMAs (~512 cycles) to land before it is used.
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    auto step = [&](const char* st, char* nx, int kl, Frags& fa, Frags& fb) {
+        read_frags(st, 1, fb);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dma(kl, nx, q);
+        fence();
+        mfmas(fa);
+        fence();
+        read_frags(st, 2, fa);
+#pragma unroll
+        for (int q = 4; q < 8; ++q) dma(kl, nx, q);
+        fence();
+        mfmas(fb);
+        fence();
+        read_frags(st, 3, fb);
+#pragma unroll
+        for (int q = 8; q < 12; ++q) dma(kl, nx, q);
+        fence();
+        mfmas(fa);
+        fence();
+#pragma unroll
+        for (int q = 12; q < 16; ++q) dma(kl, nx, q);
+        fence();
+        mfmas(fb);
+        fence();
+    };
+
+    // K loop, unrolled by two so the stage buffer of every access is static.
+    // The step after the last one reloads the last stage into the idle buffer
+    // (an L2 hit) instead of branching around the loads.
+    const int KT = K / BK;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) dma(0, lds0, q);
+    wait_vmem();
+    __syncthreads();
+    Frags fa, fb;
+    read_frags(lds0, 0, fa);
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        step(lds0, lds1, kt + 1, fa, fb);
+        wait_vmem();
+        __syncthreads();
+        read_frags(lds1, 0, fa);
+        step(lds1, lds0, min(kt + 2, KT - 1), fa, fb);
+        wait_vmem();
+        __syncthreads();
+        read_frags(lds0, 0, fa);
+    }
+    if (kt < KT) {                     // odd step count: the last step sits in lds0
+        step(lds0, lds1, KT - 1, fa, fb);
+        wait_vmem();
+    }
+
+    // ---- epilogue.  acc[mi][nj] element v of lane l: token 128 wt + 32 nj + l%32,
+    // feature 128 wf + 32 mi + 8 (v/4) + 4 (l/32) + v%4.
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj) {
+        const int t = 128 * wt + 32 * nj + (lane & 31);
+        if (t >= valid_rows) continue;
+        const int64_t row = tile_r0 + t;
+        uint16_t* out = (uint16_t*)a.out + row * (int64_t)N;
+        if (UP) {
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int vg = 0; vg < 4; ++vg) {
+                    const int col = nt * (TF / 2) + 64 * wf + 32 * mi + 8 * vg + 4 * (lane >> 5);
+                    if (col >= N) continue;
+                    const f32x16_t& g = acc[mi][nj];
+                    const f32x16_t& u = acc[mi + 2][nj];
+                    const int v = 4 * vg;
+                    *(uint2*)(out + col) =
+                        make_uint2(pack_bf16(silu_mul(g[v], u[v]), silu_mul(g[v + 1], u[v + 1])),
+                                   pack_bf16(silu_mul(g[v + 2], u[v + 2]), silu_mul(g[v + 3], u[v + 3])));
+                }
+        } else {
+            const float wt_row = row_w[nj];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int r = rbase + mi * 32 + 8 * (v >> 2) + (v & 3);
-                    if (r < valid_rows) Y[(tile_r0 + r) * (int64_t)N + col] = acc[mi][nj][v];
+                for (int vg = 0; vg < 4; ++vg) {
+                    const int col = nt * TF + 128 * wf + 32 * mi + 8 * vg + 4 * (lane >> 5);
+                    if (col >= N) continue;
+                    const f32x16_t& c = acc[mi][nj];
+                    const int v = 4 * vg;
+                    *(uint2*)(out + col) = make_uint2(pack_bf16(wt_row * c[v], wt_row * c[v + 1]),
+                                                      pack_bf16(wt_row * c[v + 2], wt_row * c[v + 3]));
                 }
         }
     }
@@ -245,7 +380,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
 
 int m_tiles_upper(const GroupArgs& g) {
     const int64_t rows = g.S + (g.G > g.E ? g.T : 0);
-    return (int)((rows + BM - 1) / BM) + g.G;
+    return (int)((rows + TT - 1) / TT) + g.G;
 }
 
 }  // namespace
@@ -254,16 +389,16 @@ hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* 
                                  const void* Ws1, const void* Ws3, void* h, int D, int F,
                                  hipStream_t s) {
     GemmArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
-               (const uint16_t*)Ws1, (const uint16_t*)Ws3, h, D, F, (F + BN / 2 - 1) / (BN / 2)};
+               (const uint16_t*)Ws1, (const uint16_t*)Ws3, h, D, F, (F + TF / 2 - 1) / (TF / 2)};
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
     grouped_gemm_bf16_kernel<true><<<(unsigned)blocks, NT, 0, s>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
-                            float* Y, int D, int F, hipStream_t s) {
+                            void* Y, int D, int F, hipStream_t s) {
     GemmArgs a{g, (const uint16_t*)h, (const uint16_t*)W2, nullptr, (const uint16_t*)Ws2, nullptr,
-               Y, D, F, (D + BN - 1) / BN};
+               Y, D, F, (D + TF - 1) / TF};
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
     grouped_gemm_bf16_kernel<false><<<(unsigned)blocks, NT, 0, s>>>(a);
     return hipGetLastError();

@@ -50,7 +50,7 @@ moe_status make_layout(int64_t T, int D, int F, int E, int k, int has_shared, mo
     L->inv = take(sizeof(int32_t) * (size_t)S);
     L->hist = take(sizeof(int32_t) * (size_t)(E + 1) * (size_t)nb);
     L->h = take(esize * (size_t)R * (size_t)F);
-    L->Y = take(sizeof(float) * (size_t)R * (size_t)D);
+    L->Y = take(esize * (size_t)R * (size_t)D);
     L->total = off;
     L->tile_rows = dt == MOE_BF16 ? kBf16TileRows : kF32TileRows;
     L->hist_blocks = nb;
@@ -145,7 +145,7 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
     int32_t* inv = (int32_t*)(ws + L.inv);
     int32_t* hist = (int32_t*)(ws + L.hist);
     void* h = ws + L.h;
-    float* Y = (float*)(ws + L.Y);
+    void* Y = ws + L.Y;
     const int64_t S = T * (int64_t)k;
 
     (void)hipGetLastError();
@@ -158,7 +158,7 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
         return MOE_ERR_HIP;
     if (mark(1) != hipSuccess) return MOE_ERR_HIP;
 
-    GroupArgs g{offsets, tile_off, perm, S, T, E, k, E + (has_shared ? 1 : 0)};
+    GroupArgs g{offsets, tile_off, perm, topk_w, S, T, E, k, E + (has_shared ? 1 : 0)};
     hipError_t e;
     if (dtype == MOE_BF16)
         e = launch_up_swiglu_bf16(g, x, W1, W3, Ws1, Ws3, h, D, F, stream);
@@ -170,12 +170,12 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
         if (dtype == MOE_BF16)
             e = launch_down_bf16(g, h, W2, Ws2, Y, D, F, stream);
         else
-            e = launch_down_f32(g, (const float*)h, (const float*)W2, (const float*)Ws2, Y, D, F,
-                                stream);
+            e = launch_down_f32(g, (const float*)h, (const float*)W2, (const float*)Ws2, (float*)Y,
+                                D, F, stream);
     }
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess)
-        e = launch_combine(Y, inv, topk_w, y, T, D, k, has_shared, dtype == MOE_BF16, stream);
+        e = launch_combine(Y, inv, y, T, D, k, has_shared, dtype == MOE_BF16, stream);
     if (e == hipSuccess) e = mark(4);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

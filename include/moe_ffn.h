@@ -76,7 +76,7 @@ typedef struct moe_ws_layout {
     size_t inv;         /* int32 [T*k] slot -> sorted position (-1 for an invalid slot) */
     size_t hist;        /* int32 scratch of the multi-block permute */
     size_t h;           /* [R, F] silu(g)*u, dtype of the call (unfused variant only) */
-    size_t Y;           /* fp32 [R, D] per-row expert outputs before weighting */
+    size_t Y;           /* [R, D] per-row expert outputs times their routing weight, dtype of the call */
     int32_t tile_rows;  /* row-tile height of the grouped GEMMs (tile_off's divisor) */
     int32_t hist_blocks;/* number of slot blocks of the multi-block permute (0: single block) */
 } moe_ws_layout;
@@ -116,10 +116,12 @@ size_t moe_ffn_workspace_size(int64_t T, int D, int F, int E, int k, int has_sha
  *
  * Stored results (bf16): per row, the gate and up products accumulate in
  * fp32, silu(g)*u is formed in fp32 and rounded once to bf16 (h); the down
- * product accumulates in fp32 (Y, kept fp32); the combine starts from the
- * shared row (or 0), adds w[t,j]*Y for j = 0..k-1 in that order in fp32 and
- * rounds once to the output dtype.  The summation order does not depend on
- * timing, so repeated calls give bitwise-identical y.
+ * product accumulates in fp32, is multiplied by the row's routing weight and
+ * rounded once to bf16 (Y); the combine starts from the shared row (or 0),
+ * adds the k weighted rows for j = 0..k-1 in that order in fp32 and rounds
+ * once to the output dtype.  In fp32 every step stays fp32.  The summation
+ * order does not depend on timing, so repeated calls give bitwise-identical
+ * y.
  *
  * Returns MOE_OK; MOE_ERR_INVALID_ARG (null pointer, pointer misaligned,
  * sizes as in moe_ffn_workspace_layout, only some of Ws1/Ws3/Ws2 given);

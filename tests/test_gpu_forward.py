@@ -84,7 +84,7 @@ def test_forward_intermediates_sampled_rows():
     gpu_forward(inp, workspace=ws)
     R = T * k + T
     h = ws[lay["h"]:lay["h"] + R * F * 2].view(torch.bfloat16).view(R, F)
-    Y = ws[lay["Y"]:lay["Y"] + R * D * 4].view(torch.float32).view(R, D)
+    Y = ws[lay["Y"]:lay["Y"] + R * D * 2].view(torch.bfloat16).view(R, D)
     ref = oracle.permute(inp["topk_idx"], E)
     rows = np.concatenate([np.arange(0, T * k, 37), np.arange(T * k - 5, T * k),
                            np.arange(T * k, R, 41), [R - 1]])
@@ -96,14 +96,16 @@ def test_forward_intermediates_sampled_rows():
             s = ref["perm"][p]
             t, e = s // k, flat[s]
             w1, w3, w2 = inp["W1"][e], inp["W3"][e], inp["W2"][e]
+            wt = float(inp["topk_w"].reshape(-1)[s])
         else:
             t = p - T * k
             w1, w3, w2 = inp["Ws1"], inp["Ws3"], inp["Ws2"]
+            wt = 1.0
         xv = inp["x"][t].astype(np.float64)
         g, u = xv @ w1, xv @ w3
         hh = brute.silu(g) * u
         check_close(hs[i], hh, "bf16", f"h row {p}")
-        check_close(Ys[i], hh @ w2.astype(np.float64), "bf16", f"Y row {p}")
+        check_close(Ys[i], wt * (hh @ w2.astype(np.float64)), "bf16", f"Y row {p}")
 
 
 def test_forward_is_bitwise_deterministic():
