@@ -43,16 +43,12 @@
 // by the host from an upper bound, and workgroups past tile_off[G] exit, so
 // no host synchronisation is needed.  Rows past a group's end are clamped
 // to its last row on load and never stored.
-#include "moe_internal.h"
+#include "mfma_common.h"
 
 namespace moe {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
+using namespace mfma;
 
 constexpr int TT = kBf16TileRows;   // 256 tokens (rows) per tile
 constexpr int TF = 256;             // MFMA features per tile (up: 128 g + 128 u)
@@ -66,39 +62,8 @@ constexpr int W_ROW = TF * 2;                        // 512 B per k row
 
 static_assert(TT == 256 && TF == 256 && BK == 64 && NT == 256, "index math below assumes these");
 
-// 16-byte-chunk swizzles (chunk index within a row).
-__device__ __forceinline__ int swz_x(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
-
-typedef __attribute__((ext_vector_type(2))) float f32x2_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-
-// Two fp32 values -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even).
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
-}
-
-// silu(g) * u in fp32 with the hardware exp2 and reciprocal (about 1 ulp each):
-// g * (1 / (1 + 2^(-g log2 e))) * u.  g -> -inf gives -0, g -> +inf gives g.
-__device__ __forceinline__ float silu_mul(float g, float u) {
-    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
-    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
-}
-
-// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-// contiguous range of logical tiles so neighbours share L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
-    const int x = bid & 7, i = bid >> 3;
-    const int per = nblk >> 3, rem = nblk & 7;
-    return x * per + min(x, rem) + i;
-}
-
-__device__ __forceinline__ void load_lds16(const void* g, char* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
-}
-
-// Wait until this wavefront's global_load_lds transfers have landed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ int swz_x(int row) { return swz8(row); }
+__device__ __forceinline__ int swz_w(int k) { return swz_tr(k); }
 
 struct GemmArgs {
     GroupArgs g;
@@ -131,31 +96,14 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wf = wave >> 1, wt = wave & 1;   // wave's feature half, token half
 
-    // ---- which group owns row tile mt: tile_off is non-decreasing, so the
-    // owner is (number of groups g < G with tile_off[g] <= mt) - 1.  One
-    // vector load of 64 entries per step and a ballot, no dependent chain.
+    // ---- the group owning row tile mt, and the tile's rows.
     const int32_t* tile_off = a.g.tile_off;
     if (mt >= tile_off[a.g.G]) return;
-    int grp = 0, grp_tile0 = 0, grp_row0_v = 0, grp_end_v = 0;
-    for (int base = 0; base < a.g.G; base += 64) {
-        const int g = base + lane;
-        const bool in = g < a.g.G;
-        const int to = in ? tile_off[g] : 0x7fffffff;
-        const int o0 = (in && g < a.g.E) ? a.g.offsets[g] : 0;
-        const int o1 = (in && g < a.g.E) ? a.g.offsets[g + 1] : 0;
-        const int n = __popcll(__ballot(to <= mt));
-        if (n == 0) break;                  // owner is the last group of the previous block
-        grp = base + n - 1;                 // owner so far: lane n - 1 of this block
-        grp_tile0 = __builtin_amdgcn_readlane(to, n - 1);
-        grp_row0_v = __builtin_amdgcn_readlane(o0, n - 1);
-        grp_end_v = __builtin_amdgcn_readlane(o1, n - 1);
-        if (n < 64) break;
-    }
+    const TileGroup tg = find_tile_group(a.g, mt, TT, lane);
+    const int grp = tg.grp;
     const bool shared = grp >= a.g.E;
-    const int64_t grp_row0 = shared ? a.g.S : (int64_t)grp_row0_v;
-    const int64_t grp_rows = shared ? a.g.T : (int64_t)(grp_end_v - grp_row0_v);
-    const int64_t tile_r0 = grp_row0 + (int64_t)(mt - grp_tile0) * TT;
-    const int valid_rows = (int)min((int64_t)TT, grp_row0 + grp_rows - tile_r0);
+    const int64_t tile_r0 = tg.tile_r0;
+    const int valid_rows = tg.valid_rows;
     if (valid_rows <= 0) return;       // only if tile_off disagrees with offsets
 
     // ---- token tile sources: wave instruction j fills LDS rows 64 wave + 8 j .. +7;
@@ -259,13 +207,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     auto read_frags = [&](const char* st, int ks, Frags& f) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(st + w_off[mi][0] + ks * 16 * W_ROW));
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(st + w_off[mi][1] + ks * 16 * W_ROW));
-            const __attribute__((ext_vector_type(8))) short v =
-                __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            f.w[mi] = __builtin_bit_cast(bf16x8_t, v);
+            f.w[mi] = cat_bf16(read_tr(st + w_off[mi][0] + ks * 16 * W_ROW),
+                               read_tr(st + w_off[mi][1] + ks * 16 * W_ROW));
         }
 #pragma unroll
         for (int nj = 0; nj < 4; ++nj) {

@@ -32,7 +32,9 @@ moe_status make_layout(int64_t T, int D, int F, int E, int k, int has_shared, mo
     const int64_t R = S + (has_shared ? T : 0);
     if (R >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
     if (dt == MOE_BF16 && (D % 64 != 0 || F % 64 != 0)) return MOE_ERR_UNSUPPORTED;
-    if (v == MOE_VARIANT_FUSED) return MOE_ERR_UNSUPPORTED;
+    if (v == MOE_VARIANT_FUSED && (dt != MOE_BF16 || D % 128 != 0 || D > 1024 || F % 128 != 0))
+        return MOE_ERR_UNSUPPORTED;
+    const bool fused = v == MOE_VARIANT_FUSED;
 
     const size_t esize = dt == MOE_BF16 ? 2 : 4;
     const int nb = permute_hist_blocks(S);
@@ -49,10 +51,10 @@ moe_status make_layout(int64_t T, int D, int F, int E, int k, int has_shared, mo
     L->perm = take(sizeof(int32_t) * (size_t)S);
     L->inv = take(sizeof(int32_t) * (size_t)S);
     L->hist = take(sizeof(int32_t) * (size_t)(E + 1) * (size_t)nb);
-    L->h = take(esize * (size_t)R * (size_t)F);
+    L->h = take(fused ? 0 : esize * (size_t)R * (size_t)F);   // the fused variant keeps h on chip
     L->Y = take(esize * (size_t)R * (size_t)D);
     L->total = off;
-    L->tile_rows = dt == MOE_BF16 ? kBf16TileRows : kF32TileRows;
+    L->tile_rows = fused ? kFusedTileRows : (dt == MOE_BF16 ? kBf16TileRows : kF32TileRows);
     L->hist_blocks = nb;
     return MOE_OK;
 }
@@ -73,7 +75,7 @@ const char* moe_status_string(moe_status status) {
 }
 
 int moe_ffn_tile_rows(moe_dtype dtype, moe_variant variant) {
-    (void)variant;
+    if (variant == MOE_VARIANT_FUSED) return kFusedTileRows;
     return dtype == MOE_BF16 ? kBf16TileRows : kF32TileRows;
 }
 
@@ -160,13 +162,19 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
 
     GroupArgs g{offsets, tile_off, perm, topk_w, S, T, E, k, E + (has_shared ? 1 : 0)};
     hipError_t e;
-    if (dtype == MOE_BF16)
+    if (variant == MOE_VARIANT_FUSED) {
+        // one launch does up, SwiGLU and down; both timing marks follow it
+        e = launch_fused_bf16(g, x, W1, W3, W2, Ws1, Ws3, Ws2, Y, D, F, stream);
+        if (e == hipSuccess) e = mark(2);
+    } else if (dtype == MOE_BF16) {
         e = launch_up_swiglu_bf16(g, x, W1, W3, Ws1, Ws3, h, D, F, stream);
-    else
+        if (e == hipSuccess) e = mark(2);
+    } else {
         e = launch_up_swiglu_f32(g, (const float*)x, (const float*)W1, (const float*)W3,
                                  (const float*)Ws1, (const float*)Ws3, (float*)h, D, F, stream);
-    if (e == hipSuccess) e = mark(2);
-    if (e == hipSuccess) {
+        if (e == hipSuccess) e = mark(2);
+    }
+    if (e == hipSuccess && variant != MOE_VARIANT_FUSED) {
         if (dtype == MOE_BF16)
             e = launch_down_bf16(g, h, W2, Ws2, Y, D, F, stream);
         else

@@ -46,6 +46,14 @@ hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* 
 hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
                             void* Yw, int D, int F, hipStream_t s);
 
+// Fused up-act-down (bf16): token tiles of kFusedTileRows rows, h kept on
+// chip; writes the same weighted Yw as the down GEMM.  Needs D % 128 == 0,
+// D <= 1024, F % 128 == 0.
+constexpr int kFusedTileRows = 64;
+hipError_t launch_fused_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
+                             const void* W2, const void* Ws1, const void* Ws3, const void* Ws2,
+                             void* Yw, int D, int F, hipStream_t s);
+
 // fp32 grouped GEMMs (plain fp32 FMA; correctness-first path).
 constexpr int kF32TileRows = 64;
 hipError_t launch_up_swiglu_f32(const GroupArgs& g, const float* x, const float* W1,

@@ -60,7 +60,8 @@ typedef enum moe_dtype {
 
 typedef enum moe_variant {
     MOE_VARIANT_UNFUSED = 0,   /* permute -> up+SwiGLU GEMM -> down GEMM -> combine */
-    MOE_VARIANT_FUSED = 1      /* permute -> fused up-act-down (h kept on chip) -> combine */
+    MOE_VARIANT_FUSED = 1      /* permute -> fused up-act-down (h kept on chip) -> combine;
+                                  bf16 only, D % 128 == 0, D <= 1024, F % 128 == 0 */
 } moe_variant;
 
 /* Byte offsets of the pieces of a forward workspace (all 256-byte aligned).
@@ -75,7 +76,7 @@ typedef struct moe_ws_layout {
     size_t perm;        /* int32 [T*k] sorted position -> slot t*k+j (-1 past the valid rows) */
     size_t inv;         /* int32 [T*k] slot -> sorted position (-1 for an invalid slot) */
     size_t hist;        /* int32 scratch of the multi-block permute */
-    size_t h;           /* [R, F] silu(g)*u, dtype of the call (unfused variant only) */
+    size_t h;           /* [R, F] silu(g)*u, dtype of the call (unfused variant; empty when fused) */
     size_t Y;           /* [R, D] per-row expert outputs times their routing weight, dtype of the call */
     int32_t tile_rows;  /* row-tile height of the grouped GEMMs (tile_off's divisor) */
     int32_t hist_blocks;/* number of slot blocks of the multi-block permute (0: single block) */
@@ -126,7 +127,15 @@ size_t moe_ffn_workspace_size(int64_t T, int D, int F, int E, int k, int has_sha
  * Returns MOE_OK; MOE_ERR_INVALID_ARG (null pointer, pointer misaligned,
  * sizes as in moe_ffn_workspace_layout, only some of Ws1/Ws3/Ws2 given);
  * MOE_ERR_UNSUPPORTED (bf16 with D or F not a multiple of 64; the fused
- * variant for a shape it does not cover); MOE_ERR_WORKSPACE; MOE_ERR_HIP.
+ * variant with fp32, D % 128 != 0, D > 1024 or F % 128 != 0);
+ * MOE_ERR_WORKSPACE; MOE_ERR_HIP.
+ *
+ * Variants: MOE_VARIANT_UNFUSED writes h [R, F] to the workspace between
+ * the up and down grouped GEMMs; MOE_VARIANT_FUSED ("Chinchilla scaling,
+ * MoE, and fused Triton kernels", fused kernel sections) computes up,
+ * SwiGLU and down per 64-token tile in one kernel and never stores h.  Both
+ * give results within the same tolerance of the exact layer; they are not
+ * bitwise equal to each other (different accumulation blocking).
  * T == 0 returns MOE_OK and launches nothing.
  */
 moe_status moe_ffn_forward(const void *x, const int32_t *topk_idx, const float *topk_w,
@@ -139,8 +148,10 @@ moe_status moe_ffn_forward(const void *x, const int32_t *topk_idx, const float *
 /*
  * moe_ffn_forward plus per-stage timing: the same call, which also records
  * events[0] before the permute, events[1] after it, events[2] after the
- * up+SwiGLU GEMM, events[3] after the down GEMM and events[4] after the
- * combine, all on `stream` (five caller-created hipEvent_t).  For measuring
+ * up+SwiGLU GEMM (the fused variant: after its single up-act-down kernel),
+ * events[3] after the down GEMM (fused: immediately after events[2]) and
+ * events[4] after the combine, all on `stream` (five caller-created
+ * hipEvent_t).  For measuring
  * each kernel's duration inside a timed loop; results are identical to
  * moe_ffn_forward.  events == NULL behaves exactly like moe_ffn_forward.
  */

@@ -79,13 +79,23 @@ def _fwd(**over):
     (dict(Ws1=FAKE), L.MOE_ERR_INVALID_ARG),             # only part of the shared expert
     (dict(D=96), L.MOE_ERR_UNSUPPORTED),                 # bf16 needs D % 64 == 0
     (dict(F=200), L.MOE_ERR_UNSUPPORTED),
-    (dict(v=1), L.MOE_ERR_UNSUPPORTED),                  # fused variant not built yet
+    (dict(v=1, D=192), L.MOE_ERR_UNSUPPORTED),           # fused needs D % 128 == 0
+    (dict(v=1, D=1152), L.MOE_ERR_UNSUPPORTED),          # fused needs D <= 1024
+    (dict(v=1, F=192), L.MOE_ERR_UNSUPPORTED),           # fused needs F % 128 == 0
+    (dict(v=1, dt=L.MOE_F32), L.MOE_ERR_UNSUPPORTED),    # fused is bf16 only
     (dict(nbytes=1024), L.MOE_ERR_WORKSPACE),
     (dict(T=1 << 30, k=2), L.MOE_ERR_INVALID_ARG),       # T*k + T >= 2^31
     (dict(T=0, x=None, idx=None, w=None, y=None), L.MOE_OK),   # nothing to do, nothing launched
 ])
 def test_forward_rejects_bad_arguments_on_host(over, status):
     assert _fwd(**over) == status
+
+
+def test_fused_layout_has_no_h_and_64_row_tiles():
+    import torch
+    lay = L.workspace_layout(16384, 1024, 4096, 16, 2, False, torch.bfloat16, "fused")
+    assert lay["tile_rows"] == 64 and lay["Y"] == lay["h"]
+    assert L.lib().moe_ffn_tile_rows(L.MOE_BF16, L.MOE_VARIANT_FUSED) == 64
 
 
 def test_permute_rejects_bad_arguments_on_host():

@@ -59,6 +59,37 @@ def test_forward_full_parity(case):
     check_close(to_f64(y), oracle_y(inp), dt, str(case))
 
 
+FUSED_CASES = [
+    # T, D, F, E, k, shared, routing
+    (700, 256, 512, 8, 2, True, "uniform"),
+    (1111, 128, 384, 5, 3, False, "zipf"),     # ragged 64-row tiles, empty experts possible
+    (300, 1024, 256, 4, 2, True, "uniform"),   # widest accumulator (D = 1024)
+    (513, 768, 640, 6, 2, False, "uniform"),
+    (1, 384, 128, 2, 1, False, "uniform"),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "T{}_D{}_F{}_E{}_k{}_{}_{}".format(*c))
+def test_fused_full_parity(case):
+    T, D, F, E, k, sh, routing = case
+    inp = make_case(T, D, F, E, k, sh, "bf16", routing, seed=31)
+    say(f"fused full parity {case}")
+    y, _ = gpu_forward(inp, variant="fused")
+    check_close(to_f64(y), oracle_y(inp), "bf16", "fused " + str(case))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_fused_workload_sampled(cfg):
+    w = moe_inputs.WORKLOADS[cfg]
+    inp = moe_inputs.make_inputs(cfg)
+    say(f"fused workload {w.name}")
+    y, _ = gpu_forward(inp, variant="fused")
+    rng = np.random.default_rng(100 + cfg)
+    tokens = np.unique(np.concatenate([np.arange(8), np.arange(w.T - 8, w.T),
+                                       rng.choice(w.T, 32, replace=False)]))
+    check_close(to_f64(y)[tokens], oracle_y(inp, tokens), w.dtype, "fused " + w.name)
+
+
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_forward_workload_sampled(cfg):
     w = moe_inputs.WORKLOADS[cfg]
