@@ -48,9 +48,14 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash(stage: str) -> str:
+def source_hash(stage: str, variant: str = "unfused") -> str:
+    """Hash of the sources a kernel is built from (stale counters are not used)."""
     h = hashlib.sha256()
-    for rel in (KERNEL_SOURCES[stage], "grouped_gemm_permute_amd/csrc/moe_internal.h"):
+    src = KERNEL_SOURCES[stage]
+    if variant == "fused" and stage == "up_swiglu":
+        src = "grouped_gemm_permute_amd/csrc/fused_bf16.hip"
+    for rel in (src, "grouped_gemm_permute_amd/csrc/mfma_common.h",
+                "grouped_gemm_permute_amd/csrc/moe_internal.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -112,17 +117,19 @@ def path_bytes(w, counts):
     return 2 * w.T * w.D * b + w.T * w.k * 8 + 3 * w.D * w.F * b * groups
 
 
-def load_traffic(workload_name, stage):
-    """Counter-derived HBM bytes per launch, if profiles/ holds a summary
-    taken from the current kernel source."""
+def load_traffic(workload_name, key):
+    """Counter-derived HBM bytes per launch ("variant:stage" key), if
+    profiles/traffic.json holds a figure taken from the current kernel
+    source; otherwise None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
-        rec = json.load(open(p)).get(workload_name, {}).get(stage)
+        rec = json.load(open(p)).get(workload_name, {}).get(key)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != source_hash(stage):
+    stage = key.split(":")[-1]
+    if not rec or rec.get("source_sha") != source_hash(stage, key.split(":")[0]):
         return None
     return rec.get("bytes_per_launch")
 
@@ -233,27 +240,46 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    hip = HipEvents()
-    evs = [hip.create(5) for _ in range(args.steps)]
+    # Timed region 1: K plain forward calls, synchronized on both sides.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # Timed region 2: the same K calls with HIP events recorded on the stream
+    # between the kernels (moe_ffn_forward_timed); each record costs a few
+    # microseconds of GPU time, so only per-kernel durations come from here.
+    hip = HipEvents()
+    evs = [hip.create(5) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     stage_ms = {st: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs]))
                 for j, st in enumerate(STAGES)}
     fwd_ms = float(np.mean([hip.elapsed_ms(e[0], e[4]) for e in evs]))
     for e in evs:
         hip.destroy(e)
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (host clock), "
-        f"{fwd_ms:.4f} ms/step (events); stages {stage_ms}")
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (host clock, no events), "
+        f"{fwd_ms:.4f} ms/step with per-kernel events; stages {stage_ms}")
 
     flop = w.flops()
     value = flop / (ms_per_step * 1e-3) / 1e12
     work = stage_work(w, counts)
-    dom = max(("up_swiglu", "down"), key=lambda s: stage_ms[s])
+    if args.variant == "fused":       # one kernel does up, SwiGLU and down
+        stage_ms.pop("down")           # an empty interval between two back-to-back events
+        work["up_swiglu"]["flop"] += work["down"]["flop"]
+        work["up_swiglu"]["bytes"] = (w.T * w.D * (2 if w.dtype == "bf16" else 4)
+                                      + 3 * w.D * w.F * (2 if w.dtype == "bf16" else 4)
+                                      * (int(sum(1 for c in counts if c > 0)) + (1 if w.shared else 0))
+                                      + (w.T * w.k + (w.T if w.shared else 0)) * w.D * 2)
+        stage_ms["down"] = 0.0
+        kernels = ("up_swiglu",)
+    else:
+        kernels = ("up_swiglu", "down")
+    dom = max(kernels, key=lambda s: stage_ms[s])
     sec = stage_ms[dom] * 1e-3
     mfma_bound = work[dom]["flop"] / work[dom]["bytes"] > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3
     if mfma_bound:
@@ -264,8 +290,8 @@ def main():
         ach = work[dom]["bytes"] / sec / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = load_traffic(w.name, dom)
-    roof["kernel"] = dom
+    roof["traffic"] = load_traffic(w.name, f"{args.variant}:{dom}")
+    roof["kernel"] = "fused_up_act_down" if args.variant == "fused" else dom
     roof["launch_ms"] = round(stage_ms[dom], 5)
     roof["algorithmic"] = work[dom]["flop"] if mfma_bound else work[dom]["bytes"]
 

@@ -36,8 +36,10 @@ class MoeError(RuntimeError):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("total", "err", "counts", "offsets", "tile_off", "perm", "inv", "hist", "h", "Y")] + \
-               [("tile_rows", ctypes.c_int32), ("hist_blocks", ctypes.c_int32)]
+                ("total", "err", "counts", "offsets", "tile_off", "tile_off64", "perm", "inv", "hist",
+                 "h", "Y")] + \
+               [("tile_rows", ctypes.c_int32), ("hist_blocks", ctypes.c_int32),
+                ("small_tiles", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -1,0 +1,249 @@
+// gemm_bf16_small.hip -- grouped GEMMs for small per-expert chunks.
+//
+// Same products as gemm_bf16.hip (up: h = bf16(silu(x . W1) * (x . W3));
+// down: Yw = bf16(w * (h . W2))), shaped for the regime where each expert
+// sees only tens to a few hundred rows and the weights dominate the traffic
+// (the "small chunks" that "Triton MoE Kernels & Memory Checkpointing",
+// Part A sections 2 and 6.1, calls the pathological regime).  There the
+// product is bound by streaming each expert's weights once, so the tile is
+// small in both directions to spread the weights over many workgroups:
+//
+//  * tile 64 rows x 64 MFMA features (up: 32 g + 32 u), K step 64;
+//  * 256 threads = 4 wavefronts (2 feature x 2 row), one 32 x 32
+//    v_mfma_f32_32x32x16_bf16 block each; two workgroups per CU;
+//  * a 4-deep ring of LDS stages (16 KiB each) filled with global_load_lds,
+//    so three stages (48 KiB per workgroup) are in flight while one computes;
+//  * tiles run n-major (all row tiles of one weight slice back to back) so
+//    the row tiles of an expert share its weight slice through L2;
+//  * up: a wavefront's 32 MFMA rows are 16 g columns followed by the same 16
+//    u columns, so accumulator element v (g) and v + 8 (u) of a lane belong
+//    to the same (row, column).
+#include "mfma_common.h"
+
+namespace moe {
+namespace {
+
+using namespace mfma;
+
+constexpr int TT = kSmallTileRows;   // 64 rows per tile
+constexpr int TF = 64;               // MFMA features per tile (up: 32 g + 32 u)
+constexpr int BK = 64;
+constexpr int NT = 256;
+constexpr int NSTAGE = 4;
+constexpr int X_ROW = BK * 2;                  // 128 B
+constexpr int X_BYTES = TT * X_ROW;            // 8 KiB
+constexpr int W_ROW = TF * 2;                  // 128 B (64 features of one k row)
+constexpr int W_BYTES = BK * W_ROW;            // 8 KiB
+constexpr int STAGE_BYTES = X_BYTES + W_BYTES; // 16 KiB
+
+static_assert(TT == 64 && TF == 64 && BK == 64 && NT == 256, "index math below assumes these");
+
+// [K][N] rows of 128 B read with ds_read_b64_tr_b16: rows k and k+2 (same
+// bank half) land on disjoint chunk sets.
+__device__ __forceinline__ int swz_tr128(int k) { return 4 * ((k >> 1) & 1); }
+
+struct SmallArgs {
+    GroupArgs g;
+    const uint16_t* a;        // up: x [T, D]; down: h [R, F]
+    const uint16_t* b0;       // up: W1; down: W2
+    const uint16_t* b1;       // up: W3
+    const uint16_t* bs0;      // shared: up Ws1, down Ws2
+    const uint16_t* bs1;      // shared: up Ws3
+    uint16_t* out;            // up: h [R, F]; down: Yw [R, D]
+    int D, F;
+    int n_tiles;
+};
+
+template <bool UP>
+__global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallArgs a) {
+    __shared__ __attribute__((aligned(1024))) char st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st3[STAGE_BYTES];
+
+    const int K = UP ? a.D : a.F;
+    const int N = UP ? a.F : a.D;
+    const int total = a.g.tile_off[a.g.G];
+    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    const int nt = id / total, mt = id - nt * total;     // n-major
+    if (nt >= a.n_tiles) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wf = wave >> 1, wt = wave & 1;
+    const TileGroup tg = find_tile_group(a.g, mt, TT, lane);
+    const int grp = tg.grp;
+    const bool shared = grp >= a.g.E;
+    const int64_t tile_r0 = tg.tile_r0;
+    const int valid_rows = tg.valid_rows;
+    if (valid_rows <= 0) return;
+
+    // ---- row tile: DMA instruction j (0, 1) of wavefront w fills rows 16 w + 8 j .. +7.
+    const char* x_src[2];
+    {
+        int64_t src_row[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            src_row[j] = tile_r0 + min(16 * wave + 8 * j + (lane >> 3), valid_rows - 1);
+        if (UP && !shared) {
+            const int32_t s0 = a.g.perm[src_row[0]], s1 = a.g.perm[src_row[1]];
+            src_row[0] = s0 / a.g.k;
+            src_row[1] = s1 / a.g.k;
+        } else if (UP) {
+            src_row[0] -= a.g.S;
+            src_row[1] -= a.g.S;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = 16 * wave + 8 * j + (lane >> 3);
+            x_src[j] = (const char*)(a.a + src_row[j] * (int64_t)K + 8 * ((lane & 7) ^ swz8(row)));
+        }
+    }
+    // ---- weight tile [64 k][64 features]: DMA instruction j (0, 1) of
+    // wavefront w fills k rows 16 w + 8 j .. +7; lane -> k row 16 w + 8 j +
+    // lane/8, physical chunk lane%8 holding logical chunk lc = phys ^ swz(k).
+    // Up: logical chunk lc -> wavefront wb = lc / 4, g when (lc / 2) is even,
+    // h column 16 wb + 8 (lc % 2) of the tile.
+    const int64_t gstride = (int64_t)a.D * a.F;
+    const char* w_src[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int kr = 16 * wave + 8 * j + (lane >> 3);
+        const int lc = (lane & 7) ^ swz_tr128(kr);
+        int col;
+        const uint16_t* base;
+        if (UP) {
+            const int kind = (lc >> 1) & 1;
+            col = nt * (TF / 2) + 16 * (lc >> 2) + 8 * (lc & 1);
+            base = shared ? (kind ? a.bs1 : a.bs0) : (kind ? a.b1 : a.b0) + grp * gstride;
+        } else {
+            col = nt * TF + 8 * lc;
+            base = shared ? a.bs0 : a.b0 + grp * gstride;
+        }
+        if (col >= N) col = 0;                 // past the last column: a valid chunk, never stored
+        w_src[j] = (const char*)(base + (int64_t)kr * N + col);
+    }
+    const int64_t w_step = (int64_t)BK * N * 2;
+    float row_w = 1.f;
+    if (!UP && !shared)
+        row_w = a.g.topk_w[a.g.perm[tile_r0 + min(32 * wt + (lane & 31), valid_rows - 1)]];
+
+    auto issue = [&](int kt, char* st) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            load_lds16(x_src[j] + (int64_t)kt * X_ROW, st + (16 * wave + 8 * j) * X_ROW);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            load_lds16(w_src[j] + kt * w_step, st + X_BYTES + (16 * wave + 8 * j) * W_ROW);
+    };
+
+    // ---- operands: weights (A) through transposed reads: lane = 16 G + s
+    // reads k = 16 ks + 8 (G>>1) + 4 r + s/4, feature 32 wf + 16 (G&1) + 4 (s&3);
+    // rows (B): row 32 wt + lane%32, logical chunk 2 ks + lane/32.
+    const int G = lane >> 4, sl = lane & 15;
+    int w_off[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int k = 8 * (G >> 1) + 4 * r + (sl >> 2);
+        const int R = 32 * wf + 16 * (G & 1) + 4 * (sl & 3);
+        w_off[r] = X_BYTES + k * W_ROW + (((R >> 3) ^ swz_tr128(k)) << 4) + 8 * (sl & 1);
+    }
+    const int xrow = 32 * wt + (lane & 31);
+    const int x_off = xrow * X_ROW, x_swz = swz8(xrow);
+
+    f32x16_t acc = {};
+    auto compute = [&](const char* st) {
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const bf16x8_t wfr = cat_bf16(read_tr(st + w_off[0] + ks * 16 * W_ROW),
+                                          read_tr(st + w_off[1] + ks * 16 * W_ROW));
+            const int c = (2 * ks + (lane >> 5)) ^ x_swz;
+            const bf16x8_t xfr = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + x_off + (c << 4)));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wfr, xfr, acc, 0, 0, 0);
+        }
+    };
+
+    // ---- 4-stage ring, unrolled by 4 so every buffer access is static.  At
+    // step kt the stages kt+1, kt+2 are in flight and kt+3 is issued into
+    // the buffer step kt-1 just released (after the barrier).  Loads past
+    // the last stage re-read the last stage (never computed on).
+    const int KT = K / BK;
+    auto wait_stage = [] { __builtin_amdgcn_s_waitcnt(0x0F78); };   // <= 8 DMA (2 stages) left
+    issue(0, st0);
+    issue(min(1, KT - 1), st1);
+    issue(min(2, KT - 1), st2);
+    for (int kt = 0; kt < KT; kt += 4) {
+        wait_stage();
+        __syncthreads();
+        issue(min(kt + 3, KT - 1), st3);
+        compute(st0);
+        wait_stage();
+        __syncthreads();
+        issue(min(kt + 4, KT - 1), st0);
+        if (kt + 1 < KT) compute(st1);
+        wait_stage();
+        __syncthreads();
+        issue(min(kt + 5, KT - 1), st1);
+        if (kt + 2 < KT) compute(st2);
+        wait_stage();
+        __syncthreads();
+        issue(min(kt + 6, KT - 1), st2);
+        if (kt + 3 < KT) compute(st3);
+    }
+    wait_vmem();
+
+    // ---- epilogue.  acc element v of lane l: row 32 wt + l%32, MFMA feature
+    // 32 wf + 8 (v/4) + 4 (l/32) + v%4.
+    const int t = xrow;
+    if (t >= valid_rows) return;
+    uint16_t* out = a.out + (tile_r0 + t) * (int64_t)N;
+    if (UP) {
+        // g: v = 0..7 (features 0..15 of the block), u: v + 8 (features 16..31)
+#pragma unroll
+        for (int vg = 0; vg < 2; ++vg) {
+            const int col = nt * (TF / 2) + 16 * wf + 8 * vg + 4 * (lane >> 5);
+            if (col >= N) continue;
+            const int v = 4 * vg;
+            *(uint2*)(out + col) =
+                make_uint2(pack_bf16(silu_mul(acc[v], acc[v + 8]), silu_mul(acc[v + 1], acc[v + 9])),
+                           pack_bf16(silu_mul(acc[v + 2], acc[v + 10]), silu_mul(acc[v + 3], acc[v + 11])));
+        }
+    } else {
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg) {
+            const int col = nt * TF + 32 * wf + 8 * vg + 4 * (lane >> 5);
+            if (col >= N) continue;
+            const int v = 4 * vg;
+            *(uint2*)(out + col) = make_uint2(pack_bf16(row_w * acc[v], row_w * acc[v + 1]),
+                                              pack_bf16(row_w * acc[v + 2], row_w * acc[v + 3]));
+        }
+    }
+}
+
+int m_tiles_upper_small(const GroupArgs& g) {
+    const int64_t rows = g.S + (g.G > g.E ? g.T : 0);
+    return (int)((rows + TT - 1) / TT) + g.G;
+}
+
+}  // namespace
+
+hipError_t launch_up_swiglu_bf16_small(const GroupArgs& g, const void* x, const void* W1,
+                                       const void* W3, const void* Ws1, const void* Ws3, void* h,
+                                       int D, int F, hipStream_t s) {
+    SmallArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
+                (const uint16_t*)Ws1, (const uint16_t*)Ws3, (uint16_t*)h, D, F,
+                (F + TF / 2 - 1) / (TF / 2)};
+    const int64_t blocks = (int64_t)m_tiles_upper_small(g) * a.n_tiles;
+    grouped_gemm_small_kernel<true><<<(unsigned)blocks, NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_bf16_small(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
+                                  void* Yw, int D, int F, hipStream_t s) {
+    SmallArgs a{g, (const uint16_t*)h, (const uint16_t*)W2, nullptr, (const uint16_t*)Ws2, nullptr,
+                (uint16_t*)Yw, D, F, (D + TF - 1) / TF};
+    const int64_t blocks = (int64_t)m_tiles_upper_small(g) * a.n_tiles;
+    grouped_gemm_small_kernel<false><<<(unsigned)blocks, NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

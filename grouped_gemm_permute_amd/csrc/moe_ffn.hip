@@ -48,13 +48,20 @@ moe_status make_layout(int64_t T, int D, int F, int E, int k, int has_shared, mo
     L->counts = take(sizeof(int32_t) * (size_t)E);
     L->offsets = take(sizeof(int32_t) * (size_t)(E + 1));
     L->tile_off = take(sizeof(int32_t) * (size_t)(E + 2));
+    L->tile_off64 = take(sizeof(int32_t) * (size_t)(E + 2));
     L->perm = take(sizeof(int32_t) * (size_t)S);
     L->inv = take(sizeof(int32_t) * (size_t)S);
     L->hist = take(sizeof(int32_t) * (size_t)(E + 1) * (size_t)nb);
     L->h = take(fused ? 0 : esize * (size_t)R * (size_t)F);   // the fused variant keeps h on chip
     L->Y = take(esize * (size_t)R * (size_t)D);
     L->total = off;
-    L->tile_rows = fused ? kFusedTileRows : (dt == MOE_BF16 ? kBf16TileRows : kF32TileRows);
+    // bf16 unfused: groups averaging under one 256-row tile are bound by
+    // streaming their weights; they run on the small-tile kernels.
+    const int G = E + (has_shared ? 1 : 0);
+    L->small_tiles = (!fused && dt == MOE_BF16 && R < (int64_t)kBf16TileRows * G) ? 1 : 0;
+    L->tile_rows = fused ? kFusedTileRows
+                         : (dt == MOE_BF16 ? (L->small_tiles ? kSmallTileRows : kBf16TileRows)
+                                           : kF32TileRows);
     L->hist_blocks = nb;
     return MOE_OK;
 }
@@ -143,6 +150,7 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
     int32_t* counts = (int32_t*)(ws + L.counts);
     int32_t* offsets = (int32_t*)(ws + L.offsets);
     int32_t* tile_off = (int32_t*)(ws + L.tile_off);
+    int32_t* tile_off64 = (int32_t*)(ws + L.tile_off64);
     int32_t* perm = (int32_t*)(ws + L.perm);
     int32_t* inv = (int32_t*)(ws + L.inv);
     int32_t* hist = (int32_t*)(ws + L.hist);
@@ -156,7 +164,7 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
     };
     if (mark(0) != hipSuccess) return MOE_ERR_HIP;
     if (launch_permute(topk_idx, S, E, L.tile_rows, has_shared ? T : 0, counts, offsets, tile_off,
-                       perm, inv, err, hist, L.hist_blocks, stream) != hipSuccess)
+                       perm, inv, err, hist, L.hist_blocks, stream, 64, tile_off64) != hipSuccess)
         return MOE_ERR_HIP;
     if (mark(1) != hipSuccess) return MOE_ERR_HIP;
 
@@ -165,6 +173,9 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
     if (variant == MOE_VARIANT_FUSED) {
         // one launch does up, SwiGLU and down; both timing marks follow it
         e = launch_fused_bf16(g, x, W1, W3, W2, Ws1, Ws3, Ws2, Y, D, F, stream);
+        if (e == hipSuccess) e = mark(2);
+    } else if (dtype == MOE_BF16 && L.small_tiles) {
+        e = launch_up_swiglu_bf16_small(g, x, W1, W3, Ws1, Ws3, h, D, F, stream);
         if (e == hipSuccess) e = mark(2);
     } else if (dtype == MOE_BF16) {
         e = launch_up_swiglu_bf16(g, x, W1, W3, Ws1, Ws3, h, D, F, stream);
@@ -175,7 +186,9 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
         if (e == hipSuccess) e = mark(2);
     }
     if (e == hipSuccess && variant != MOE_VARIANT_FUSED) {
-        if (dtype == MOE_BF16)
+        if (dtype == MOE_BF16 && L.small_tiles)
+            e = launch_down_bf16_small(g, h, W2, Ws2, Y, D, F, stream);
+        else if (dtype == MOE_BF16)
             e = launch_down_bf16(g, h, W2, Ws2, Y, D, F, stream);
         else
             e = launch_down_f32(g, (const float*)h, (const float*)W2, (const float*)Ws2, (float*)Y,

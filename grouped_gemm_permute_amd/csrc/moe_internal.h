@@ -18,10 +18,12 @@ inline int permute_hist_blocks(int64_t S) {
 }
 
 // Stable counting sort of slots by expert (see moe_expert_permute).
-// hist: int32 [(E+1) * nblocks] when nblocks > 0.
+// hist: int32 [(E+1) * nblocks] when nblocks > 0.  tile_off2 (optional,
+// [E+2]) receives the row-tile prefix for tiles of tile_rows2 rows.
 hipError_t launch_permute(const int32_t* idx, int64_t S, int E, int tile_rows, int64_t shared_rows,
                           int32_t* counts, int32_t* offsets, int32_t* tile_off, int32_t* perm,
-                          int32_t* inv, int32_t* err, int32_t* hist, int nblocks, hipStream_t s);
+                          int32_t* inv, int32_t* err, int32_t* hist, int nblocks, hipStream_t s,
+                          int tile_rows2 = 0, int32_t* tile_off2 = nullptr);
 
 // Everything the grouped GEMMs read about the routed groups.
 struct GroupArgs {
@@ -45,6 +47,15 @@ hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* 
 // w(p) the routing weight of the slot in row p (1 for shared rows).
 hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
                             void* Yw, int D, int F, hipStream_t s);
+
+// Small-chunk grouped GEMMs (bf16): 64-row x 64-feature tiles, a 4-deep
+// load ring, for groups too small to fill the GPU with 256-row tiles.
+constexpr int kSmallTileRows = 64;
+hipError_t launch_up_swiglu_bf16_small(const GroupArgs& g, const void* x, const void* W1,
+                                       const void* W3, const void* Ws1, const void* Ws3, void* h,
+                                       int D, int F, hipStream_t s);
+hipError_t launch_down_bf16_small(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
+                                  void* Yw, int D, int F, hipStream_t s);
 
 // Fused up-act-down (bf16): token tiles of kFusedTileRows rows, h kept on
 // chip; writes the same weighted Yw as the down GEMM.  Needs D % 128 == 0,

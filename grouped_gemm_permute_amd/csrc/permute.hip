@@ -50,23 +50,35 @@ __device__ __forceinline__ int key_of(const int32_t* idx, int64_t s, int64_t S, 
     return (e >= 0 && e < E) ? e : E;                // E: invalid id
 }
 
-// Serial prefix sums by one thread: counts/offsets/tile_off/err from cnt[0..E].
-__device__ void finish_scan(const int32_t* cnt, int E, int tile_rows, int64_t shared_rows,
-                            int32_t* counts, int32_t* offsets, int32_t* tile_off, int32_t* err,
+struct TileSpec {
+    int rows;          // tile height
+    int32_t* off;      // [E+2] row-tile prefix, or null
+};
+
+// Serial prefix sums by one thread: counts/offsets/err and up to two row-tile
+// prefixes from cnt[0..E].
+__device__ void finish_scan(const int32_t* cnt, int E, TileSpec ta, TileSpec tb,
+                            int64_t shared_rows, int32_t* counts, int32_t* offsets, int32_t* err,
                             int32_t* run) {
-    int32_t acc = 0, tiles = 0;
+    int32_t acc = 0, tiles_a = 0, tiles_b = 0;
     for (int e = 0; e < E; ++e) {
         const int32_t c = cnt[e];
         counts[e] = c;
         offsets[e] = acc;
-        tile_off[e] = tiles;
+        ta.off[e] = tiles_a;
+        if (tb.off) tb.off[e] = tiles_b;
         if (run) run[e] = acc;
         acc += c;
-        tiles += (c + tile_rows - 1) / tile_rows;
+        tiles_a += (c + ta.rows - 1) / ta.rows;
+        if (tb.off) tiles_b += (c + tb.rows - 1) / tb.rows;
     }
     offsets[E] = acc;
-    tile_off[E] = tiles;
-    tile_off[E + 1] = tiles + (int32_t)((shared_rows + tile_rows - 1) / tile_rows);
+    ta.off[E] = tiles_a;
+    ta.off[E + 1] = tiles_a + (int32_t)((shared_rows + ta.rows - 1) / ta.rows);
+    if (tb.off) {
+        tb.off[E] = tiles_b;
+        tb.off[E + 1] = tiles_b + (int32_t)((shared_rows + tb.rows - 1) / tb.rows);
+    }
     err[0] = cnt[E];
 }
 
@@ -110,8 +122,8 @@ __device__ void scatter_chunk(const int32_t* idx, int64_t c0, int64_t end, int64
 __device__ __forceinline__ int key_bits(int E) { return 32 - __clz(E + 1); }
 
 __global__ __launch_bounds__(kSingleThreads) void permute_single_kernel(
-    const int32_t* __restrict__ idx, int64_t S, int E, int tile_rows, int64_t shared_rows,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ idx, int64_t S, int E, TileSpec ta, TileSpec tb, int64_t shared_rows,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ err) {
     __shared__ int32_t cnt[kMaxExperts + 1];
     __shared__ int32_t run[kMaxExperts];
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(kSingleThreads) void permute_single_kernel(
     __syncthreads();
     for (int64_t s = tid; s < S; s += kSingleThreads) atomicAdd(&cnt[key_of(idx, s, S, E)], 1);
     __syncthreads();
-    if (tid == 0) finish_scan(cnt, E, tile_rows, shared_rows, counts, offsets, tile_off, err, run);
+    if (tid == 0) finish_scan(cnt, E, ta, tb, shared_rows, counts, offsets, err, run);
     __syncthreads();
     const int nbits = key_bits(E);
     for (int64_t c0 = 0; c0 < S; c0 += kSingleThreads)
@@ -146,29 +158,45 @@ __global__ __launch_bounds__(kScatterThreads) void permute_hist_kernel(
 }
 
 // Turns hist into per-(expert, block) start positions and writes the
-// per-expert results.
+// per-expert results.  One thread per expert row; each row is read in
+// batches of 16 independent loads (two passes: totals, then exclusive
+// prefixes plus the expert's start).
 __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
-    int32_t* __restrict__ hist, int nb, int64_t S, int E, int tile_rows, int64_t shared_rows,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ hist, int nb, int64_t S, int E, TileSpec ta, TileSpec tb,
+    int64_t shared_rows, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ err) {
+    constexpr int B = 16;
     __shared__ int32_t cnt[kMaxExperts + 1];
     __shared__ int32_t start[kMaxExperts];
     const int tid = threadIdx.x;
     for (int e = tid; e <= E; e += kScanThreads) {
+        const int32_t* row = hist + (int64_t)e * nb;
         int32_t sum = 0;
-        for (int b = 0; b < nb; ++b) {
-            const int32_t v = hist[(int64_t)e * nb + b];
-            hist[(int64_t)e * nb + b] = sum;
-            sum += v;
+        for (int b0 = 0; b0 < nb; b0 += B) {
+            int32_t v[B];
+#pragma unroll
+            for (int i = 0; i < B; ++i) v[i] = b0 + i < nb ? row[b0 + i] : 0;
+#pragma unroll
+            for (int i = 0; i < B; ++i) sum += v[i];
         }
         cnt[e] = sum;
     }
     __syncthreads();
-    if (tid == 0) finish_scan(cnt, E, tile_rows, shared_rows, counts, offsets, tile_off, err, start);
+    if (tid == 0) finish_scan(cnt, E, ta, tb, shared_rows, counts, offsets, err, start);
     __syncthreads();
     for (int e = tid; e < E; e += kScanThreads) {
-        const int32_t base = start[e];
-        for (int b = 0; b < nb; ++b) hist[(int64_t)e * nb + b] += base;
+        int32_t* row = hist + (int64_t)e * nb;
+        int32_t run = start[e];
+        for (int b0 = 0; b0 < nb; b0 += B) {
+            int32_t v[B];
+#pragma unroll
+            for (int i = 0; i < B; ++i) v[i] = b0 + i < nb ? row[b0 + i] : 0;
+#pragma unroll
+            for (int i = 0; i < B; ++i) {
+                if (b0 + i < nb) row[b0 + i] = run;
+                run += v[i];
+            }
+        }
     }
     const int32_t valid = (int32_t)(S - cnt[E]);
     for (int64_t p = valid + tid; p < S; p += kScanThreads) perm[p] = -1;
@@ -194,15 +222,17 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
 
 hipError_t launch_permute(const int32_t* idx, int64_t S, int E, int tile_rows, int64_t shared_rows,
                           int32_t* counts, int32_t* offsets, int32_t* tile_off, int32_t* perm,
-                          int32_t* inv, int32_t* err, int32_t* hist, int nblocks, hipStream_t s) {
+                          int32_t* inv, int32_t* err, int32_t* hist, int nblocks, hipStream_t s,
+                          int tile_rows2, int32_t* tile_off2) {
+    const TileSpec ta{tile_rows, tile_off}, tb{tile_rows2 > 0 ? tile_rows2 : 1, tile_off2};
     if (nblocks == 0) {
-        permute_single_kernel<<<1, kSingleThreads, 0, s>>>(idx, S, E, tile_rows, shared_rows, counts,
-                                                           offsets, tile_off, perm, inv, err);
+        permute_single_kernel<<<1, kSingleThreads, 0, s>>>(idx, S, E, ta, tb, shared_rows, counts,
+                                                           offsets, perm, inv, err);
         return hipGetLastError();
     }
     permute_hist_kernel<<<nblocks, kScatterThreads, 0, s>>>(idx, S, E, hist);
-    permute_scan_kernel<<<1, kScanThreads, 0, s>>>(hist, nblocks, S, E, tile_rows, shared_rows,
-                                                   counts, offsets, tile_off, perm, err);
+    permute_scan_kernel<<<1, kScanThreads, 0, s>>>(hist, nblocks, S, E, ta, tb, shared_rows,
+                                                   counts, offsets, perm, err);
     permute_scatter_kernel<<<nblocks, kScatterThreads, 0, s>>>(idx, S, E, hist, perm, inv);
     return hipGetLastError();
 }

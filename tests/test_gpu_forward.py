@@ -47,6 +47,9 @@ FULL_CASES = [
     (300, 64, 64, 1, 1, False, "bf16", "uniform"),
     (1500, 192, 320, 6, 3, True, "bf16", "zipf"),
     (1111, 320, 128, 16, 4, False, "bf16", "zipf"),      # empty / tiny experts
+    # groups averaging < 256 rows run on the small-tile kernels
+    (200, 512, 1024, 16, 2, False, "bf16", "zipf"),      # ~25 rows per expert, many empty
+    (64, 768, 1536, 8, 2, True, "bf16", "uniform"),      # layer shape, tiny batch + shared
 ]
 
 
