@@ -76,8 +76,8 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
     const int F = a.F;
     const int NC = F / CH;
 
-    const int mt = xcd_remap(blockIdx.x, gridDim.x);
-    if (mt >= a.g.tile_off[a.g.G]) return;
+    const int mt = xcd_remap_work(blockIdx.x, a.g.tile_off[a.g.G]);
+    if (mt < 0) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const TileGroup tg = find_tile_group(a.g, mt, TT, lane);
@@ -346,14 +346,14 @@ hipError_t launch_fused_bf16(const GroupArgs& g, const void* x, const void* W1, 
     const int64_t rows = g.S + (g.G > g.E ? g.T : 0);
     const unsigned blocks = (unsigned)((rows + TT - 1) / TT + g.G);
     switch (D / 128) {
-        case 1: fused_up_act_down_kernel<1><<<blocks, NT, 0, s>>>(a); break;
-        case 2: fused_up_act_down_kernel<2><<<blocks, NT, 0, s>>>(a); break;
-        case 3: fused_up_act_down_kernel<3><<<blocks, NT, 0, s>>>(a); break;
-        case 4: fused_up_act_down_kernel<4><<<blocks, NT, 0, s>>>(a); break;
-        case 5: fused_up_act_down_kernel<5><<<blocks, NT, 0, s>>>(a); break;
-        case 6: fused_up_act_down_kernel<6><<<blocks, NT, 0, s>>>(a); break;
-        case 7: fused_up_act_down_kernel<7><<<blocks, NT, 0, s>>>(a); break;
-        case 8: fused_up_act_down_kernel<8><<<blocks, NT, 0, s>>>(a); break;
+        case 1: fused_up_act_down_kernel<1><<<grid_for_work(blocks), NT, 0, s>>>(a); break;
+        case 2: fused_up_act_down_kernel<2><<<grid_for_work(blocks), NT, 0, s>>>(a); break;
+        case 3: fused_up_act_down_kernel<3><<<grid_for_work(blocks), NT, 0, s>>>(a); break;
+        case 4: fused_up_act_down_kernel<4><<<grid_for_work(blocks), NT, 0, s>>>(a); break;
+        case 5: fused_up_act_down_kernel<5><<<grid_for_work(blocks), NT, 0, s>>>(a); break;
+        case 6: fused_up_act_down_kernel<6><<<grid_for_work(blocks), NT, 0, s>>>(a); break;
+        case 7: fused_up_act_down_kernel<7><<<grid_for_work(blocks), NT, 0, s>>>(a); break;
+        case 8: fused_up_act_down_kernel<8><<<grid_for_work(blocks), NT, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -90,7 +90,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     const int N = UP ? a.F : a.D;      // output columns
     const int ldw = N;                 // weight row stride (elements)
 
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int bid = xcd_remap_work(blockIdx.x, a.g.tile_off[a.g.G] * a.n_tiles);
+    if (bid < 0) return;
     const int mt = bid / a.n_tiles, nt = bid - mt * a.n_tiles;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -334,7 +335,7 @@ hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* 
     GemmArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, h, D, F, (F + TF / 2 - 1) / (TF / 2)};
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<true><<<(unsigned)blocks, NT, 0, s>>>(a);
+    grouped_gemm_bf16_kernel<true><<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -343,7 +344,7 @@ hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, c
     GemmArgs a{g, (const uint16_t*)h, (const uint16_t*)W2, nullptr, (const uint16_t*)Ws2, nullptr,
                Y, D, F, (D + TF - 1) / TF};
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<false><<<(unsigned)blocks, NT, 0, s>>>(a);
+    grouped_gemm_bf16_kernel<false><<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();
 }
 

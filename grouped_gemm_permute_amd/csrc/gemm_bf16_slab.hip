@@ -1,0 +1,319 @@
+// gemm_bf16_slab.hip -- up+SwiGLU grouped GEMM for small per-expert chunks.
+//
+// Same product as the up GEMM of gemm_bf16.hip (h = bf16(silu(x . W1) *
+// (x . W3)) on the rows of each group), shaped for the regime where every
+// expert sees at most a few hundred rows and streaming the weights is the
+// cost (the "small chunks" that "Triton MoE Kernels & Memory Checkpointing",
+// Part A sections 2 and 6.1, calls the pathological regime).
+//
+// Every byte a workgroup stages passes through its CU's memory pipe, which
+// moves a few tens of bytes per clock; the kernel is bound by the total
+// bytes staged, i.e. by how often each operand is re-read.  A row tile of
+// 32 RB rows is chosen by the host to hold a whole typical group, so each
+// group's weight slab is streamed exactly once, and the token rows (which
+// are small) are the operand re-read once per column slab:
+//
+//  * tile = 32 RB rows x 128 MFMA features = 64 output columns (four MFMA
+//    blocks, each 16 W1 columns followed by the same 16 W3 columns, so
+//    accumulator elements v (g) and v + 8 (u) of a lane pair up);
+//  * 256 threads = 4 wavefronts; wavefront w owns feature block w for all RB
+//    row blocks (RB v_mfma_f32_32x32x16_bf16 accumulators), so the slow
+//    transposed weight reads are not replicated across wavefronts;
+//  * K step 64; a ring of 4 LDS stages (3 for the tallest tiles) filled with
+//    global_load_lds, and the operands of the next stage are read from LDS
+//    while the MFMAs of the current one run; rows past the group's end are clamped to
+//    its last row, which costs the memory pipe next to nothing (all lanes of
+//    an instruction then hit one line) and keeps every wavefront's load count
+//    per stage fixed, so the waits are compile-time counts;
+//  * tiles run n-major so the workgroups of one XCD share their token rows
+//    through its L2.
+#include "mfma_common.h"
+
+namespace moe {
+namespace {
+
+using namespace mfma;
+
+constexpr int FB = 4;                  // MFMA feature blocks per tile (one per wavefront)
+constexpr int TFM = 32 * FB;           // 128 MFMA features
+constexpr int TCOL = TFM / 2;          // 64 output columns
+constexpr int BK = 64;
+constexpr int NT = 256;
+constexpr int X_ROW = BK * 2;          // 128 B per token row
+constexpr int W_ROW = TFM * 2;         // 256 B per k row
+constexpr int W_BYTES = BK * W_ROW;    // 16 KiB
+
+static_assert(NT == 256 && FB == 4 && BK == 64 && W_BYTES == 16384, "index math below assumes these");
+
+struct SlabArgs {
+    GroupArgs g;
+    const uint16_t* x;        // [T, D]
+    const uint16_t* w1;       // [E, D, F]
+    const uint16_t* w3;
+    const uint16_t* ws1;      // shared expert [D, F]
+    const uint16_t* ws3;
+    uint16_t* h;              // [R, F]
+    int D, F;
+    int n_tiles;
+};
+
+template <int RB>
+__global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a) {
+    constexpr int TT = 32 * RB;
+    constexpr int X_BYTES = TT * X_ROW;
+    constexpr int STAGE_BYTES = X_BYTES + W_BYTES;
+    constexpr int PER_STAGE = RB + W_BYTES / 1024 / 4;     // global_load_lds per wavefront per stage
+    // Four stage buffers when they fit in LDS, else three; separate LDS
+    // objects so the compiler sees that reads of one do not alias the
+    // asynchronous loads into another.
+    constexpr int NS = 4 * STAGE_BYTES <= 160 * 1024 ? 4 : 3;
+    __shared__ __attribute__((aligned(1024))) char st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st3[NS == 4 ? STAGE_BYTES : 16];
+
+    const int K = a.D, N = a.F;
+    const int total = a.g.tile_off[a.g.G];
+    const int id = xcd_remap_work(blockIdx.x, total * a.n_tiles);
+    if (id < 0) return;
+    const int nt = id / total, mt = id - nt * total;     // n-major
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const TileGroup tg = find_tile_group(a.g, mt, TT, lane);
+    const int grp = tg.grp;
+    const bool shared = grp >= a.g.E;
+    const int64_t tile_r0 = tg.tile_r0;
+    const int valid_rows = tg.valid_rows;
+    if (valid_rows <= 0) return;
+
+    // ---- token rows: DMA instruction j (0 .. RB-1) of wavefront w fills rows
+    // 8 q .. 8 q + 7 with q = w + 4 j; lane -> row 8 q + lane/8, physical
+    // chunk lane%8 holding logical chunk (lane%8) ^ swz8(row).
+    const char* x_src[RB];
+    {
+        int64_t src_row[RB];
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+            src_row[j] = tile_r0 + min(8 * (wave + 4 * j) + (lane >> 3), valid_rows - 1);
+        if (!shared) {
+            int32_t slot[RB];
+#pragma unroll
+            for (int j = 0; j < RB; ++j) slot[j] = a.g.perm[src_row[j]];
+#pragma unroll
+            for (int j = 0; j < RB; ++j) src_row[j] = slot[j] / a.g.k;
+        } else {
+#pragma unroll
+            for (int j = 0; j < RB; ++j) src_row[j] -= a.g.S;
+        }
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            const int row = 8 * (wave + 4 * j) + (lane >> 3);
+            x_src[j] = (const char*)(a.x + src_row[j] * (int64_t)K + 8 * ((lane & 7) ^ swz8(row)));
+        }
+    }
+    // ---- weight slab [64 k][128 features]: DMA instruction j (0..3) of
+    // wavefront w fills k rows 4 q .. 4 q + 3 with q = w + 4 j; lane -> k row
+    // 4 q + lane/16, physical chunk lane%16 holding logical chunk
+    // cl = phys ^ swz_tr(k) = MFMA features 8 cl .. 8 cl + 7: block cl / 4,
+    // W3 when (cl / 2) is odd, output column 16 (cl / 4) + 8 (cl % 2).
+    const int64_t gstride = (int64_t)a.D * a.F;
+    const char* w_src[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int kr = 4 * (wave + 4 * j) + (lane >> 4);
+        const int cl = (lane & 15) ^ swz_tr(kr);
+        const int kind = (cl >> 1) & 1;
+        int col = nt * TCOL + 16 * (cl >> 2) + 8 * (cl & 1);
+        if (col >= N) col = 0;                 // past the last column: a valid chunk, never stored
+        const uint16_t* base = shared ? (kind ? a.ws3 : a.ws1) : (kind ? a.w3 : a.w1) + grp * gstride;
+        w_src[j] = (const char*)(base + (int64_t)kr * N + col);
+    }
+    const int64_t w_step = (int64_t)BK * N * 2;
+
+    auto issue = [&](int kt, char* st) {
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+            load_lds16(x_src[j] + (int64_t)kt * X_ROW, st + 8 * (wave + 4 * j) * X_ROW);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            load_lds16(w_src[j] + kt * w_step, st + X_BYTES + 4 * (wave + 4 * j) * W_ROW);
+    };
+
+    // ---- operand reads.  Weights (A), transposed: lane = 16 G + s reads
+    // k = 16 ks + 8 (G>>1) + 4 r + s/4, feature 32 w + 16 (G&1) + 4 (s&3).
+    // Rows (B): row 32 j + lane%32, logical chunk 2 ks + lane/32.
+    const int G = lane >> 4, sl = lane & 15;
+    int w_off[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int k = 8 * (G >> 1) + 4 * r + (sl >> 2);
+        const int R = 32 * wave + 16 * (G & 1) + 4 * (sl & 3);
+        w_off[r] = X_BYTES + k * W_ROW + (((R >> 3) ^ swz_tr(k)) << 4) + 8 * ((R >> 2) & 1);
+    }
+    const int xl = lane & 31;
+
+    f32x16_t acc[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) acc[j] = f32x16_t{};
+
+    struct Frags {
+        bf16x8_t w[BK / 16], x[BK / 16][RB];
+    };
+    auto read_frags = [&](const char* st, Frags& f) {
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            f.w[ks] = cat_bf16(read_tr(st + w_off[0] + ks * 16 * W_ROW),
+                               read_tr(st + w_off[1] + ks * 16 * W_ROW));
+#pragma unroll
+            for (int j = 0; j < RB; ++j) {
+                const int row = 32 * j + xl;
+                const int c = (2 * ks + (lane >> 5)) ^ swz8(row);
+                f.x[ks][j] =
+                    __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + row * X_ROW + (c << 4)));
+            }
+        }
+    };
+    auto mfmas = [&](const Frags& f) {
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+            for (int j = 0; j < RB; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[ks], f.x[ks][j], acc[j], 0, 0, 0);
+    };
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+
+    // ---- ring of NS stages, software-pipelined one stage deep in registers.
+    // Step s (its operands fc already in registers):
+    //   wait until stage s+1 has landed (at most NS-3 later stages of this
+    //   wavefront's loads outstanding) and fc's reads have returned, barrier;
+    //   issue the loads of stage s+NS-1 into the buffer of stage s-1;
+    //   read stage s+1's operands into fn;
+    //   MFMAs on fc -- the reads of fn land under them.
+    // The buffer of stage s-1 is free at step s: its operands were read in
+    // step s-2 and consumed by the MFMAs of step s-1, which every wavefront
+    // finished before arriving at this barrier.  Loads past the last stage
+    // re-read the last stage (into buffers never computed on), so the number
+    // of loads per stage stays fixed; operands read past the last stage are
+    // never used.
+    const int KT = K / BK;
+    constexpr int WAIT_N = (NS - 3) * PER_STAGE;
+    auto wait_stage = [] {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(WAIT_N, 0));
+        __builtin_amdgcn_s_barrier();
+    };
+    auto step = [&](Frags& fc, Frags& fn, const char* nxt, char* dma, int kl) {
+        wait_stage();
+        fence();
+        issue(kl, dma);
+        read_frags(nxt, fn);
+        fence();
+        mfmas(fc);
+        fence();
+    };
+    Frags fa, fb;
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+        issue(min(i, KT - 1), i == 0 ? st0 : i == 1 ? st1 : st2);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * PER_STAGE, 15));   // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    fence();
+    read_frags(st0, fa);
+    fence();
+    int kt = 0;
+    if constexpr (NS == 4) {
+        // buffers rotate with period 4, operand sets with period 2
+        for (; kt + 4 <= KT; kt += 4) {
+            step(fa, fb, st1, st3, min(kt + 3, KT - 1));
+            step(fb, fa, st2, st0, min(kt + 4, KT - 1));
+            step(fa, fb, st3, st1, min(kt + 5, KT - 1));
+            step(fb, fa, st0, st2, min(kt + 6, KT - 1));
+        }
+        if (kt < KT) {
+            step(fa, fb, st1, st3, KT - 1);
+            if (kt + 1 < KT) {
+                step(fb, fa, st2, st0, KT - 1);
+                if (kt + 2 < KT) step(fa, fb, st3, st1, KT - 1);
+            }
+        }
+    } else {
+        // buffers rotate with period 3, operand sets with period 2
+        for (; kt + 6 <= KT; kt += 6) {
+            step(fa, fb, st1, st2, min(kt + 2, KT - 1));
+            step(fb, fa, st2, st0, min(kt + 3, KT - 1));
+            step(fa, fb, st0, st1, min(kt + 4, KT - 1));
+            step(fb, fa, st1, st2, min(kt + 5, KT - 1));
+            step(fa, fb, st2, st0, min(kt + 6, KT - 1));
+            step(fb, fa, st0, st1, min(kt + 7, KT - 1));
+        }
+        if (kt < KT) {
+            step(fa, fb, st1, st2, KT - 1);
+            if (kt + 1 < KT) {
+                step(fb, fa, st2, st0, KT - 1);
+                if (kt + 2 < KT) {
+                    step(fa, fb, st0, st1, KT - 1);
+                    if (kt + 3 < KT) {
+                        step(fb, fa, st1, st2, KT - 1);
+                        if (kt + 4 < KT) step(fa, fb, st2, st0, KT - 1);
+                    }
+                }
+            }
+        }
+    }
+    wait_vmem();
+
+    // ---- epilogue.  acc[j] element v of lane l: row 32 j + l%32, MFMA
+    // feature 32 w + 8 (v/4) + 4 (l/32) + v%4; g at v < 8, its u at v + 8.
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+        const int t = 32 * j + xl;
+        if (t >= valid_rows) continue;
+        uint16_t* out = a.h + (tile_r0 + t) * (int64_t)N;
+#pragma unroll
+        for (int vg = 0; vg < 2; ++vg) {
+            const int col = nt * TCOL + 16 * wave + 8 * vg + 4 * (lane >> 5);
+            if (col >= N) continue;
+            const int v = 4 * vg;
+            const f32x16_t& c = acc[j];
+            *(uint2*)(out + col) =
+                make_uint2(pack_bf16(silu_mul(c[v], c[v + 8]), silu_mul(c[v + 1], c[v + 9])),
+                           pack_bf16(silu_mul(c[v + 2], c[v + 10]), silu_mul(c[v + 3], c[v + 11])));
+        }
+    }
+}
+
+template <int RB>
+hipError_t launch_rb(const SlabArgs& a, hipStream_t s) {
+    const int64_t rows = a.g.S + (a.g.G > a.g.E ? a.g.T : 0);
+    const int64_t m_upper = (rows + 32 * RB - 1) / (32 * RB) + a.g.G;
+    const int64_t blocks = m_upper * a.n_tiles;
+    up_swiglu_slab_kernel<RB><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int slab_row_blocks(int64_t rows, int groups) {
+    // a tile of 32 RB rows holds a group of 1.25x the average size
+    const int64_t avg = groups > 0 ? rows / groups : rows;
+    const int64_t rb = (avg * 5 / 4 + 31) / 32;
+    return (int)(rb < 1 ? 1 : (rb > kSlabMaxRowBlocks ? kSlabMaxRowBlocks : rb));
+}
+
+hipError_t launch_up_swiglu_bf16_slab(const GroupArgs& g, int rb, const void* x, const void* W1,
+                                      const void* W3, const void* Ws1, const void* Ws3, void* h,
+                                      int D, int F, hipStream_t s) {
+    SlabArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
+               (const uint16_t*)Ws1, (const uint16_t*)Ws3, (uint16_t*)h, D, F,
+               (F + TCOL - 1) / TCOL};
+    switch (rb) {
+        case 1: return launch_rb<1>(a, s);
+        case 2: return launch_rb<2>(a, s);
+        case 3: return launch_rb<3>(a, s);
+        case 4: return launch_rb<4>(a, s);
+        case 5: return launch_rb<5>(a, s);
+        case 6: return launch_rb<6>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

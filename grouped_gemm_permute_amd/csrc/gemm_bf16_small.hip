@@ -64,9 +64,9 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallAr
     const int K = UP ? a.D : a.F;
     const int N = UP ? a.F : a.D;
     const int total = a.g.tile_off[a.g.G];
-    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    const int id = xcd_remap_work(blockIdx.x, total * a.n_tiles);
+    if (id < 0) return;
     const int nt = id / total, mt = id - nt * total;     // n-major
-    if (nt >= a.n_tiles) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wf = wave >> 1, wt = wave & 1;
@@ -167,25 +167,30 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallAr
     // the buffer step kt-1 just released (after the barrier).  Loads past
     // the last stage re-read the last stage (never computed on).
     const int KT = K / BK;
-    auto wait_stage = [] { __builtin_amdgcn_s_waitcnt(0x0F78); };   // <= 8 DMA (2 stages) left
+    // Wait until at most 8 of this wavefront's loads (two stages) are
+    // outstanding, i.e. stage kt has landed, then a bare s_barrier:
+    // __syncthreads() would also wait for every outstanding load and drain the
+    // ring.  The barrier also orders the buffer reuse: every wavefront's
+    // reads of the buffer refilled next were consumed by its MFMAs before it
+    // arrived.
+    auto wait_stage = [] {
+        __builtin_amdgcn_s_waitcnt(0x0F78);
+        __builtin_amdgcn_s_barrier();
+    };
     issue(0, st0);
     issue(min(1, KT - 1), st1);
     issue(min(2, KT - 1), st2);
     for (int kt = 0; kt < KT; kt += 4) {
         wait_stage();
-        __syncthreads();
         issue(min(kt + 3, KT - 1), st3);
         compute(st0);
         wait_stage();
-        __syncthreads();
         issue(min(kt + 4, KT - 1), st0);
         if (kt + 1 < KT) compute(st1);
         wait_stage();
-        __syncthreads();
         issue(min(kt + 5, KT - 1), st1);
         if (kt + 2 < KT) compute(st2);
         wait_stage();
-        __syncthreads();
         issue(min(kt + 6, KT - 1), st2);
         if (kt + 3 < KT) compute(st3);
     }
@@ -233,7 +238,7 @@ hipError_t launch_up_swiglu_bf16_small(const GroupArgs& g, const void* x, const 
                 (const uint16_t*)Ws1, (const uint16_t*)Ws3, (uint16_t*)h, D, F,
                 (F + TF / 2 - 1) / (TF / 2)};
     const int64_t blocks = (int64_t)m_tiles_upper_small(g) * a.n_tiles;
-    grouped_gemm_small_kernel<true><<<(unsigned)blocks, NT, 0, s>>>(a);
+    grouped_gemm_small_kernel<true><<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -242,7 +247,7 @@ hipError_t launch_down_bf16_small(const GroupArgs& g, const void* h, const void*
     SmallArgs a{g, (const uint16_t*)h, (const uint16_t*)W2, nullptr, (const uint16_t*)Ws2, nullptr,
                 (uint16_t*)Yw, D, F, (D + TF - 1) / TF};
     const int64_t blocks = (int64_t)m_tiles_upper_small(g) * a.n_tiles;
-    grouped_gemm_small_kernel<false><<<(unsigned)blocks, NT, 0, s>>>(a);
+    grouped_gemm_small_kernel<false><<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();
 }
 

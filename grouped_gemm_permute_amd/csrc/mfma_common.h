@@ -47,10 +47,29 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
     return x * per + min(x, rem) + i;
 }
 
+// The same for a grid sized from an upper bound on the tile count: the
+// `work` tiles that exist (known only on the device) are spread evenly over
+// the XCDs, each XCD taking a contiguous range; returns -1 for a workgroup
+// with no tile.  The grid must hold at least 8 * ceil(work / 8) workgroups
+// (grid_for_work).
+__device__ __forceinline__ int xcd_remap_work(int bid, int work) {
+    const int x = bid & 7, i = bid >> 3;
+    const int per = work >> 3, rem = work & 7;
+    if (i >= per + (x < rem ? 1 : 0)) return -1;
+    return x * per + min(x, rem) + i;
+}
+
 // 16 bytes per lane global -> LDS; the wavefront's 64 lanes fill 1 KiB of
 // LDS starting at `lds` (wave-uniform), lane i at lds + 16 i.
 __device__ __forceinline__ void load_lds16(const void* g, char* lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// s_waitcnt immediate (gfx9 encoding): at most vm vector-memory and lgkm
+// LDS/scalar operations of this wavefront outstanding (vm up to 63, lgkm up
+// to 15; 15 leaves the LDS counter unchecked).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
 }
 
 // Wait until this wavefront's global_load_lds transfers (vector memory) have

@@ -58,9 +58,12 @@ moe_status make_layout(int64_t T, int D, int F, int E, int k, int has_shared, mo
     // bf16 unfused: groups averaging under one 256-row tile are bound by
     // streaming their weights; they run on the small-tile kernels.
     const int G = E + (has_shared ? 1 : 0);
+    // Their up GEMM tiles hold a whole typical group (tile_off); the down
+    // GEMM runs on 64-row tiles (tile_off64).
     L->small_tiles = (!fused && dt == MOE_BF16 && R < (int64_t)kBf16TileRows * G) ? 1 : 0;
     L->tile_rows = fused ? kFusedTileRows
-                         : (dt == MOE_BF16 ? (L->small_tiles ? kSmallTileRows : kBf16TileRows)
+                         : (dt == MOE_BF16 ? (L->small_tiles ? 32 * slab_row_blocks(R, G)
+                                                             : kBf16TileRows)
                                            : kF32TileRows);
     L->hist_blocks = nb;
     return MOE_OK;
@@ -175,7 +178,7 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
         e = launch_fused_bf16(g, x, W1, W3, W2, Ws1, Ws3, Ws2, Y, D, F, stream);
         if (e == hipSuccess) e = mark(2);
     } else if (dtype == MOE_BF16 && L.small_tiles) {
-        e = launch_up_swiglu_bf16_small(g, x, W1, W3, Ws1, Ws3, h, D, F, stream);
+        e = launch_up_swiglu_bf16_slab(g, L.tile_rows / 32, x, W1, W3, Ws1, Ws3, h, D, F, stream);
         if (e == hipSuccess) e = mark(2);
     } else if (dtype == MOE_BF16) {
         e = launch_up_swiglu_bf16(g, x, W1, W3, Ws1, Ws3, h, D, F, stream);
@@ -186,8 +189,11 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
         if (e == hipSuccess) e = mark(2);
     }
     if (e == hipSuccess && variant != MOE_VARIANT_FUSED) {
-        if (dtype == MOE_BF16 && L.small_tiles)
-            e = launch_down_bf16_small(g, h, W2, Ws2, Y, D, F, stream);
+        if (dtype == MOE_BF16 && L.small_tiles) {
+            GroupArgs g64 = g;
+            g64.tile_off = tile_off64;
+            e = launch_down_bf16_small(g64, h, W2, Ws2, Y, D, F, stream);
+        }
         else if (dtype == MOE_BF16)
             e = launch_down_bf16(g, h, W2, Ws2, Y, D, F, stream);
         else

@@ -25,6 +25,10 @@ hipError_t launch_permute(const int32_t* idx, int64_t S, int E, int tile_rows, i
                           int32_t* inv, int32_t* err, int32_t* hist, int nblocks, hipStream_t s,
                           int tile_rows2 = 0, int32_t* tile_off2 = nullptr);
 
+// Grid for a kernel whose `upper` tiles (an upper bound) are spread over the
+// 8 XCDs by xcd_remap_work: a multiple of 8 no smaller than upper.
+inline unsigned grid_for_work(int64_t upper) { return (unsigned)((upper + 7) / 8 * 8); }
+
 // Everything the grouped GEMMs read about the routed groups.
 struct GroupArgs {
     const int32_t* offsets;   // [E+1] routed row starts
@@ -48,9 +52,16 @@ hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* 
 hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
                             void* Yw, int D, int F, hipStream_t s);
 
-// Small-chunk grouped GEMMs (bf16): 64-row x 64-feature tiles, a 4-deep
-// load ring, for groups too small to fill the GPU with 256-row tiles.
+// Small-chunk grouped GEMMs (bf16), for groups too small to fill the GPU
+// with 256-row tiles.  The up GEMM runs on row tiles of 32 * rb rows that hold
+// a whole typical group (rb from slab_row_blocks), each weight slab streamed
+// once; the down GEMM on 64-row x 64-feature tiles with a 4-deep load ring.
 constexpr int kSmallTileRows = 64;
+constexpr int kSlabMaxRowBlocks = 6;
+int slab_row_blocks(int64_t rows, int groups);
+hipError_t launch_up_swiglu_bf16_slab(const GroupArgs& g, int rb, const void* x, const void* W1,
+                                      const void* W3, const void* Ws1, const void* Ws3, void* h,
+                                      int D, int F, hipStream_t s);
 hipError_t launch_up_swiglu_bf16_small(const GroupArgs& g, const void* x, const void* W1,
                                        const void* W3, const void* Ws1, const void* Ws3, void* h,
                                        int D, int F, hipStream_t s);

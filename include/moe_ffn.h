@@ -73,7 +73,7 @@ typedef struct moe_ws_layout {
     size_t counts;      /* int32 [E] rows per expert */
     size_t offsets;     /* int32 [E+1] exclusive prefix sum of counts */
     size_t tile_off;    /* int32 [E+2] prefix sum of ceil(rows/tile_rows), shared group last */
-    size_t tile_off64;  /* int32 [E+2] the same prefix for 64-row tiles */
+    size_t tile_off64;  /* int32 [E+2] the same prefix for 64-row tiles (small-chunk down GEMM) */
     size_t perm;        /* int32 [T*k] sorted position -> slot t*k+j (-1 past the valid rows) */
     size_t inv;         /* int32 [T*k] slot -> sorted position (-1 for an invalid slot) */
     size_t hist;        /* int32 scratch of the multi-block permute */
@@ -81,16 +81,18 @@ typedef struct moe_ws_layout {
     size_t Y;           /* [R, D] per-row expert outputs times their routing weight, dtype of the call */
     int32_t tile_rows;  /* row-tile height of the grouped GEMMs (tile_off's divisor) */
     int32_t hist_blocks;/* number of slot blocks of the multi-block permute (0: single block) */
-    int32_t small_tiles;/* 1: the call uses the small-chunk kernels (64-row x 64-column tiles,
-                           chosen when the groups average fewer than 256 rows), 0: 256-row tiles */
+    int32_t small_tiles;/* 1: the call uses the small-chunk kernels, chosen when the groups
+                           average fewer than 256 rows: the up GEMM on tiles of tile_rows rows
+                           (a multiple of 32 sized to hold a typical group), the down GEMM on
+                           64-row tiles; 0: 256-row tiles */
 } moe_ws_layout;
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *moe_status_string(moe_status status);
 
 /* Row-tile height the grouped GEMMs of (dtype, variant) use for large
- * groups (bf16 unfused: 256; fused: 64; fp32: 64).  Small groups use 64-row
- * tiles; moe_ffn_workspace_layout reports the value a given shape uses. */
+ * groups (bf16 unfused: 256; fused: 64; fp32: 64).  Small groups use other
+ * heights; moe_ffn_workspace_layout reports the value a given shape uses. */
 int moe_ffn_tile_rows(moe_dtype dtype, moe_variant variant);
 
 /*

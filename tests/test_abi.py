@@ -50,6 +50,9 @@ def test_workspace_layout_is_aligned_and_sized():
     assert L.workspace_size(32768, 768, 1536, 8, 2, True, torch.bfloat16) == lay["total"]
     small = L.workspace_layout(512, 768, 1536, 8, 2, False, torch.bfloat16)
     assert small["hist_blocks"] == 0
+    # 128 rows per expert on average: up tiles of 160 rows hold a whole group
+    assert small["small_tiles"] == 1 and small["tile_rows"] == 160
+    assert lay["small_tiles"] == 0 and lay["tile_rows"] == 256
 
 
 def _fwd(**over):

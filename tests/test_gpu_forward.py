@@ -50,6 +50,8 @@ FULL_CASES = [
     # groups averaging < 256 rows run on the small-tile kernels
     (200, 512, 1024, 16, 2, False, "bf16", "zipf"),      # ~25 rows per expert, many empty
     (64, 768, 1536, 8, 2, True, "bf16", "uniform"),      # layer shape, tiny batch + shared
+    (300, 128, 320, 4, 2, False, "bf16", "uniform"),     # up tiles of 192 rows, one per expert
+    (1000, 64, 128, 32, 3, False, "bf16", "zipf"),       # 128-row up tiles, skewed: multi-tile groups
 ]
 
 
