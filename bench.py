@@ -42,16 +42,20 @@ KERNEL_SOURCES = {             # the source each stage's kernel is built from
     "down": "grouped_gemm_permute_amd/csrc/gemm_bf16.hip",
     "combine": "grouped_gemm_permute_amd/csrc/combine.hip",
 }
+SMALL_SOURCES = {              # groups averaging under 256 rows (small_tiles)
+    "up_swiglu": "grouped_gemm_permute_amd/csrc/gemm_bf16_slab.hip",
+    "down": "grouped_gemm_permute_amd/csrc/gemm_bf16_small.hip",
+}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash(stage: str, variant: str = "unfused") -> str:
+def source_hash(stage: str, variant: str = "unfused", small: bool = False) -> str:
     """Hash of the sources a kernel is built from (stale counters are not used)."""
     h = hashlib.sha256()
-    src = KERNEL_SOURCES[stage]
+    src = SMALL_SOURCES.get(stage, KERNEL_SOURCES[stage]) if small else KERNEL_SOURCES[stage]
     if variant == "fused" and stage == "up_swiglu":
         src = "grouped_gemm_permute_amd/csrc/fused_bf16.hip"
     for rel in (src, "grouped_gemm_permute_amd/csrc/mfma_common.h",
@@ -98,14 +102,19 @@ def stage_work(w, counts):
     rows = w.T * w.k + (w.T if w.shared else 0)
     groups = int(sum(1 for c in counts if c > 0)) + (1 if w.shared else 0)
     wbytes = w.D * w.F * b
+    S = w.T * w.k
     return {
-        "permute": {"flop": 0, "bytes": w.T * w.k * 4 * 3 + 4 * (3 * w.E + 3)},
+        # topk_idx in; counts, offsets, tile prefixes, perm and inv out
+        "permute": {"flop": 0, "bytes": S * 4 * 3 + 4 * (4 * w.E + 6)},
+        # x once, [W1|W3] of every active group, h out
         "up_swiglu": {"flop": 4 * w.D * w.F * rows,
                       "bytes": w.T * w.D * b + 2 * wbytes * groups + rows * w.F * b},
+        # h, W2 of every active group, routing weights, weighted Yw out (storage dtype)
         "down": {"flop": 2 * w.D * w.F * rows,
-                 "bytes": rows * w.F * b + wbytes * groups + rows * w.D * 4},
-        "combine": {"flop": 2 * w.k * w.D * w.T,
-                    "bytes": rows * w.D * 4 + w.T * w.k * 8 + w.T * w.D * b},
+                 "bytes": rows * w.F * b + wbytes * groups + S * 4 + rows * w.D * b},
+        # Yw and inv in, y out
+        "combine": {"flop": w.k * w.D * w.T,
+                    "bytes": rows * w.D * b + S * 4 + w.T * w.D * b},
     }
 
 
@@ -117,7 +126,7 @@ def path_bytes(w, counts):
     return 2 * w.T * w.D * b + w.T * w.k * 8 + 3 * w.D * w.F * b * groups
 
 
-def load_traffic(workload_name, key):
+def load_traffic(workload_name, key, small=False):
     """Counter-derived HBM bytes per launch ("variant:stage" key), if
     profiles/traffic.json holds a figure taken from the current kernel
     source; otherwise None."""
@@ -129,7 +138,7 @@ def load_traffic(workload_name, key):
     except (OSError, ValueError):
         return None
     stage = key.split(":")[-1]
-    if not rec or rec.get("source_sha") != source_hash(stage, key.split(":")[0]):
+    if not rec or rec.get("source_sha") != source_hash(stage, key.split(":")[0], small):
         return None
     return rec.get("bytes_per_launch")
 
@@ -290,7 +299,9 @@ def main():
         ach = work[dom]["bytes"] / sec / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = load_traffic(w.name, f"{args.variant}:{dom}")
+    small = bool(gg.workspace_layout(w.T, w.D, w.F, w.E, w.k, w.shared, dt,
+                                     args.variant)["small_tiles"])
+    roof["traffic"] = load_traffic(w.name, f"{args.variant}:{dom}", small)
     roof["kernel"] = "fused_up_act_down" if args.variant == "fused" else dom
     roof["launch_ms"] = round(stage_ms[dom], 5)
     roof["algorithmic"] = work[dom]["flop"] if mfma_bound else work[dom]["bytes"]
