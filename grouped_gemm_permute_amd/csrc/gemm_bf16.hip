@@ -22,19 +22,21 @@
 //  * the MFMA computes the transposed tile C^T = W^T . X^T: its A operand is
 //    a 32-feature block of the weights, its B operand a 32-token block of
 //    rows, so each lane ends with 4 consecutive output features of one token
-//    and stores 8 bytes (h, bf16) or 16 bytes (Y, fp32) at a time;
+//    and stores 8 bytes at a time;
 //  * workgroup tile 256 tokens x 256 MFMA features (up: 128 W1 + 128 W3
-//    columns of the same 128 outputs), K step 64, wave tile 128 x 128 =
-//    4 x 4 v_mfma_f32_32x32x16_bf16 accumulators;
-//  * both tiles go global -> LDS with global_load_lds (16 bytes per lane, no
-//    registers), double-buffered (2 x 64 KiB); the loads of step k+1 are in
-//    flight while step k computes;
+//    columns of the same 128 outputs); wavefront w owns features
+//    64 w .. 64 w + 63 of all 256 tokens: 2 x 8 v_mfma_f32_32x32x16_bf16
+//    accumulators.  Spreading the wavefronts over the features rather than
+//    2 x 2 halves the slow transposed weight reads per MFMA;
+//  * K step 32; both tiles go global -> LDS with global_load_lds (16 bytes
+//    per lane, no registers) into a ring of 4 stages (4 x 32 KiB): up to
+//    three stages are in flight while one computes;
 //  * token rows are K-contiguous in memory and in LDS (read with
 //    ds_read_b128); the weights stay [K][N] (N contiguous) in LDS and the
 //    MFMA's K-consecutive operand is produced by ds_read_b64_tr_b16, which
 //    hands each lane 4 consecutive K values of its own column;
-//  * LDS rows are XOR-swizzled in 16-byte chunks (token rows by
-//    (row ^ row/8) & 7, weight rows by 4 (k & 3)); since global_load_lds
+//  * LDS rows are XOR-swizzled in 16-byte chunks (64-byte token rows by
+//    (row / 4) & 3, 512-byte weight rows by 4 (k & 3)); since global_load_lds
 //    writes each wavefront's 1 KiB contiguously, the swizzle is applied by
 //    choosing which global chunk each lane fetches.
 //
@@ -42,7 +44,7 @@
 // tile_off[g+1]-1 (computed by the permute on the device), the grid is sized
 // by the host from an upper bound, and workgroups past tile_off[G] exit, so
 // no host synchronisation is needed.  Rows past a group's end are clamped
-// to its last row on load and never stored.
+// to their group's last row on load and never stored.
 #include "mfma_common.h"
 
 namespace moe {
@@ -52,18 +54,19 @@ using namespace mfma;
 
 constexpr int TT = kBf16TileRows;   // 256 tokens (rows) per tile
 constexpr int TF = 256;             // MFMA features per tile (up: 128 g + 128 u)
-constexpr int BK = 64;
+constexpr int BK = 32;
 constexpr int NT = 256;
-constexpr int X_BYTES = TT * BK * 2;                 // 32 KiB token tile
-constexpr int W_BYTES = BK * TF * 2;                 // 32 KiB weight tile
-constexpr int STAGE_BYTES = X_BYTES + W_BYTES;
-constexpr int X_ROW = BK * 2;                        // 128 B per token row
+constexpr int X_ROW = BK * 2;                        // 64 B per token row
+constexpr int X_BYTES = TT * X_ROW;                  // 16 KiB token tile
 constexpr int W_ROW = TF * 2;                        // 512 B per k row
+constexpr int W_BYTES = BK * W_ROW;                  // 16 KiB weight tile
+constexpr int STAGE_BYTES = X_BYTES + W_BYTES;       // 32 KiB
 
-static_assert(TT == 256 && TF == 256 && BK == 64 && NT == 256, "index math below assumes these");
+static_assert(TT == 256 && TF == 256 && BK == 32 && NT == 256, "index math below assumes these");
 
-__device__ __forceinline__ int swz_x(int row) { return swz8(row); }
-__device__ __forceinline__ int swz_w(int k) { return swz_tr(k); }
+// 64-byte token rows (4 chunks): 16 consecutive rows read at one logical
+// chunk hit 16 distinct bank groups.
+__device__ __forceinline__ int swz_x(int row) { return (row >> 2) & 3; }
 
 struct GemmArgs {
     GroupArgs g;
@@ -79,12 +82,13 @@ struct GemmArgs {
 
 template <bool UP>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs a) {
-    // Two stage buffers as separate LDS objects: every access names its buffer
-    // statically, so the compiler knows reads of one buffer do not alias the
-    // asynchronous global_load_lds writes into the other and does not wait
-    // for them.
-    __shared__ __attribute__((aligned(1024))) char lds0[STAGE_BYTES];   // 64 KiB
-    __shared__ __attribute__((aligned(1024))) char lds1[STAGE_BYTES];   // 64 KiB
+    // Four stage buffers as separate LDS objects: every access names its
+    // buffer statically, so the compiler knows reads of one buffer do not
+    // alias the asynchronous global_load_lds writes into the others.
+    __shared__ __attribute__((aligned(1024))) char st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st3[STAGE_BYTES];
 
     const int K = UP ? a.D : a.F;      // reduction length
     const int N = UP ? a.F : a.D;      // output columns
@@ -95,11 +99,9 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     const int mt = bid / a.n_tiles, nt = bid - mt * a.n_tiles;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wf = wave >> 1, wt = wave & 1;   // wave's feature half, token half
 
     // ---- the group owning row tile mt, and the tile's rows.
-    const int32_t* tile_off = a.g.tile_off;
-    if (mt >= tile_off[a.g.G]) return;
+    if (mt >= a.g.tile_off[a.g.G]) return;
     const TileGroup tg = find_tile_group(a.g, mt, TT, lane);
     const int grp = tg.grp;
     const bool shared = grp >= a.g.E;
@@ -107,57 +109,65 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     const int valid_rows = tg.valid_rows;
     if (valid_rows <= 0) return;       // only if tile_off disagrees with offsets
 
-    // ---- token tile sources: wave instruction j fills LDS rows 64 wave + 8 j .. +7;
-    // lane -> row 64 wave + 8 j + lane/8, physical chunk lane%8.  Routed rows of
-    // the up GEMM gather token perm[p] / k (all eight index loads in flight at
+    // ---- token tile sources: DMA instruction j (0..3) of wavefront w fills
+    // rows 64 w + 16 j .. +15; lane -> row 64 w + 16 j + lane/4, physical
+    // chunk lane%4 holding logical chunk (lane%4) ^ swz_x(row).  Routed rows of
+    // the up GEMM gather token perm[p] / k (all index loads in flight at
     // once); shared rows read token p - S; the down GEMM reads row p of h.
-    int64_t src_row[8];
-    if (UP && !shared) {
-        int32_t slot[8];
+    const char* x_src[4];
+    {
+        int64_t src_row[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            slot[j] = a.g.perm[tile_r0 + min(64 * wave + 8 * j + (lane >> 3), valid_rows - 1)];
+        for (int j = 0; j < 4; ++j)
+            src_row[j] = tile_r0 + min(64 * wave + 16 * j + (lane >> 2), valid_rows - 1);
+        if (UP && !shared) {
+            int32_t slot[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) src_row[j] = slot[j] / a.g.k;
-    } else {
+            for (int j = 0; j < 4; ++j) slot[j] = a.g.perm[src_row[j]];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            src_row[j] = tile_r0 + min(64 * wave + 8 * j + (lane >> 3), valid_rows - 1) -
-                         (UP ? a.g.S : 0);
-    }
-    // Down GEMM: routing weight of each of this lane's 4 output rows (1 on shared rows).
-    float row_w[4] = {1.f, 1.f, 1.f, 1.f};
-    if (!UP && !shared) {
+            for (int j = 0; j < 4; ++j) src_row[j] = slot[j] / a.g.k;
+        } else if (UP) {
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj) {
-            const int t = min(128 * wt + 32 * nj + (lane & 31), valid_rows - 1);
-            row_w[nj] = a.g.topk_w[a.g.perm[tile_r0 + t]];
+            for (int j = 0; j < 4; ++j) src_row[j] -= a.g.S;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 64 * wave + 16 * j + (lane >> 2);
+            x_src[j] = (const char*)(a.a + src_row[j] * (int64_t)K + 8 * ((lane & 3) ^ swz_x(row)));
         }
     }
-    const char* x_src[8];
+    // Down GEMM: routing weight of each of this lane's 8 output rows (1 on shared rows).
+    float row_w[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int row = 64 * wave + 8 * j + (lane >> 3);
-        const int c = (lane & 7) ^ swz_x(row);
-        x_src[j] = (const char*)(a.a + src_row[j] * (int64_t)K + 8 * c);
+    for (int nj = 0; nj < 8; ++nj) row_w[nj] = 1.f;
+    if (!UP && !shared) {
+        int32_t slot[8];
+#pragma unroll
+        for (int nj = 0; nj < 8; ++nj)
+            slot[nj] = a.g.perm[tile_r0 + min(32 * nj + (lane & 31), valid_rows - 1)];
+#pragma unroll
+        for (int nj = 0; nj < 8; ++nj) row_w[nj] = a.g.topk_w[slot[nj]];
     }
 
-    // ---- weight tile sources: wave instruction j fills k rows 16 wave + 2 j, +1;
-    // lane -> row 16 wave + 2 j + lane/32, physical chunk lane%32.
+    // ---- weight tile sources: DMA instruction j (0..3) of wavefront w fills
+    // k rows 8 w + 2 j, +1; lane -> k row 8 w + 2 j + lane/32, physical chunk
+    // lane%32 holding logical chunk cl = phys ^ swz_tr(k) = MFMA features
+    // 8 cl .. 8 cl + 7.  Up: wavefront block wb = cl / 8, g when (cl / 4) is
+    // even, u when odd, output column 32 wb + 8 (cl % 4) of the tile's 128.
     const int64_t gstride = (int64_t)a.D * a.F;
-    const char* w_src[8];
+    const char* w_src[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int kr = 16 * wave + 2 * j + (lane >> 5);
-        const int c = (lane & 31) ^ swz_w(kr);          // logical chunk: 8 feature columns
+    for (int j = 0; j < 4; ++j) {
+        const int kr = 8 * wave + 2 * j + (lane >> 5);
+        const int cl = (lane & 31) ^ swz_tr(kr);
         int col;
         const uint16_t* base;
         if (UP) {
-            const int half = c >> 4, kind = (c >> 3) & 1;   // kind 0: W1 (g), 1: W3 (u)
-            col = nt * (TF / 2) + half * 64 + (c & 7) * 8;
+            const int kind = (cl >> 2) & 1;
+            col = nt * (TF / 2) + 32 * (cl >> 3) + 8 * (cl & 3);
             base = shared ? (kind ? a.bs1 : a.bs0) : (kind ? a.b1 : a.b0) + grp * gstride;
         } else {
-            col = nt * TF + c * 8;
+            col = nt * TF + 8 * cl;
             base = shared ? a.bs0 : a.b0 + grp * gstride;
         }
         if (col >= N) col = 0;                 // past the last column: a valid chunk, never stored
@@ -165,160 +175,197 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     }
     const int64_t w_step = (int64_t)BK * ldw * 2;      // bytes per K step in the weights
 
-    // One global_load_lds of the stage-kt tiles into buffer xs: instruction
-    // q < 8 is token-tile instruction q, q >= 8 weight-tile instruction q - 8.
-    auto dma = [&](int kt, char* xs, int q) {
-        if (q < 8)
-            load_lds16(x_src[q] + (int64_t)kt * X_ROW, xs + (64 * wave + 8 * q) * X_ROW);
-        else
-            load_lds16(w_src[q - 8] + kt * w_step, xs + X_BYTES + (16 * wave + 2 * (q - 8)) * W_ROW);
+    auto issue = [&](int kt, char* st) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            load_lds16(x_src[j] + (int64_t)kt * X_ROW, st + (64 * wave + 16 * j) * X_ROW);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            load_lds16(w_src[j] + kt * w_step, st + X_BYTES + (8 * wave + 2 * j) * W_ROW);
     };
 
     // ---- MFMA operand read offsets (bytes within a stage).
-    // Weight operand (A): lane = 16 G + s reads k = 16 ks + 8 (G>>1) + 4 r + s/4,
-    // feature R = 128 wf + 32 mi + 16 (G&1) + 4 (s&3).
-    const int G = lane >> 4, s = lane & 15;
-    int w_off[4][2];   // [mi][r] for ks = 0; later ks add 16 rows (swizzle repeats every 4 rows)
+    // Weight operand (A), transposed read: lane = 16 G + s of k16 slice ks
+    // reads k = 16 ks + 8 (G / 2) + 4 r + s / 4 (r = 0, 1 for the two halves),
+    // feature 64 w + 32 mi + 16 (G % 2) + 4 (s % 4).
+    const int G = lane >> 4, sl = lane & 15;
+    int w_off[2][2];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            const int k = 8 * (G >> 1) + 4 * r + (s >> 2);
-            const int R = 128 * wf + 32 * mi + 16 * (G & 1) + 4 * (s & 3);
-            w_off[mi][r] = X_BYTES + k * W_ROW + (((R >> 3) ^ swz_w(k)) << 4) + 8 * (s & 1);
+            const int k = 8 * (G >> 1) + 4 * r + (sl >> 2);
+            const int R = 64 * wave + 32 * mi + 16 * (G & 1) + 4 * (sl & 3);
+            w_off[mi][r] = X_BYTES + k * W_ROW + (((R >> 3) ^ swz_tr(k)) << 4) + 8 * ((R >> 2) & 1);
         }
-    // Token operand (B): lane reads row 128 wt + 32 nj + lane%32, logical chunk 2 ks + lane/32.
-    int x_row_off[4], x_swz[4];
-#pragma unroll
-    for (int nj = 0; nj < 4; ++nj) {
-        const int row = 128 * wt + 32 * nj + (lane & 31);
-        x_row_off[nj] = row * X_ROW;
-        x_swz[nj] = swz_x(row);
-    }
+    // Token operand (B): lane reads row 32 nj + lane%32, logical chunk
+    // 2 ks + lane/32; rows 32 nj + l and l share swz_x, so one offset serves
+    // all eight blocks.
+    const int xr = lane & 31;
+    const int x_base = xr * X_ROW;
+    const int x_sw = swz_x(xr);
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[2][8];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x16_t{};
+        for (int nj = 0; nj < 8; ++nj) acc[mi][nj] = f32x16_t{};
 
     struct Frags {
-        bf16x8_t w[4], x[4];
+        bf16x8_t w[2][2], x[2][8];      // [k16 slice][block]
     };
-    auto read_frags = [&](const char* st, int ks, Frags& f) {
+    auto read_frags = [&](const char* st, Frags& f) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            f.w[mi] = cat_bf16(read_tr(st + w_off[mi][0] + ks * 16 * W_ROW),
-                               read_tr(st + w_off[mi][1] + ks * 16 * W_ROW));
-        }
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj) {
-            const int c = (2 * ks + (lane >> 5)) ^ x_swz[nj];
-            f.x[nj] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + x_row_off[nj] + (c << 4)));
+            for (int mi = 0; mi < 2; ++mi)
+                f.w[ks][mi] = cat_bf16(read_tr(st + w_off[mi][0] + ks * 16 * W_ROW),
+                                       read_tr(st + w_off[mi][1] + ks * 16 * W_ROW));
+            const int c = ((2 * ks + (lane >> 5)) ^ x_sw) << 4;
+#pragma unroll
+            for (int nj = 0; nj < 8; ++nj)
+                f.x[ks][nj] = __builtin_bit_cast(
+                    bf16x8_t, *(const u32x4_t*)(st + x_base + nj * 32 * X_ROW + c));
         }
     };
     auto mfmas = [&](const Frags& f) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int nj = 0; nj < 4; ++nj)
-                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[mi], f.x[nj], acc[mi][nj],
-                                                                      0, 0, 0);
+            for (int nj = 0; nj < 8; ++nj)
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[ks][mi], f.x[ks][nj],
+                                                                          acc[mi][nj], 0, 0, 0);
     };
-    // One K step on stage buffer st (its ks = 0 operands already in fa) while
-    // stage kl streams into nx.  Each k16 slice first issues the next slice's
-    // 12 LDS reads and 4 of the next stage's global_load_lds, then its own 16
-    // independent MFMAs; the scheduling fences keep that order, so every LDS
-    // read has 16 MFMAs (~512 cycles) to land before it is used.
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-    auto step = [&](const char* st, char* nx, int kl, Frags& fa, Frags& fb) {
-        read_frags(st, 1, fb);
+
+    // ---- 4-stage ring, software-pipelined one stage deep in registers.
+    // Step s (its operands fc already in registers):
+    //   wait until stage s+1 has landed (one later stage of this wavefront's
+    //   loads may still be outstanding) and fc's LDS reads have returned;
+    //   barrier;
+    //   issue the loads of stage s+3 into the buffer of stage s-1;
+    //   read stage s+1's operands into fn;
+    //   32 MFMAs on fc -- the reads of fn land under them.
+    // The buffer of stage s-1 is free at step s: its operands were read in
+    // step s-2 and consumed by the MFMAs of step s-1, which every wavefront
+    // finished before arriving at this barrier.  Loads past the last stage
+    // re-read the last stage (into buffers never computed on), so the number
+    // of loads per stage stays fixed.
+    const int KT = K / BK;
+    constexpr int PER_STAGE = 8;       // global_load_lds per wavefront per stage
+    auto wait_stage = [] {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(PER_STAGE, 0));
+        __builtin_amdgcn_s_barrier();
+    };
+    auto step = [&](Frags& fc, Frags& fn, const char* nxt, char* dma, int kl) {
+        wait_stage();
+        fence();
+        issue(kl, dma);
+        read_frags(nxt, fn);
+        mfmas(fc);
+        // A wavefront issues in order and stalls on a load or LDS read while
+        // that pipe is backed up, so bursts of either would idle the MFMAs:
+        // per 4 MFMAs, one global_load_lds and three LDS reads
+        // (32 MFMAs, 8 loads, 24 reads per step).
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dma(kl, nx, q);
-        fence();
-        mfmas(fa);
-        fence();
-        read_frags(st, 2, fa);
-#pragma unroll
-        for (int q = 4; q < 8; ++q) dma(kl, nx, q);
-        fence();
-        mfmas(fb);
-        fence();
-        read_frags(st, 3, fb);
-#pragma unroll
-        for (int q = 8; q < 12; ++q) dma(kl, nx, q);
-        fence();
-        mfmas(fa);
-        fence();
-#pragma unroll
-        for (int q = 12; q < 16; ++q) dma(kl, nx, q);
-        fence();
-        mfmas(fb);
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
         fence();
     };
-
-    // K loop, unrolled by two so the stage buffer of every access is static.
-    // The step after the last one reloads the last stage into the idle buffer
-    // (an L2 hit) instead of branching around the loads.
-    const int KT = K / BK;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) dma(0, lds0, q);
-    wait_vmem();
-    __syncthreads();
     Frags fa, fb;
-    read_frags(lds0, 0, fa);
+    issue(0, st0);
+    issue(min(1, KT - 1), st1);
+    issue(min(2, KT - 1), st2);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * PER_STAGE, 15));   // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    fence();
+    read_frags(st0, fa);
+    fence();
     int kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-        step(lds0, lds1, kt + 1, fa, fb);
-        wait_vmem();
-        __syncthreads();
-        read_frags(lds1, 0, fa);
-        step(lds1, lds0, min(kt + 2, KT - 1), fa, fb);
-        wait_vmem();
-        __syncthreads();
-        read_frags(lds0, 0, fa);
+    for (; kt + 4 <= KT; kt += 4) {
+        step(fa, fb, st1, st3, min(kt + 3, KT - 1));
+        step(fb, fa, st2, st0, min(kt + 4, KT - 1));
+        step(fa, fb, st3, st1, min(kt + 5, KT - 1));
+        step(fb, fa, st0, st2, min(kt + 6, KT - 1));
     }
-    if (kt < KT) {                     // odd step count: the last step sits in lds0
-        step(lds0, lds1, KT - 1, fa, fb);
-        wait_vmem();
+    if (kt < KT) {
+        step(fa, fb, st1, st3, KT - 1);
+        if (kt + 1 < KT) {
+            step(fb, fa, st2, st0, KT - 1);
+            if (kt + 2 < KT) step(fa, fb, st3, st1, KT - 1);
+        }
     }
+    wait_vmem();
 
-    // ---- epilogue.  acc[mi][nj] element v of lane l: token 128 wt + 32 nj + l%32,
-    // feature 128 wf + 32 mi + 8 (v/4) + 4 (l/32) + v%4.
+    // ---- epilogue, staged through LDS so that every store instruction
+    // writes whole row segments (16 bytes per lane, 256 or 512 contiguous
+    // bytes per row) instead of 8-byte pieces of 32 rows.  acc[mi][nj]
+    // element v of lane l: token 32 nj + l%32, MFMA feature
+    // 64 w + 32 mi + 8 (v/4) + 4 (l/32) + v%4.  Up: h column 32 w + the
+    // feature's offset in its 32-block (g in mi = 0, u in mi = 1); down:
+    // output column = MFMA feature.  Tile rows 64 q .. 64 q + 63 are staged in
+    // stage buffer q, 16-byte chunks XOR-swizzled by the row's low 4 bits.
+    constexpr int OCOLS = UP ? TF / 2 : TF;     // output columns of the tile
+    constexpr int OROW = OCOLS * 2;             // bytes per staged row
+    constexpr int OCH = OROW / 16;              // 16-byte chunks per row
+    static_assert(64 * OROW <= STAGE_BYTES, "a stage buffer holds 64 staged rows");
+    auto orow = [&](int r) -> char* {
+        char* b = r < 64 ? st0 : r < 128 ? st1 : r < 192 ? st2 : st3;
+        return b + (r & 63) * OROW;
+    };
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // this wavefront's loads and LDS reads done
+    __syncthreads();                                // ... and every other wavefront's
 #pragma unroll
-    for (int nj = 0; nj < 4; ++nj) {
-        const int t = 128 * wt + 32 * nj + (lane & 31);
-        if (t >= valid_rows) continue;
-        const int64_t row = tile_r0 + t;
-        uint16_t* out = (uint16_t*)a.out + row * (int64_t)N;
+    for (int nj = 0; nj < 8; ++nj) {
+        const int t = 32 * nj + (lane & 31);
+        char* rowp = orow(t);
+        const int sw = t & 15;
         if (UP) {
+            const f32x16_t& g = acc[0][nj];
+            const f32x16_t& u = acc[1][nj];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int vg = 0; vg < 4; ++vg) {
-                    const int col = nt * (TF / 2) + 64 * wf + 32 * mi + 8 * vg + 4 * (lane >> 5);
-                    if (col >= N) continue;
-                    const f32x16_t& g = acc[mi][nj];
-                    const f32x16_t& u = acc[mi + 2][nj];
-                    const int v = 4 * vg;
-                    *(uint2*)(out + col) =
-                        make_uint2(pack_bf16(silu_mul(g[v], u[v]), silu_mul(g[v + 1], u[v + 1])),
-                                   pack_bf16(silu_mul(g[v + 2], u[v + 2]), silu_mul(g[v + 3], u[v + 3])));
-                }
+            for (int vg = 0; vg < 4; ++vg) {
+                const int v = 4 * vg;
+                const int c = 4 * wave + vg;
+                *(uint2*)(rowp + ((c ^ sw) << 4) + 8 * (lane >> 5)) =
+                    make_uint2(pack_bf16(silu_mul(g[v], u[v]), silu_mul(g[v + 1], u[v + 1])),
+                               pack_bf16(silu_mul(g[v + 2], u[v + 2]), silu_mul(g[v + 3], u[v + 3])));
+            }
         } else {
             const float wt_row = row_w[nj];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < 2; ++mi) {
+                const f32x16_t& c = acc[mi][nj];
 #pragma unroll
                 for (int vg = 0; vg < 4; ++vg) {
-                    const int col = nt * TF + 128 * wf + 32 * mi + 8 * vg + 4 * (lane >> 5);
-                    if (col >= N) continue;
-                    const f32x16_t& c = acc[mi][nj];
                     const int v = 4 * vg;
-                    *(uint2*)(out + col) = make_uint2(pack_bf16(wt_row * c[v], wt_row * c[v + 1]),
-                                                      pack_bf16(wt_row * c[v + 2], wt_row * c[v + 3]));
+                    const int ch = 8 * wave + 4 * mi + vg;
+                    *(uint2*)(rowp + ((ch ^ sw) << 4) + 8 * (lane >> 5)) =
+                        make_uint2(pack_bf16(wt_row * c[v], wt_row * c[v + 1]),
+                                   pack_bf16(wt_row * c[v + 2], wt_row * c[v + 3]));
                 }
+            }
         }
+    }
+    __syncthreads();
+    constexpr int ROWS_PER_PASS = NT / OCH;
+    const int c = tid % OCH;
+    const int col = nt * OCOLS + 8 * c;
+#pragma unroll 4
+    for (int r = tid / OCH; r < TT; r += ROWS_PER_PASS) {
+        if (r >= valid_rows) break;
+        const u32x4_t v = *(const u32x4_t*)(orow(r) + ((c ^ (r & 15)) << 4));
+        if (col < N) *(u32x4_t*)((uint16_t*)a.out + (tile_r0 + r) * (int64_t)N + col) = v;
     }
 }
 
