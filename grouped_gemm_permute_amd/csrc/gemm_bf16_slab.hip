@@ -25,8 +25,9 @@
 //    its last row, which costs the memory pipe next to nothing (all lanes of
 //    an instruction then hit one line) and keeps every wavefront's load count
 //    per stage fixed, so the waits are compile-time counts;
-//  * tiles run n-major so the workgroups of one XCD share their token rows
-//    through its L2.
+//  * tiles run m-major (all column slabs of one row tile back to back), so
+//    the workgroups of one XCD stream whole weight rows of one group in step
+//    and share that group's token rows through the XCD's L2.
 #include "mfma_common.h"
 
 namespace moe {
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a)
     const int total = a.g.tile_off[a.g.G];
     const int id = xcd_remap_work(blockIdx.x, total * a.n_tiles);
     if (id < 0) return;
-    const int nt = id / total, mt = id - nt * total;     // n-major
+    const int mt = id / a.n_tiles, nt = id - mt * a.n_tiles;     // m-major
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const TileGroup tg = find_tile_group(a.g, mt, TT, lane);
@@ -206,8 +207,17 @@ __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a)
         fence();
         issue(kl, dma);
         read_frags(nxt, fn);
-        fence();
         mfmas(fc);
+        // The in-order wavefront stalls on a load or LDS read while that pipe
+        // is backed up; spread them between the MFMAs (4 RB MFMAs, RB + 4
+        // loads, 4 RB + 8 reads per step): each MFMA is followed by one load
+        // and two reads until those run out.
+#pragma unroll
+        for (int i = 0; i < 4 * RB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read
+        }
         fence();
     };
     Frags fa, fb;

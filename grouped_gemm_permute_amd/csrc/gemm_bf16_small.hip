@@ -11,10 +11,13 @@
 //  * tile 64 rows x 64 MFMA features (up: 32 g + 32 u), K step 64;
 //  * 256 threads = 4 wavefronts (2 feature x 2 row), one 32 x 32
 //    v_mfma_f32_32x32x16_bf16 block each; two workgroups per CU;
-//  * a 4-deep ring of LDS stages (16 KiB each) filled with global_load_lds,
-//    so three stages (48 KiB per workgroup) are in flight while one computes;
-//  * tiles run n-major (all row tiles of one weight slice back to back) so
-//    the row tiles of an expert share its weight slice through L2;
+//  * a 4-deep ring of LDS stages (16 KiB each) filled with global_load_lds
+//    (two stages in flight while one computes), and the next stage's
+//    operands read from LDS while the current stage's MFMAs run;
+//  * tiles run m-major (all column tiles of one row tile back to back), so
+//    an XCD works through one group's whole weight matrix with neighbouring
+//    workgroups reading neighbouring parts of each weight row, and the
+//    group's next row tile finds the weights in that XCD's L2;
 //  * up: a wavefront's 32 MFMA rows are 16 g columns followed by the same 16
 //    u columns, so accumulator element v (g) and v + 8 (u) of a lane belong
 //    to the same (row, column).
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallAr
     const int total = a.g.tile_off[a.g.G];
     const int id = xcd_remap_work(blockIdx.x, total * a.n_tiles);
     if (id < 0) return;
-    const int nt = id / total, mt = id - nt * total;     // n-major
+    const int mt = id / a.n_tiles, nt = id - mt * a.n_tiles;     // m-major
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wf = wave >> 1, wt = wave & 1;
@@ -151,48 +154,72 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallAr
     const int x_off = xrow * X_ROW, x_swz = swz8(xrow);
 
     f32x16_t acc = {};
-    auto compute = [&](const char* st) {
+    struct Frags {
+        bf16x8_t w[BK / 16], x[BK / 16];
+    };
+    auto read_frags = [&](const char* st, Frags& f) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            const bf16x8_t wfr = cat_bf16(read_tr(st + w_off[0] + ks * 16 * W_ROW),
-                                          read_tr(st + w_off[1] + ks * 16 * W_ROW));
+            f.w[ks] = cat_bf16(read_tr(st + w_off[0] + ks * 16 * W_ROW),
+                               read_tr(st + w_off[1] + ks * 16 * W_ROW));
             const int c = (2 * ks + (lane >> 5)) ^ x_swz;
-            const bf16x8_t xfr = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + x_off + (c << 4)));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wfr, xfr, acc, 0, 0, 0);
+            f.x[ks] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + x_off + (c << 4)));
         }
     };
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
-    // ---- 4-stage ring, unrolled by 4 so every buffer access is static.  At
-    // step kt the stages kt+1, kt+2 are in flight and kt+3 is issued into
-    // the buffer step kt-1 just released (after the barrier).  Loads past
-    // the last stage re-read the last stage (never computed on).
+    // ---- 4-stage ring, software-pipelined one stage deep in registers.
+    // Step s (its operands fc already in registers): wait until stage s+1
+    // has landed (one later stage of this wavefront's loads may still be
+    // outstanding) and fc's LDS reads have returned, then a bare s_barrier
+    // (__syncthreads() would also wait for the stage in flight and drain the
+    // ring); issue the loads of stage s+3 into the buffer of stage s-1; read
+    // stage s+1's operands into fn; MFMAs on fc, the reads landing under
+    // them.  The buffer of stage s-1 is free: its operands were read in step
+    // s-2 and consumed by the MFMAs of step s-1, which every wavefront
+    // finished before this barrier.  Loads past the last stage re-read the
+    // last stage (never computed on), so each stage has the same load count.
     const int KT = K / BK;
-    // Wait until at most 8 of this wavefront's loads (two stages) are
-    // outstanding, i.e. stage kt has landed, then a bare s_barrier:
-    // __syncthreads() would also wait for every outstanding load and drain the
-    // ring.  The barrier also orders the buffer reuse: every wavefront's
-    // reads of the buffer refilled next were consumed by its MFMAs before it
-    // arrived.
-    auto wait_stage = [] {
-        __builtin_amdgcn_s_waitcnt(0x0F78);
+    constexpr int PER_STAGE = 4;       // global_load_lds per wavefront per stage
+    auto step = [&](Frags& fc, Frags& fn, const char* nxt, char* dma, int kl) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(PER_STAGE, 0));
         __builtin_amdgcn_s_barrier();
+        fence();
+        issue(kl, dma);
+        read_frags(nxt, fn);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.w[ks], fc.x[ks], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < BK / 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS read
+        }
+        fence();
     };
+    Frags fa, fb;
     issue(0, st0);
     issue(min(1, KT - 1), st1);
     issue(min(2, KT - 1), st2);
-    for (int kt = 0; kt < KT; kt += 4) {
-        wait_stage();
-        issue(min(kt + 3, KT - 1), st3);
-        compute(st0);
-        wait_stage();
-        issue(min(kt + 4, KT - 1), st0);
-        if (kt + 1 < KT) compute(st1);
-        wait_stage();
-        issue(min(kt + 5, KT - 1), st1);
-        if (kt + 2 < KT) compute(st2);
-        wait_stage();
-        issue(min(kt + 6, KT - 1), st2);
-        if (kt + 3 < KT) compute(st3);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * PER_STAGE, 15));   // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    fence();
+    read_frags(st0, fa);
+    fence();
+    int kt = 0;
+    for (; kt + 4 <= KT; kt += 4) {
+        step(fa, fb, st1, st3, min(kt + 3, KT - 1));
+        step(fb, fa, st2, st0, min(kt + 4, KT - 1));
+        step(fa, fb, st3, st1, min(kt + 5, KT - 1));
+        step(fb, fa, st0, st2, min(kt + 6, KT - 1));
+    }
+    if (kt < KT) {
+        step(fa, fb, st1, st3, KT - 1);
+        if (kt + 1 < KT) {
+            step(fb, fa, st2, st0, KT - 1);
+            if (kt + 2 < KT) step(fa, fb, st3, st1, KT - 1);
+        }
     }
     wait_vmem();
 
