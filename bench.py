@@ -109,12 +109,12 @@ def stage_work(w, counts):
         # x once, [W1|W3] of every active group, h out
         "up_swiglu": {"flop": 4 * w.D * w.F * rows,
                       "bytes": w.T * w.D * b + 2 * wbytes * groups + rows * w.F * b},
-        # h, W2 of every active group, routing weights, weighted Yw out (storage dtype)
+        # h, W2 of every active group, Y out (storage dtype)
         "down": {"flop": 2 * w.D * w.F * rows,
-                 "bytes": rows * w.F * b + wbytes * groups + S * 4 + rows * w.D * b},
-        # Yw and inv in, y out
-        "combine": {"flop": w.k * w.D * w.T,
-                    "bytes": rows * w.D * b + S * 4 + w.T * w.D * b},
+                 "bytes": rows * w.F * b + wbytes * groups + rows * w.D * b},
+        # Y, inv and routing weights in, y out
+        "combine": {"flop": 2 * w.k * w.D * w.T,
+                    "bytes": rows * w.D * b + S * 8 + w.T * w.D * b},
     }
 
 

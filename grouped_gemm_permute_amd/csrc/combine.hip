@@ -1,19 +1,19 @@
 // combine.hip -- unpermute and weighted combine.
 //
-//   y[t] = Yw[S + t] + sum_{j=0}^{k-1} Yw[inv[t*k + j]]
+//   y[t] = Y[S + t] + sum_{j=0}^{k-1} topk_w[t, j] * Y[inv[t*k + j]]
 //
-// where Yw holds every row's expert output already multiplied by its
-// routing weight (the down GEMM's epilogue applies it) and row S + t is the
-// shared expert's output for token t (absent without a shared expert).
+// where Y holds every row's expert output (the down GEMM's result) and row
+// S + t is the shared expert's output for token t (absent without a shared
+// expert, weight 1).
 // "Chinchilla scaling, MoE, and fused Triton kernels" (section "PyTorch MoE
 // implementation") gathers each token's k expert rows through the inverse
 // permutation and sums them weighted; "Triton MoE Kernels & Memory
 // Checkpointing" (Part A, section 10.3 step 4) scales by the routing weight
-// after W2 and adds the result back into the token's row.  Here the terms
-// are added in fp32 in j order, starting from the shared row (or 0), and
-// rounded once to the output type, so the result does not depend on
-// scheduling (no scatter atomics).  Slots with inv = -1 (invalid ids) add
-// nothing.
+// after W2 and adds the result back into the token's row.  Here each term
+// is scaled and added in fp32 (one fused multiply-add per term) in j order,
+// starting from the shared row (or 0), and rounded once to the output
+// type, so the result does not depend on scheduling (no scatter atomics).
+// Slots with inv = -1 (invalid ids) add nothing.
 #include "moe_internal.h"
 
 namespace moe {
@@ -32,8 +32,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v 
 
 // bf16: one thread per (token, 8 consecutive columns); D % 8 == 0 (the bf16
 // path requires D % 64 == 0), all accesses 16 bytes.
-__global__ __launch_bounds__(NT) void combine_bf16_kernel(const uint16_t* __restrict__ Yw,
+__global__ __launch_bounds__(NT) void combine_bf16_kernel(const uint16_t* __restrict__ Y,
                                                          const int32_t* __restrict__ inv,
+                                                         const float* __restrict__ topk_w,
                                                          uint16_t* __restrict__ y, int64_t T, int D,
                                                          int k, int has_shared) {
     const int cg = D / 8;
@@ -43,28 +44,29 @@ __global__ __launch_bounds__(NT) void combine_bf16_kernel(const uint16_t* __rest
     const int c = (int)(gid - t * cg) * 8;
     const int64_t S = T * k;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto add = [&](const uint16_t* src) {
+    auto add = [&](const uint16_t* src, float wt) {
         const uint4 v = *(const uint4*)src;
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += bf16_lo(w[i]);
-            acc[2 * i + 1] += bf16_hi(w[i]);
+            acc[2 * i] = fmaf(wt, bf16_lo(w[i]), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(wt, bf16_hi(w[i]), acc[2 * i + 1]);
         }
     };
-    if (has_shared) add(Yw + (S + t) * D + c);
+    if (has_shared) add(Y + (S + t) * D + c, 1.f);
     for (int j = 0; j < k; ++j) {
         const int32_t p = inv[t * k + j];
         if (p < 0 || p >= S) continue;      // invalid slot (p == -1)
-        add(Yw + (int64_t)p * D + c);
+        add(Y + (int64_t)p * D + c, topk_w[t * k + j]);
     }
     *(uint4*)(y + t * D + c) = make_uint4(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
                                           pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7]));
 }
 
 // fp32: one thread per (token, column).
-__global__ __launch_bounds__(NT) void combine_f32_kernel(const float* __restrict__ Yw,
+__global__ __launch_bounds__(NT) void combine_f32_kernel(const float* __restrict__ Y,
                                                         const int32_t* __restrict__ inv,
+                                                        const float* __restrict__ topk_w,
                                                         float* __restrict__ y, int64_t T, int D,
                                                         int k, int has_shared) {
     const int64_t gid = (int64_t)blockIdx.x * NT + threadIdx.x;
@@ -72,27 +74,27 @@ __global__ __launch_bounds__(NT) void combine_f32_kernel(const float* __restrict
     const int64_t t = gid / D;
     const int c = (int)(gid - t * D);
     const int64_t S = T * k;
-    float acc = has_shared ? Yw[(S + t) * D + c] : 0.f;
+    float acc = has_shared ? Y[(S + t) * D + c] : 0.f;
     for (int j = 0; j < k; ++j) {
         const int32_t p = inv[t * k + j];
         if (p < 0 || p >= S) continue;
-        acc += Yw[(int64_t)p * D + c];
+        acc = fmaf(topk_w[t * k + j], Y[(int64_t)p * D + c], acc);
     }
     y[t * D + c] = acc;
 }
 
 }  // namespace
 
-hipError_t launch_combine(const void* Yw, const int32_t* inv, void* y, int64_t T, int D, int k,
-                          bool has_shared, bool bf16, hipStream_t s) {
+hipError_t launch_combine(const void* Y, const int32_t* inv, const float* topk_w, void* y,
+                          int64_t T, int D, int k, bool has_shared, bool bf16, hipStream_t s) {
     if (bf16) {
         const int64_t threads = T * (D / 8);
         combine_bf16_kernel<<<(unsigned)((threads + NT - 1) / NT), NT, 0, s>>>(
-            (const uint16_t*)Yw, inv, (uint16_t*)y, T, D, k, has_shared);
+            (const uint16_t*)Y, inv, topk_w, (uint16_t*)y, T, D, k, has_shared);
     } else {
         const int64_t threads = T * D;
         combine_f32_kernel<<<(unsigned)((threads + NT - 1) / NT), NT, 0, s>>>(
-            (const float*)Yw, inv, (float*)y, T, D, k, has_shared);
+            (const float*)Y, inv, topk_w, (float*)y, T, D, k, has_shared);
     }
     return hipGetLastError();
 }

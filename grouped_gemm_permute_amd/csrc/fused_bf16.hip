@@ -13,7 +13,7 @@
 //     g, u = x_tile . W1[:, f], x_tile . W3[:, f]        (fp32 accumulate, K = D)
 //     h    = bf16(silu(g) * u)                           (into LDS)
 //     acc += h . W2[f, :]                                (fp32 accumulate, K = CH)
-//   Yw[row] = bf16(w(row) * acc[row])                    (routing weight; 1 on shared rows)
+//   Y[row] = bf16(acc[row])                              (the combine applies the routing weight)
 //
 // Shapes and placement on gfx950 (256 threads = 4 wavefronts, one per SIMD):
 //  * token tile TT = 64 rows of one group; the fp32 accumulator acc is
@@ -56,7 +56,7 @@ struct FusedArgs {
     const uint16_t* x;                     // [T, D]
     const uint16_t *W1, *W3, *W2;          // [E, D, F], [E, D, F], [E, F, D]
     const uint16_t *Ws1, *Ws3, *Ws2;       // shared expert or null
-    uint16_t* Yw;                          // [R, D] bf16 weighted expert outputs
+    uint16_t* Y;                           // [R, D] bf16 expert outputs
     int D, F;
 };
 
@@ -115,15 +115,6 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
             const int row = 16 * wave + 8 * j + (lane >> 3);
             const int c = (lane & 7) ^ swz8(row);
             x_src[j] = (const char*)(a.x + src_row[j] * (int64_t)D + 8 * c);
-        }
-    }
-    // Routing weight of this lane's two output rows (token blocks 0 and 1).
-    float row_w[2] = {1.f, 1.f};
-    if (!shared) {
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const int t = min(32 * tb + (lane & 31), valid_rows - 1);
-            row_w[tb] = a.g.topk_w[a.g.perm[tile_r0 + t]];
         }
     }
 
@@ -320,8 +311,7 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
     for (int tb = 0; tb < 2; ++tb) {
         const int t = 32 * tb + (lane & 31);
         if (t >= valid_rows) continue;
-        uint16_t* out = a.Yw + (tile_r0 + t) * (int64_t)D;
-        const float wt = row_w[tb];
+        uint16_t* out = a.Y + (tile_r0 + t) * (int64_t)D;
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
@@ -329,8 +319,8 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
                 const int col = WCOLS * wave + 32 * fb + 8 * vg + 4 * (lane >> 5);
                 const f32x16_t& y = acc_y[fb][tb];
                 const int v = 4 * vg;
-                *(uint2*)(out + col) = make_uint2(pack_bf16(wt * y[v], wt * y[v + 1]),
-                                                  pack_bf16(wt * y[v + 2], wt * y[v + 3]));
+                *(uint2*)(out + col) = make_uint2(pack_bf16(y[v], y[v + 1]),
+                                                  pack_bf16(y[v + 2], y[v + 3]));
             }
     }
 }
@@ -339,10 +329,10 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
 
 hipError_t launch_fused_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
                              const void* W2, const void* Ws1, const void* Ws3, const void* Ws2,
-                             void* Yw, int D, int F, hipStream_t s) {
+                             void* Y, int D, int F, hipStream_t s) {
     FusedArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
                 (const uint16_t*)W2, (const uint16_t*)Ws1, (const uint16_t*)Ws3,
-                (const uint16_t*)Ws2, (uint16_t*)Yw, D, F};
+                (const uint16_t*)Ws2, (uint16_t*)Y, D, F};
     const int64_t rows = g.S + (g.G > g.E ? g.T : 0);
     const unsigned blocks = (unsigned)((rows + TT - 1) / TT + g.G);
     switch (D / 128) {

@@ -13,10 +13,9 @@
 //              GEMM of "Triton MoE Kernels & Memory Checkpointing" (Part A,
 //              sections 6 and 10.1) with fp32 SiLU and a single cast of the
 //              product to the storage type.
-//  down:       Yw[p] = bf16(w(p) * (h[p] . W2[grp]))   (fp32 accumulate), the
-//              per-expert W2 product followed by the scaling with the routing
-//              weight of the same page's section 10.3 step 4; w(p) is the
-//              weight of the slot in row p (1 on shared rows).
+//  down:       Y[p] = bf16(h[p] . W2[grp])   (fp32 accumulate), the per-expert
+//              W2 product of the same page's section 10.3; the combine applies
+//              the routing weight (its step 4).
 //
 // Tile engine (256 threads = 4 wavefronts, one per SIMD):
 //  * the MFMA computes the transposed tile C^T = W^T . X^T: its A operand is
@@ -75,7 +74,7 @@ struct GemmArgs {
     const uint16_t* b1;       // up: W3; down: unused
     const uint16_t* bs0;      // shared expert: up Ws1, down Ws2
     const uint16_t* bs1;      // up Ws3
-    void* out;                // up: h bf16 [R, F]; down: Yw bf16 [R, D]
+    void* out;                // up: h bf16 [R, F]; down: Y bf16 [R, D]
     int D, F;
     int n_tiles;              // column tiles
 };
@@ -136,19 +135,6 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
             x_src[j] = (const char*)(a.a + src_row[j] * (int64_t)K + 8 * ((lane & 3) ^ swz_x(row)));
         }
     }
-    // Down GEMM: routing weight of each of this lane's 8 output rows (1 on shared rows).
-    float row_w[8];
-#pragma unroll
-    for (int nj = 0; nj < 8; ++nj) row_w[nj] = 1.f;
-    if (!UP && !shared) {
-        int32_t slot[8];
-#pragma unroll
-        for (int nj = 0; nj < 8; ++nj)
-            slot[nj] = a.g.perm[tile_r0 + min(32 * nj + (lane & 31), valid_rows - 1)];
-#pragma unroll
-        for (int nj = 0; nj < 8; ++nj) row_w[nj] = a.g.topk_w[slot[nj]];
-    }
-
     // ---- weight tile sources: DMA instruction j (0..3) of wavefront w fills
     // k rows 8 w + 2 j, +1; lane -> k row 8 w + 2 j + lane/32, physical chunk
     // lane%32 holding logical chunk cl = phys ^ swz_tr(k) = MFMA features
@@ -342,7 +328,6 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
                                pack_bf16(silu_mul(g[v + 2], u[v + 2]), silu_mul(g[v + 3], u[v + 3])));
             }
         } else {
-            const float wt_row = row_w[nj];
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi) {
                 const f32x16_t& c = acc[mi][nj];
@@ -351,8 +336,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
                     const int v = 4 * vg;
                     const int ch = 8 * wave + 4 * mi + vg;
                     *(uint2*)(rowp + ((ch ^ sw) << 4) + 8 * (lane >> 5)) =
-                        make_uint2(pack_bf16(wt_row * c[v], wt_row * c[v + 1]),
-                                   pack_bf16(wt_row * c[v + 2], wt_row * c[v + 3]));
+                        make_uint2(pack_bf16(c[v], c[v + 1]), pack_bf16(c[v + 2], c[v + 3]));
                 }
             }
         }

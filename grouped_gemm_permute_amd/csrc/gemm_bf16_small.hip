@@ -1,7 +1,7 @@
 // gemm_bf16_small.hip -- grouped GEMMs for small per-expert chunks.
 //
 // Same products as gemm_bf16.hip (up: h = bf16(silu(x . W1) * (x . W3));
-// down: Yw = bf16(w * (h . W2))), shaped for the regime where each expert
+// down: Y = bf16(h . W2)), shaped for the regime where each expert
 // sees only tens to a few hundred rows and the weights dominate the traffic
 // (the "small chunks" that "Triton MoE Kernels & Memory Checkpointing",
 // Part A sections 2 and 6.1, calls the pathological regime).  There the
@@ -52,7 +52,7 @@ struct SmallArgs {
     const uint16_t* b1;       // up: W3
     const uint16_t* bs0;      // shared: up Ws1, down Ws2
     const uint16_t* bs1;      // shared: up Ws3
-    uint16_t* out;            // up: h [R, F]; down: Yw [R, D]
+    uint16_t* out;            // up: h [R, F]; down: Y [R, D]
     int D, F;
     int n_tiles;
 };
@@ -126,9 +126,6 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallAr
         w_src[j] = (const char*)(base + (int64_t)kr * N + col);
     }
     const int64_t w_step = (int64_t)BK * N * 2;
-    float row_w = 1.f;
-    if (!UP && !shared)
-        row_w = a.g.topk_w[a.g.perm[tile_r0 + min(32 * wt + (lane & 31), valid_rows - 1)]];
 
     auto issue = [&](int kt, char* st) {
 #pragma unroll
@@ -245,8 +242,8 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallAr
             const int col = nt * TF + 32 * wf + 8 * vg + 4 * (lane >> 5);
             if (col >= N) continue;
             const int v = 4 * vg;
-            *(uint2*)(out + col) = make_uint2(pack_bf16(row_w * acc[v], row_w * acc[v + 1]),
-                                              pack_bf16(row_w * acc[v + 2], row_w * acc[v + 3]));
+            *(uint2*)(out + col) = make_uint2(pack_bf16(acc[v], acc[v + 1]),
+                                              pack_bf16(acc[v + 2], acc[v + 3]));
         }
     }
 }
@@ -270,9 +267,9 @@ hipError_t launch_up_swiglu_bf16_small(const GroupArgs& g, const void* x, const 
 }
 
 hipError_t launch_down_bf16_small(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
-                                  void* Yw, int D, int F, hipStream_t s) {
+                                  void* Y, int D, int F, hipStream_t s) {
     SmallArgs a{g, (const uint16_t*)h, (const uint16_t*)W2, nullptr, (const uint16_t*)Ws2, nullptr,
-                (uint16_t*)Yw, D, F, (D + TF - 1) / TF};
+                (uint16_t*)Y, D, F, (D + TF - 1) / TF};
     const int64_t blocks = (int64_t)m_tiles_upper_small(g) * a.n_tiles;
     grouped_gemm_small_kernel<false><<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();

@@ -5,8 +5,8 @@
 // Checkpointing", Part A section 5.1).
 //
 //   up:   h[p][n] = silu(sum_d x[tok(p)][d] W1[g][d][n]) * sum_d x[tok(p)][d] W3[g][d][n]
-//   down: Yw[p][n] = w(p) * sum_f h[p][f] W2[g][f][n]   (w(p): routing weight of
-//         the slot in row p, 1 on shared rows)
+//   down: Y[p][n] = sum_f h[p][f] W2[g][f][n]   (the combine applies the
+//         routing weight)
 //
 // Row p < offsets[E] belongs to routed expert g (offsets[g] <= p <
 // offsets[g+1]) and reads token perm[p] / k; row S + t is the shared expert
@@ -67,11 +67,10 @@ __global__ __launch_bounds__(NT) void down_f32_kernel(GroupArgs g, const float* 
     const int grp = row_group(g, p);
     if (grp < 0) return;
     const float* w2 = grp == g.E ? Ws2 : W2 + (int64_t)grp * F * D;
-    const float wt = grp == g.E ? 1.0f : g.topk_w[g.perm[p]];
     const float* hr = h + p * F;
     float acc = 0.f;
     for (int f = 0; f < F; ++f) acc = fmaf(hr[f], w2[(int64_t)f * D + n], acc);
-    Y[p * D + n] = wt * acc;
+    Y[p * D + n] = acc;
 }
 
 int64_t rows_of(const GroupArgs& g) { return g.S + (g.G > g.E ? g.T : 0); }

@@ -171,7 +171,7 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
         return MOE_ERR_HIP;
     if (mark(1) != hipSuccess) return MOE_ERR_HIP;
 
-    GroupArgs g{offsets, tile_off, perm, topk_w, S, T, E, k, E + (has_shared ? 1 : 0)};
+    GroupArgs g{offsets, tile_off, perm, S, T, E, k, E + (has_shared ? 1 : 0)};
     hipError_t e;
     if (variant == MOE_VARIANT_FUSED) {
         // one launch does up, SwiGLU and down; both timing marks follow it
@@ -202,7 +202,7 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
     }
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess)
-        e = launch_combine(Y, inv, y, T, D, k, has_shared, dtype == MOE_BF16, stream);
+        e = launch_combine(Y, inv, topk_w, y, T, D, k, has_shared, dtype == MOE_BF16, stream);
     if (e == hipSuccess) e = mark(4);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

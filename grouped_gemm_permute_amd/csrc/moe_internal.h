@@ -34,7 +34,6 @@ struct GroupArgs {
     const int32_t* offsets;   // [E+1] routed row starts
     const int32_t* tile_off;  // [G+1] row-tile prefix, G = E + has_shared
     const int32_t* perm;      // [S] sorted row -> slot
-    const float* topk_w;      // [S] routing weight of each slot (applied by the down GEMM)
     int64_t S;                // T*k: first shared row
     int64_t T;
     int E;
@@ -47,10 +46,10 @@ constexpr int kBf16TileRows = 256;
 hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
                                  const void* Ws1, const void* Ws3, void* h, int D, int F,
                                  hipStream_t s);
-// Down GEMM output: Yw[p] = w(p) * (h[p] . W2[grp]) rounded to bf16, with
-// w(p) the routing weight of the slot in row p (1 for shared rows).
+// Down GEMM output: Y[p] = h[p] . W2[grp] rounded to bf16 (the routing
+// weight is applied by the combine).
 hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
-                            void* Yw, int D, int F, hipStream_t s);
+                            void* Y, int D, int F, hipStream_t s);
 
 // Small-chunk grouped GEMMs (bf16), for groups too small to fill the GPU
 // with 256-row tiles.  The up GEMM runs on row tiles of 32 * rb rows that hold
@@ -66,15 +65,15 @@ hipError_t launch_up_swiglu_bf16_small(const GroupArgs& g, const void* x, const 
                                        const void* W3, const void* Ws1, const void* Ws3, void* h,
                                        int D, int F, hipStream_t s);
 hipError_t launch_down_bf16_small(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
-                                  void* Yw, int D, int F, hipStream_t s);
+                                  void* Y, int D, int F, hipStream_t s);
 
 // Fused up-act-down (bf16): token tiles of kFusedTileRows rows, h kept on
-// chip; writes the same weighted Yw as the down GEMM.  Needs D % 128 == 0,
+// chip; writes the same Y as the down GEMM.  Needs D % 128 == 0,
 // D <= 1024, F % 128 == 0.
 constexpr int kFusedTileRows = 64;
 hipError_t launch_fused_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
                              const void* W2, const void* Ws1, const void* Ws3, const void* Ws2,
-                             void* Yw, int D, int F, hipStream_t s);
+                             void* Y, int D, int F, hipStream_t s);
 
 // fp32 grouped GEMMs (plain fp32 FMA; correctness-first path).
 constexpr int kF32TileRows = 64;
@@ -82,11 +81,12 @@ hipError_t launch_up_swiglu_f32(const GroupArgs& g, const float* x, const float*
                                 const float* W3, const float* Ws1, const float* Ws3, float* h,
                                 int D, int F, hipStream_t s);
 hipError_t launch_down_f32(const GroupArgs& g, const float* h, const float* W2, const float* Ws2,
-                           float* Yw, int D, int F, hipStream_t s);
+                           float* Y, int D, int F, hipStream_t s);
 
-// y[t] = Yw[S+t] (shared, if any) + sum_j Yw[inv[t*k+j]], in fp32 in j order,
-// rounded once.  Yw is bf16 when bf16 is set, else fp32; y has the same type.
-hipError_t launch_combine(const void* Yw, const int32_t* inv, void* y, int64_t T, int D, int k,
-                          bool has_shared, bool bf16, hipStream_t s);
+// y[t] = Y[S+t] (shared, if any) + sum_j topk_w[t,j] * Y[inv[t*k+j]], in fp32
+// in j order, rounded once.  Y is bf16 when bf16 is set, else fp32; y has
+// the same type.
+hipError_t launch_combine(const void* Y, const int32_t* inv, const float* topk_w, void* y,
+                          int64_t T, int D, int k, bool has_shared, bool bf16, hipStream_t s);
 
 }  // namespace moe

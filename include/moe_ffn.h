@@ -78,7 +78,7 @@ typedef struct moe_ws_layout {
     size_t inv;         /* int32 [T*k] slot -> sorted position (-1 for an invalid slot) */
     size_t hist;        /* int32 scratch of the multi-block permute */
     size_t h;           /* [R, F] silu(g)*u, dtype of the call (unfused variant; empty when fused) */
-    size_t Y;           /* [R, D] per-row expert outputs times their routing weight, dtype of the call */
+    size_t Y;           /* [R, D] per-row expert outputs (unweighted), dtype of the call */
     int32_t tile_rows;  /* row-tile height of the grouped GEMMs (tile_off's divisor) */
     int32_t hist_blocks;/* number of slot blocks of the multi-block permute (0: single block) */
     int32_t small_tiles;/* 1: the call uses the small-chunk kernels, chosen when the groups
@@ -123,10 +123,10 @@ size_t moe_ffn_workspace_size(int64_t T, int D, int F, int E, int k, int has_sha
  *
  * Stored results (bf16): per row, the gate and up products accumulate in
  * fp32, silu(g)*u is formed in fp32 and rounded once to bf16 (h); the down
- * product accumulates in fp32, is multiplied by the row's routing weight and
- * rounded once to bf16 (Y); the combine starts from the shared row (or 0),
- * adds the k weighted rows for j = 0..k-1 in that order in fp32 and rounds
- * once to the output dtype.  In fp32 every step stays fp32.  The summation
+ * product accumulates in fp32 and is rounded once to bf16 (Y); the combine
+ * starts from the shared row (or 0), adds topk_w[t,j] * Y[row of slot t*k+j]
+ * for j = 0..k-1 in that order as fp32 fused multiply-adds and rounds once
+ * to the output dtype.  In fp32 every step stays fp32.  The summation
  * order does not depend on timing, so repeated calls give bitwise-identical
  * y.
  *

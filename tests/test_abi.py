@@ -44,7 +44,7 @@ def test_workspace_layout_is_aligned_and_sized():
     for key in ("err", "counts", "offsets", "tile_off", "perm", "inv", "hist", "h", "Y"):
         assert lay[key] % 256 == 0
     assert lay["err"] == 0
-    assert lay["Y"] + R * 768 * 2 <= lay["total"]   # bf16 weighted expert outputs
+    assert lay["Y"] + R * 768 * 2 <= lay["total"]   # bf16 expert outputs
     assert lay["h"] + R * 1536 * 2 <= lay["Y"]
     assert lay["hist_blocks"] == (65536 + 2047) // 2048
     assert L.workspace_size(32768, 768, 1536, 8, 2, True, torch.bfloat16) == lay["total"]

@@ -132,16 +132,14 @@ def test_forward_intermediates_sampled_rows():
             s = ref["perm"][p]
             t, e = s // k, flat[s]
             w1, w3, w2 = inp["W1"][e], inp["W3"][e], inp["W2"][e]
-            wt = float(inp["topk_w"].reshape(-1)[s])
         else:
             t = p - T * k
             w1, w3, w2 = inp["Ws1"], inp["Ws3"], inp["Ws2"]
-            wt = 1.0
         xv = inp["x"][t].astype(np.float64)
         g, u = xv @ w1, xv @ w3
         hh = brute.silu(g) * u
         check_close(hs[i], hh, "bf16", f"h row {p}")
-        check_close(Ys[i], wt * (hh @ w2.astype(np.float64)), "bf16", f"Y row {p}")
+        check_close(Ys[i], hh @ w2.astype(np.float64), "bf16", f"Y row {p}")
 
 
 def test_forward_is_bitwise_deterministic():
