@@ -19,8 +19,11 @@
 // (found with one ballot per key bit), across wavefronts and slot blocks it
 // is a prefix sum in (expert, block) order.
 //
-// Small problems run as one workgroup; larger ones as three launches
-// (per-block histograms, one scan workgroup, per-block scatter).
+// Small problems run as one workgroup.  Larger ones take per-block
+// histograms first; then, while the histogram table is small, every scatter
+// block scans the small histogram table itself (two launches), and beyond
+// that one scan workgroup turns the table into start positions between the
+// two (three launches).
 #include "moe_internal.h"
 
 namespace moe {
@@ -29,6 +32,9 @@ namespace {
 constexpr int kSingleThreads = 512;
 constexpr int kScatterThreads = 256;
 constexpr int kScanThreads = 1024;
+// Largest histogram table, (E+1) x nblocks entries, that every scatter block
+// re-reads itself instead of a separate scan launch.
+constexpr int64_t kFusedScanEntries = 8192;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -218,6 +224,54 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
         scatter_chunk<kScatterThreads>(idx, c0, hi, S, E, nbits, run, wcnt, perm, inv);
 }
 
+// Scan and scatter in one launch.  Block b reads the histogram table
+// (E+1) x nb, forms per-expert totals and the counts of blocks before b,
+// takes its start position per expert (offset of the expert plus the slots
+// of that expert in earlier blocks) and scatters its slots.  Block 0 also
+// writes counts, offsets, the tile prefixes, the error count and the -1
+// tail of perm.
+__global__ __launch_bounds__(kScatterThreads) void permute_scan_scatter_kernel(
+    const int32_t* __restrict__ idx, int64_t S, int E, const int32_t* __restrict__ hist,
+    TileSpec ta, TileSpec tb, int64_t shared_rows, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    int32_t* __restrict__ err) {
+    __shared__ int32_t tot[kMaxExperts + 1];
+    __shared__ int32_t run[kMaxExperts + 1];
+    __shared__ int32_t wcnt[(kScatterThreads / 64) * kMaxExperts];
+    const int tid = threadIdx.x, b = blockIdx.x, nb = gridDim.x;
+    for (int e = tid; e <= E; e += kScatterThreads) tot[e] = run[e] = 0;
+    for (int i = tid; i < (kScatterThreads / 64) * E; i += kScatterThreads) wcnt[i] = 0;
+    __syncthreads();
+    const int n = (E + 1) * nb;
+    for (int i = tid; i < n; i += kScatterThreads) {
+        const int e = i / nb, bb = i - e * nb;
+        const int32_t v = hist[i];
+        if (v) {
+            atomicAdd(&tot[e], v);
+            if (bb < b) atomicAdd(&run[e], v);
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int32_t acc = 0;
+        for (int e = 0; e < E; ++e) {
+            run[e] += acc;
+            acc += tot[e];
+        }
+        if (b == 0) finish_scan(tot, E, ta, tb, shared_rows, counts, offsets, err, nullptr);
+    }
+    __syncthreads();
+    if (b == 0) {
+        const int32_t valid = (int32_t)(S - tot[E]);
+        for (int64_t p = valid + tid; p < S; p += kScatterThreads) perm[p] = -1;
+    }
+    const int nbits = key_bits(E);
+    const int64_t lo = (int64_t)b * kPermuteBlockSlots;
+    const int64_t hi = min(S, lo + kPermuteBlockSlots);
+    for (int64_t c0 = lo; c0 < hi; c0 += kScatterThreads)
+        scatter_chunk<kScatterThreads>(idx, c0, hi, S, E, nbits, run, wcnt, perm, inv);
+}
+
 }  // namespace
 
 hipError_t launch_permute(const int32_t* idx, int64_t S, int E, int tile_rows, int64_t shared_rows,
@@ -231,6 +285,11 @@ hipError_t launch_permute(const int32_t* idx, int64_t S, int E, int tile_rows, i
         return hipGetLastError();
     }
     permute_hist_kernel<<<nblocks, kScatterThreads, 0, s>>>(idx, S, E, hist);
+    if ((int64_t)(E + 1) * nblocks <= kFusedScanEntries) {
+        permute_scan_scatter_kernel<<<nblocks, kScatterThreads, 0, s>>>(
+            idx, S, E, hist, ta, tb, shared_rows, counts, offsets, perm, inv, err);
+        return hipGetLastError();
+    }
     permute_scan_kernel<<<1, kScanThreads, 0, s>>>(hist, nblocks, S, E, ta, tb, shared_rows,
                                                    counts, offsets, perm, err);
     permute_scatter_kernel<<<nblocks, kScatterThreads, 0, s>>>(idx, S, E, hist, perm, inv);

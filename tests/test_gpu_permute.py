@@ -25,7 +25,9 @@ def run_and_compare(idx_np, E, tile_rows, shared_rows, label):
 
 
 @pytest.mark.parametrize("T,k,E", [(1, 1, 1), (64, 2, 4), (100, 3, 5), (2048, 2, 8),
-                                   (2049, 2, 8), (5000, 2, 8), (40000, 2, 64), (3000, 4, 1024)])
+                                   (2049, 2, 8), (5000, 2, 8), (40000, 2, 64), (3000, 4, 1024),
+                                   # histogram tables past the fused-scan limit: separate scan launch
+                                   (5000, 4, 1024), (200000, 2, 64)])
 def test_permute_uniform(T, k, E):
     rng = np.random.default_rng(T + E)
     idx = rng.integers(0, E, (T, k)).astype(np.int32)
