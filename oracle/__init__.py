@@ -1,4 +1,4 @@
-"""CPU oracle for the top-k routed MoE SwiGLU FFN forward (test infrastructure).
+"""CPU oracle for the top-k routed MoE SwiGLU FFN, forward and backward (test infrastructure).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It shares no code with the HIP path
@@ -12,7 +12,9 @@ Two independent evaluations are offered:
   pages' order (counting sort, per-expert loop over sorted rows, unpermute,
   combine in j order) and also returns the sorted-row intermediates h and Y.
   ``permute`` is the stable counting sort with per-expert counts, offsets and
-  row-tile offsets.
+  row-tile offsets.  ``backward`` is the vector-Jacobian product of the
+  layer (dx, the weight gradients and the routing weights' gradient) by the
+  chain rule on the recomputed forward (Part A section 8 of the first page).
 * ``brute.py``: a separate numpy fp64 brute force for tiny inputs.
 
 Definitions followed are cited in ``moe_oracle.c`` ("Triton MoE Kernels &
@@ -57,6 +59,8 @@ def _load():
         lib.moe_oracle_forward_dense.restype = ci
         lib.moe_oracle_forward_dense.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i64, ci, ci,
                                                  P, i64, P, ci]
+        lib.moe_oracle_backward.restype = ci
+        lib.moe_oracle_backward.argtypes = [P] * 10 + [i64, i64, i64, ci, ci] + [P] * 8 + [ci]
         lib.moe_oracle_forward_permuted.restype = i64
         lib.moe_oracle_forward_permuted.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i64, ci,
                                                     ci, P, P, P, P, P, P, P, ci]
@@ -145,6 +149,43 @@ def forward_permuted(x, topk_idx, topk_w, W1, W3, W2, shared=None, nthreads=1) -
         raise MemoryError("oracle allocation failed")
     return dict(y=y, h=h[:R], Y=Y[:R], counts=counts, offsets=offsets, perm=perm[:S],
                 inv=inv[:S], bad=int(bad))
+
+
+def backward(x, topk_idx, topk_w, W1, W3, W2, shared, dy, nthreads=1) -> dict:
+    """Vector-Jacobian product of the layer for the incoming gradient dy
+    [T,D], fp64: dx [T,D], dW1/dW3 [E,D,F], dW2 [E,F,D], dw [T,k] (the
+    routing weights' gradient, 0 for invalid slots) and, with a shared
+    expert, dWs1/dWs3 [D,F] and dWs2 [F,D] (else None)."""
+    x = _f64(x)
+    T, D = x.shape
+    E, _, F = W1.shape
+    k = topk_idx.shape[1]
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    w = _f64(topk_w)
+    W1, W3, W2 = _f64(W1), _f64(W3), _f64(W2)
+    Ws1, Ws3, Ws2 = _shared(shared)
+    dy = _f64(dy)
+    out = dict(dx=np.empty((T, D)), dW1=np.empty((E, D, F)), dW3=np.empty((E, D, F)),
+               dW2=np.empty((E, F, D)), dw=np.empty((T, k)))
+    sh = Ws1 is not None
+    out.update(dWs1=np.empty((D, F)) if sh else None, dWs3=np.empty((D, F)) if sh else None,
+               dWs2=np.empty((F, D)) if sh else None)
+    rc = _load().moe_oracle_backward(
+        _ptr(x), _ptr(idx), _ptr(w), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1), _ptr(Ws3),
+        _ptr(Ws2), _ptr(dy), T, D, F, E, k, _ptr(out["dx"]), _ptr(out["dW1"]), _ptr(out["dW3"]),
+        _ptr(out["dW2"]), _ptr(out["dWs1"]), _ptr(out["dWs3"]), _ptr(out["dWs2"]),
+        _ptr(out["dw"]), nthreads)
+    if rc != 0:
+        raise MemoryError("oracle allocation failed")
+    return out
+
+
+def backward_flops(T: int, D: int, F: int, k: int, shared: bool) -> int:
+    """Algorithmic FLOPs of one backward with the gate and up products
+    recomputed: per row, the two recomputed up products (4 D F), the
+    gradient of h through W2 (2 D F), the W2 gradient (2 D F), the two W1/W3
+    gradients (4 D F) and dx through W1 and W3 (4 D F): 16 D F."""
+    return 16 * D * F * (T * k + (T if shared else 0))
 
 
 def flops(T: int, D: int, F: int, k: int, shared: bool) -> int:

@@ -42,6 +42,26 @@
  *    sorted position (inv = -1), is not counted and contributes nothing; the
  *    function returns how many such slots it saw.
  *
+ * Backward (moe_oracle_backward): the vector-Jacobian product of the same
+ * layer for an incoming gradient dy, by the chain rule on the recomputed
+ * forward, as "Triton MoE Kernels & Memory Checkpointing" (Part A, section 8)
+ * does it: the gate and up products are recomputed, their gradients are the
+ * upstream gradient times the derivative of silu(g) * u, and the weight
+ * gradients are the outer products of those gradients with the inputs.
+ * Per routed slot (token t, choice j, expert e, weight w = w[t,j]):
+ *
+ *   g = x W1[e],  u = x W3[e],  h = silu(g) * u,  o = h W2[e]
+ *   dw[t,j]  = dy[t] . o                    (gradient of the routing weight)
+ *   dh       = (w dy[t]) W2[e]^T
+ *   dg       = dh * u * silu'(g),   silu'(z) = s (1 + z (1 - s)),  s = 1 / (1 + exp(-z))
+ *   du       = dh * silu(g)
+ *   dW2[e]  += h^T (w dy[t]),  dW1[e] += x^T dg,  dW3[e] += x^T du
+ *   dx[t]   += dg W1[e]^T + du W3[e]^T
+ *
+ * and the same with w = 1 and the shared weights for the shared expert.
+ * dx[t] accumulates the shared expert first, then j = 0 .. k-1; each weight
+ * gradient accumulates tokens in ascending order (choices ascending).
+ *
  * Build: gcc -O2 -fPIC -shared -ffp-contract=off -pthread (no -ffast-math).
  */
 #include <math.h>
@@ -51,6 +71,13 @@
 #include <string.h>
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* d silu / dz = s + z s (1 - s) with s the logistic sigmoid of z. */
+static double dsilu(double z)
+{
+    const double s = 1.0 / (1.0 + exp(-z));
+    return s * (1.0 + z * (1.0 - s));
+}
 
 /*
  * Counting sort of the flattened slots by expert id (stable).
@@ -137,6 +164,9 @@ typedef struct {
     const int32_t *perm, *offsets;
     int64_t S;
     double *h_out, *Y_out;     /* sorted-row results [S(+T), F] and [S(+T), D] */
+    /* backward */
+    const double *dy;
+    double *dx, *dW1, *dW3, *dW2, *dWs1, *dWs3, *dWs2, *dw;
     /* work split */
     int64_t lo, hi;
     int status;
@@ -299,4 +329,149 @@ int64_t moe_oracle_forward_permuted(const double *x, const int32_t *idx, const d
         }
     }
     return bad;
+}
+
+/*
+ * Backward of one (token, expert) pair with routing weight wt (1 for the
+ * shared expert).  xr, dyr: the token's rows [D].  Recomputes g, u, h (and
+ * o when dw is wanted), then adds the pair's contributions to whichever of
+ * dx_acc [D], dW1/dW3 [D,F], dW2 [F,D] and *dw are not NULL.  sc holds 6F
+ * doubles of scratch.
+ */
+static void swiglu_row_backward(const double *xr, const double *dyr, double wt,
+                                const double *W1, const double *W3, const double *W2,
+                                int64_t D, int64_t F, double *sc, double *dx_acc,
+                                double *dW1, double *dW3, double *dW2, double *dw)
+{
+    double *g = sc, *u = sc + F, *h = sc + 2 * F, *dh = sc + 3 * F, *dg = sc + 4 * F,
+           *du = sc + 5 * F;
+    for (int64_t f = 0; f < F; ++f) { g[f] = 0.0; u[f] = 0.0; }
+    for (int64_t d = 0; d < D; ++d) {
+        const double xd = xr[d];
+        const double *w1 = W1 + d * F, *w3 = W3 + d * F;
+        for (int64_t f = 0; f < F; ++f) {
+            g[f] += xd * w1[f];
+            u[f] += xd * w3[f];
+        }
+    }
+    for (int64_t f = 0; f < F; ++f) h[f] = silu(g[f]) * u[f];
+    if (dw) {                                    /* dw = dy . (h W2) */
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            double o = 0.0;
+            for (int64_t f = 0; f < F; ++f) o += h[f] * W2[f * D + d];
+            acc += dyr[d] * o;
+        }
+        *dw = acc;
+    }
+    for (int64_t f = 0; f < F; ++f) {            /* dh[f] = sum_d W2[f][d] (wt dy[d]) */
+        const double *w2 = W2 + f * D;
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d) acc += w2[d] * (wt * dyr[d]);
+        dh[f] = acc;
+    }
+    for (int64_t f = 0; f < F; ++f) {
+        dg[f] = dh[f] * u[f] * dsilu(g[f]);
+        du[f] = dh[f] * silu(g[f]);
+    }
+    if (dW2)
+        for (int64_t f = 0; f < F; ++f)
+            for (int64_t d = 0; d < D; ++d) dW2[f * D + d] += h[f] * (wt * dyr[d]);
+    if (dW1)
+        for (int64_t d = 0; d < D; ++d)
+            for (int64_t f = 0; f < F; ++f) {
+                dW1[d * F + f] += xr[d] * dg[f];
+                dW3[d * F + f] += xr[d] * du[f];
+            }
+    if (dx_acc)
+        for (int64_t d = 0; d < D; ++d) {
+            const double *w1 = W1 + d * F, *w3 = W3 + d * F;
+            double a1 = 0.0, a3 = 0.0;
+            for (int64_t f = 0; f < F; ++f) {
+                a1 += w1[f] * dg[f];
+                a3 += w3[f] * du[f];
+            }
+            dx_acc[d] = dx_acc[d] + a1 + a3;
+        }
+}
+
+/* Tokens [lo, hi): dx[t] and dw[t, :]. */
+static void *bwd_token_worker(void *arg)
+{
+    job_t *J = (job_t *)arg;
+    const int64_t D = J->D, F = J->F;
+    double *sc = malloc(sizeof(double) * 6 * F);
+    if (!sc) { J->status = -1; return NULL; }
+    for (int64_t t = J->lo; t < J->hi; ++t) {
+        const double *xr = J->x + t * D, *dyr = J->dy + t * D;
+        double *dxr = J->dx + t * D;
+        for (int64_t d = 0; d < D; ++d) dxr[d] = 0.0;
+        if (J->Ws1)
+            swiglu_row_backward(xr, dyr, 1.0, J->Ws1, J->Ws3, J->Ws2, D, F, sc, dxr,
+                                NULL, NULL, NULL, NULL);
+        for (int j = 0; j < J->k; ++j) {
+            const int32_t e = J->idx[t * J->k + j];
+            double *dwp = J->dw + t * J->k + j;
+            *dwp = 0.0;
+            if (e < 0 || e >= J->E) continue;
+            swiglu_row_backward(xr, dyr, J->w[t * J->k + j], J->W1 + (int64_t)e * D * F,
+                                J->W3 + (int64_t)e * D * F, J->W2 + (int64_t)e * F * D, D, F,
+                                sc, dxr, NULL, NULL, NULL, dwp);
+        }
+    }
+    free(sc);
+    return NULL;
+}
+
+/* Groups [lo, hi) of 0..E (E: the shared expert): the weight gradients. */
+static void *bwd_expert_worker(void *arg)
+{
+    job_t *J = (job_t *)arg;
+    const int64_t D = J->D, F = J->F;
+    double *sc = malloc(sizeof(double) * 6 * F);
+    if (!sc) { J->status = -1; return NULL; }
+    for (int64_t grp = J->lo; grp < J->hi; ++grp) {
+        const int shared = grp == J->E;
+        const double *A1 = shared ? J->Ws1 : J->W1 + grp * D * F;
+        const double *A3 = shared ? J->Ws3 : J->W3 + grp * D * F;
+        const double *A2 = shared ? J->Ws2 : J->W2 + grp * F * D;
+        double *g1 = shared ? J->dWs1 : J->dW1 + grp * D * F;
+        double *g3 = shared ? J->dWs3 : J->dW3 + grp * D * F;
+        double *g2 = shared ? J->dWs2 : J->dW2 + grp * F * D;
+        memset(g1, 0, sizeof(double) * (size_t)(D * F));
+        memset(g3, 0, sizeof(double) * (size_t)(D * F));
+        memset(g2, 0, sizeof(double) * (size_t)(F * D));
+        for (int64_t t = 0; t < J->T; ++t)
+            for (int j = 0; j < (shared ? 1 : J->k); ++j) {
+                if (!shared && J->idx[t * J->k + j] != grp) continue;
+                swiglu_row_backward(J->x + t * D, J->dy + t * D, shared ? 1.0 : J->w[t * J->k + j],
+                                    A1, A3, A2, D, F, sc, NULL, g1, g3, g2, NULL);
+            }
+    }
+    free(sc);
+    return NULL;
+}
+
+/*
+ * Backward of the layer for the incoming gradient dy [T,D]: dx [T,D],
+ * dW1/dW3 [E,D,F], dW2 [E,F,D], dw [T,k] (0 for invalid slots) and, when
+ * Ws1 is not NULL, dWs1/dWs3 [D,F] and dWs2 [F,D].  Returns 0, or -1 on
+ * allocation failure.
+ */
+int moe_oracle_backward(const double *x, const int32_t *idx, const double *w,
+                        const double *W1, const double *W3, const double *W2,
+                        const double *Ws1, const double *Ws3, const double *Ws2,
+                        const double *dy, int64_t T, int64_t D, int64_t F, int E, int k,
+                        double *dx, double *dW1, double *dW3, double *dW2,
+                        double *dWs1, double *dWs3, double *dWs2, double *dw, int nthreads)
+{
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.x = x; J.idx = idx; J.w = w; J.W1 = W1; J.W3 = W3; J.W2 = W2;
+    J.Ws1 = Ws1; J.Ws3 = Ws3; J.Ws2 = Ws2;
+    J.T = T; J.D = D; J.F = F; J.E = E; J.k = k;
+    J.dy = dy; J.dx = dx; J.dW1 = dW1; J.dW3 = dW3; J.dW2 = dW2;
+    J.dWs1 = dWs1; J.dWs3 = dWs3; J.dWs2 = dWs2; J.dw = dw;
+    if (T > 0 && run_jobs(&J, T, nthreads, bwd_token_worker)) return -1;
+    return run_jobs(&J, E + (Ws1 ? 1 : 0), nthreads, bwd_expert_worker);
 }
