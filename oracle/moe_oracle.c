@@ -126,11 +126,11 @@ int64_t moe_oracle_permute(const int32_t *idx, int64_t S, int E, int BM, int64_t
 }
 
 /*
- * One expert on one row: out[D] = SwiGLU(xr) with W1,W3 [D,F] and W2 [F,D].
- * h[F] receives silu(g)*u.  g and u are scratch of length F.
+ * Gate and up products of one row and the gated activation:
+ * g = xr W1, u = xr W3 (W1, W3 [D,F]), h = silu(g) * u, all of length F.
  */
-static void swiglu_row(const double *xr, const double *W1, const double *W3, const double *W2,
-                       int64_t D, int64_t F, double *g, double *u, double *h, double *out)
+static void gate_up_row(const double *xr, const double *W1, const double *W3, int64_t D,
+                        int64_t F, double *g, double *u, double *h)
 {
     for (int64_t f = 0; f < F; ++f) { g[f] = 0.0; u[f] = 0.0; }
     for (int64_t d = 0; d < D; ++d) {          /* g[f] = sum_d x[d] W1[d][f], d ascending */
@@ -142,6 +142,16 @@ static void swiglu_row(const double *xr, const double *W1, const double *W3, con
         }
     }
     for (int64_t f = 0; f < F; ++f) h[f] = silu(g[f]) * u[f];
+}
+
+/*
+ * One expert on one row: out[D] = SwiGLU(xr) with W1,W3 [D,F] and W2 [F,D].
+ * h[F] receives silu(g)*u.  g and u are scratch of length F.
+ */
+static void swiglu_row(const double *xr, const double *W1, const double *W3, const double *W2,
+                       int64_t D, int64_t F, double *g, double *u, double *h, double *out)
+{
+    gate_up_row(xr, W1, W3, D, F, g, u, h);
     for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
     for (int64_t f = 0; f < F; ++f) {          /* out[d] = sum_f h[f] W2[f][d], f ascending */
         const double hf = h[f];
@@ -345,16 +355,7 @@ static void swiglu_row_backward(const double *xr, const double *dyr, double wt,
 {
     double *g = sc, *u = sc + F, *h = sc + 2 * F, *dh = sc + 3 * F, *dg = sc + 4 * F,
            *du = sc + 5 * F;
-    for (int64_t f = 0; f < F; ++f) { g[f] = 0.0; u[f] = 0.0; }
-    for (int64_t d = 0; d < D; ++d) {
-        const double xd = xr[d];
-        const double *w1 = W1 + d * F, *w3 = W3 + d * F;
-        for (int64_t f = 0; f < F; ++f) {
-            g[f] += xd * w1[f];
-            u[f] += xd * w3[f];
-        }
-    }
-    for (int64_t f = 0; f < F; ++f) h[f] = silu(g[f]) * u[f];
+    gate_up_row(xr, W1, W3, D, F, g, u, h);
     if (dw) {                                    /* dw = dy . (h W2) */
         double acc = 0.0;
         for (int64_t d = 0; d < D; ++d) {
