@@ -1,10 +1,11 @@
-"""MI355X (gfx950) top-k routed MoE SwiGLU FFN forward.
+"""MI355X (gfx950) top-k routed MoE SwiGLU FFN: forward and backward.
 
 Hand-written HIP kernels behind a C ABI (include/moe_ffn.h, built into
 libmoe_ffn.so): stable counting-sort expert permute, bf16-MFMA grouped
 GEMMs over [W1|W3] with a fused silu(g)*u epilogue and over W2, and a
-deterministic unpermute/combine.  This package is the Python binding:
+deterministic unpermute/combine, and the layer's backward.  This package is the Python binding:
 torch supplies device memory and streams, nothing else.
 """
-from ._lib import (MoeError, alloc_workspace, device_error, expert_permute, forward, lib,  # noqa: F401
-                   status_string, tile_rows, workspace_layout, workspace_size, EXPORTS, LIB_PATH)
+from ._lib import (MoeError, alloc_workspace, backward, backward_workspace_layout,  # noqa: F401
+                   device_error, expert_permute, forward, lib, status_string, tile_rows,
+                   workspace_layout, workspace_size, EXPORTS, LIB_PATH)

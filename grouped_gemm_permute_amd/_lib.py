@@ -24,7 +24,8 @@ MOE_VARIANT_UNFUSED, MOE_VARIANT_FUSED = 0, 1
 EXPORTS = (
     "moe_status_string", "moe_ffn_tile_rows", "moe_ffn_workspace_layout", "moe_ffn_workspace_size",
     "moe_ffn_forward", "moe_ffn_forward_timed", "moe_expert_permute", "moe_expert_permute_scratch_size",
-    "moe_ffn_get_device_error",
+    "moe_ffn_get_device_error", "moe_ffn_backward_workspace_layout", "moe_ffn_backward_workspace_size",
+    "moe_ffn_backward", "moe_ffn_backward_timed",
 )
 
 
@@ -40,6 +41,16 @@ class WsLayout(ctypes.Structure):
                  "h", "Y")] + \
                [("tile_rows", ctypes.c_int32), ("hist_blocks", ctypes.c_int32),
                 ("small_tiles", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class BwdWsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("total", "err", "counts", "offsets", "tile_off", "tile_off64", "perm", "inv", "hist",
+                 "gu", "dgu", "hw", "dxr", "dwpart")] + \
+               [("tile_rows", ctypes.c_int32), ("hist_blocks", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -72,6 +83,16 @@ def lib():
         L.moe_expert_permute.argtypes = [P, i64, ci, ci, ci, i64, P, P, P, P, P, P, P, sz, P]
         L.moe_expert_permute_scratch_size.restype = sz
         L.moe_expert_permute_scratch_size.argtypes = [i64, ci, ci]
+        L.moe_ffn_backward_workspace_layout.restype = ci
+        L.moe_ffn_backward_workspace_layout.argtypes = [i64, ci, ci, ci, ci, ci, ci,
+                                                        ctypes.POINTER(BwdWsLayout)]
+        L.moe_ffn_backward_workspace_size.restype = sz
+        L.moe_ffn_backward_workspace_size.argtypes = [i64, ci, ci, ci, ci, ci, ci]
+        bwd_args = [P] * 18 + [i64, ci, ci, ci, ci, ci, P, sz, P]
+        L.moe_ffn_backward.restype = ci
+        L.moe_ffn_backward.argtypes = bwd_args
+        L.moe_ffn_backward_timed.restype = ci
+        L.moe_ffn_backward_timed.argtypes = bwd_args + [P]
         L.moe_ffn_get_device_error.restype = ci
         L.moe_ffn_get_device_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32)]
         _lib = L
@@ -196,3 +217,59 @@ def device_error(workspace, stream=None) -> int:
     _check(lib().moe_ffn_get_device_error(_ptr(workspace), _stream(stream), ctypes.byref(v)),
            "moe_ffn_get_device_error")
     return int(v.value)
+
+
+def backward_workspace_layout(T, D, F, E, k, has_shared, dtype) -> dict:
+    L = BwdWsLayout()
+    _check(lib().moe_ffn_backward_workspace_layout(T, D, F, E, k, int(has_shared), _dtype_enum(dtype),
+                                                   ctypes.byref(L)),
+           "moe_ffn_backward_workspace_layout")
+    return L.as_dict()
+
+
+def backward(x, topk_idx, topk_w, W1, W3, W2, shared, dy, out=None, workspace=None, stream=None,
+             events=None) -> dict:
+    """moe_ffn_backward(...): gradients of the layer for the incoming dy [T,D].
+    Returns dx [T,D] (x's dtype), dW1/dW3 [E,D,F], dW2 [E,F,D], dWs1/dWs3
+    [D,F], dWs2 [F,D] (None without a shared expert) and dtopk_w [T,k], all
+    fp32 except dx.  ``out`` may supply any of these tensors.  ``events``: a
+    ctypes array of eight hipEvent_t handles (moe_ffn_backward_timed)."""
+    if topk_idx.dtype != torch.int32 or topk_w.dtype != torch.float32:
+        raise TypeError("topk_idx must be int32 and topk_w float32")
+    for t in (x, topk_idx, topk_w, W1, W3, W2, dy, *(shared or ())):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    T, D = x.shape
+    E, _, F = W1.shape
+    k = topk_idx.shape[1]
+    if dy.shape != (T, D) or dy.dtype != x.dtype:
+        raise ValueError("dy must be [T,D] with x's dtype")
+    if W1.shape != (E, D, F) or W3.shape != (E, D, F) or W2.shape != (E, F, D):
+        raise ValueError("weight shapes must be W1/W3 [E,D,F], W2 [E,F,D]")
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    o = dict(out or {})
+    o.setdefault("dx", torch.empty((T, D), dtype=x.dtype, device=dev))
+    o.setdefault("dW1", torch.empty((E, D, F), **f32))
+    o.setdefault("dW3", torch.empty((E, D, F), **f32))
+    o.setdefault("dW2", torch.empty((E, F, D), **f32))
+    o.setdefault("dtopk_w", torch.empty((T, k), **f32))
+    if shared is not None:
+        o.setdefault("dWs1", torch.empty((D, F), **f32))
+        o.setdefault("dWs3", torch.empty((D, F), **f32))
+        o.setdefault("dWs2", torch.empty((F, D), **f32))
+    else:
+        o["dWs1"] = o["dWs3"] = o["dWs2"] = None
+    Ws1, Ws3, Ws2 = shared if shared is not None else (None, None, None)
+    if workspace is None:
+        n = backward_workspace_layout(T, D, F, E, k, shared is not None, x.dtype)["total"]
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    args = (_ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1),
+            _ptr(Ws3), _ptr(Ws2), _ptr(dy), _ptr(o["dx"]), _ptr(o["dW1"]), _ptr(o["dW3"]),
+            _ptr(o["dW2"]), _ptr(o["dWs1"]), _ptr(o["dWs3"]), _ptr(o["dWs2"]), _ptr(o["dtopk_w"]),
+            T, D, F, E, k, _dtype_enum(x.dtype), _ptr(workspace), workspace.numel(), _stream(stream))
+    if events is None:
+        _check(lib().moe_ffn_backward(*args), "moe_ffn_backward")
+    else:
+        _check(lib().moe_ffn_backward_timed(*args, events), "moe_ffn_backward_timed")
+    return o

@@ -13,7 +13,8 @@
 // is scaled and added in fp32 (one fused multiply-add per term) in j order,
 // starting from the shared row (or 0), and rounded once to the output
 // type, so the result does not depend on scheduling (no scatter atomics).
-// Slots with inv = -1 (invalid ids) add nothing.
+// Slots with inv = -1 (invalid ids) add nothing.  topk_w == nullptr means
+// weight 1 on every slot (the backward's gather of dx rows).
 #include "moe_internal.h"
 
 namespace moe {
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(NT) void combine_bf16_kernel(const uint16_t* __rest
     for (int j = 0; j < k; ++j) {
         const int32_t p = inv[t * k + j];
         if (p < 0 || p >= S) continue;      // invalid slot (p == -1)
-        add(Y + (int64_t)p * D + c, topk_w[t * k + j]);
+        add(Y + (int64_t)p * D + c, topk_w ? topk_w[t * k + j] : 1.f);
     }
     *(uint4*)(y + t * D + c) = make_uint4(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
                                           pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7]));
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(NT) void combine_f32_kernel(const float* __restrict
     for (int j = 0; j < k; ++j) {
         const int32_t p = inv[t * k + j];
         if (p < 0 || p >= S) continue;
-        acc = fmaf(topk_w[t * k + j], Y[(int64_t)p * D + c], acc);
+        acc = fmaf(topk_w ? topk_w[t * k + j] : 1.f, Y[(int64_t)p * D + c], acc);
     }
     y[t * D + c] = acc;
 }

@@ -1,0 +1,52 @@
+// moe_bwd_internal.h -- launchers of the backward pass shared between the
+// translation units of libmoe_ffn.so.  Not part of the public ABI.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// Width of the column blocks whose partial sums of dy . o the dh kernel
+// writes (one fp32 per row and block).
+constexpr int kBwdDwBlock = 64;
+inline int bwd_dw_blocks(int F) { return (F + kBwdDwBlock - 1) / kBwdDwBlock; }
+
+// Everything the backward kernels read about the problem besides the
+// tensors of one stage.
+struct BwdArgs {
+    GroupArgs g;
+    const float* topk_w;   // [S] routing weight of each slot
+    int D, F;
+    bool bf16;             // element type of x, dy, weights and the row buffers
+};
+
+// gu[p] = [x W1 | x W3] of row p (gate in columns 0..F-1, up in F..2F-1),
+// fp32 accumulation, stored in the row element type.
+hipError_t launch_bwd_gate_up(const BwdArgs& a, const void* x, const void* W1, const void* W3,
+                              const void* Ws1, const void* Ws3, void* gu, hipStream_t s);
+
+// From dh' = dy[tok(p)] W2[grp]^T (fp32 accumulation) and the row's g, u:
+//   dwpart[p][b] = sum over columns f of block b of dh'[f] * h[f], h = silu(g) * u
+//   dgu[p] = [dg | du] with dh = w dh', dg = dh * u * silu'(g), du = dh * silu(g)
+//   hw[p]  = w * h
+// (w = the routing weight of the row's slot, 1 on shared rows).
+hipError_t launch_bwd_dh(const BwdArgs& a, const void* dy, const void* W2, const void* Ws2,
+                         const void* gu, void* dgu, void* hw, float* dwpart, hipStream_t s);
+
+// dxr[p] = dg W1[grp]^T + du W3[grp]^T (fp32 accumulation, row element type).
+hipError_t launch_bwd_dx_rows(const BwdArgs& a, const void* dgu, const void* W1, const void* W3,
+                              const void* Ws1, const void* Ws3, void* dxr, hipStream_t s);
+
+// Weight gradients, fp32, every element written (zero for an empty group):
+//   [dW1 | dW3][grp] = sum over the group's rows p of x[tok(p)]^T dgu[p]
+//   dW2[grp]         = sum over the group's rows p of hw[p]^T dy[tok(p)]
+hipError_t launch_bwd_dw13(const BwdArgs& a, const void* x, const void* dgu, float* dW1,
+                           float* dW3, float* dWs1, float* dWs3, hipStream_t s);
+hipError_t launch_bwd_dw2(const BwdArgs& a, const void* hw, const void* dy, float* dW2,
+                          float* dWs2, hipStream_t s);
+
+// dtopk_w[s] = sum_b dwpart[inv[s]][b] in b order (0 for an invalid slot).
+hipError_t launch_bwd_dtopk(const BwdArgs& a, const int32_t* inv, const float* dwpart,
+                            float* dtopk_w, hipStream_t s);
+
+}  // namespace moe

@@ -204,6 +204,106 @@ size_t moe_expert_permute_scratch_size(int64_t T, int k, int E);
  */
 moe_status moe_ffn_get_device_error(const void *workspace, hipStream_t stream, int32_t *out);
 
+/* ------------------------------------------------------------------------
+ * Backward pass.
+ *
+ * The vector-Jacobian product of the layer for an incoming gradient dy:
+ * the autograd contract of "Triton MoE Kernels & Memory Checkpointing"
+ * (Part A, section 8) -- the gate and up products are recomputed from x
+ * instead of being saved by the forward, their gradients are the upstream
+ * gradient times the derivative of silu(g) * u, and the weight gradients
+ * are the outer products of those gradients with the inputs -- extended by
+ * the same chain rule through W2 and the weighted combine (same page,
+ * section 10.3).  Per routed slot (token t, choice j, expert e, weight w):
+ *
+ *   g = x[t] W1[e], u = x[t] W3[e], h = silu(g) * u, o = h W2[e]
+ *   dtopk_w[t,j] = dy[t] . o
+ *   dh = w dy[t] W2[e]^T,  dg = dh * u * silu'(g),  du = dh * silu(g)
+ *   dW2[e] += h^T (w dy[t]),  dW1[e] += x[t]^T dg,  dW3[e] += x[t]^T du
+ *   dx[t]  += dg W1[e]^T + du W3[e]^T
+ *
+ * and the same with w = 1 and the shared weights for the shared expert.
+ * ------------------------------------------------------------------------ */
+
+/* Byte offsets of the pieces of a backward workspace (256-byte aligned);
+ * rows as in the forward (R = T*k + T*[shared]). */
+typedef struct moe_bwd_ws_layout {
+    size_t total;       /* bytes the workspace must hold */
+    size_t err, counts, offsets, tile_off, tile_off64, perm, inv, hist;   /* the permute's, as forward */
+    size_t gu;          /* [R, 2F] recomputed gate (columns 0..F-1) and up (F..2F-1), dtype of the call */
+    size_t dgu;         /* [R, 2F] gradients of the gate and up products, dtype of the call */
+    size_t hw;          /* [R, F]  w * h per row, dtype of the call */
+    size_t dxr;         /* [R, D]  each row's contribution to dx, dtype of the call */
+    size_t dwpart;      /* fp32 [R, ceil(F/64)] partial sums of dy . o per 64 columns */
+    int32_t tile_rows;  /* row-tile height of tile_off */
+    int32_t hist_blocks;/* slot blocks of the multi-block permute (0: single block) */
+} moe_bwd_ws_layout;
+
+/* Fill *layout for a backward call of these sizes.  Returns MOE_OK,
+ * MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED under the same rules as
+ * moe_ffn_workspace_layout (variant unfused). */
+moe_status moe_ffn_backward_workspace_layout(int64_t T, int D, int F, int E, int k, int has_shared,
+                                             moe_dtype dtype, moe_bwd_ws_layout *layout);
+
+/* Backward workspace bytes; 0 if the sizes are invalid or unsupported. */
+size_t moe_ffn_backward_workspace_size(int64_t T, int D, int F, int E, int k, int has_shared,
+                                       moe_dtype dtype);
+
+/*
+ * Backward of moe_ffn_forward for the incoming gradient dy.
+ *
+ *   x, topk_idx, topk_w, W1, W3, W2, Ws1, Ws3, Ws2: the forward's inputs
+ *                (same types, layouts and alignment rules; the shared
+ *                weights all NULL for none)
+ *   dy        [T, D]     dtype; gradient of the loss with respect to y
+ *   dx        [T, D]     dtype; out, fully overwritten
+ *   dW1, dW3  [E, D, F]  fp32; out, fully overwritten (zero for an expert no slot chose)
+ *   dW2       [E, F, D]  fp32; out
+ *   dWs1, dWs3 [D, F], dWs2 [F, D]  fp32; out, required exactly when the
+ *                shared weights are given
+ *   dtopk_w   [T, k]     fp32; out, dy[t] . o for each slot, 0 for an
+ *                invalid slot
+ *   workspace >= moe_ffn_backward_workspace_size() bytes, 256-byte aligned
+ *
+ * Precision: fp32 accumulation throughout.  bf16 calls store the recomputed
+ * g and u, the gradients dg and du, w*h and the per-row dx contributions as
+ * bf16 (round to nearest even) between kernels; the weight gradients and
+ * dtopk_w are written in fp32.  Summation orders are fixed (no atomics), so
+ * repeated calls give bitwise-identical results.  Slots with an
+ * out-of-range id are counted in the error flag (moe_ffn_get_device_error)
+ * and contribute nothing.
+ *
+ * Returns MOE_OK, MOE_ERR_INVALID_ARG (null or misaligned pointer, sizes
+ * as in the forward, only some of the shared weights or their gradients
+ * given), MOE_ERR_UNSUPPORTED (bf16 with D or F not a multiple of 64),
+ * MOE_ERR_WORKSPACE, MOE_ERR_HIP.  With T == 0 the weight gradients are
+ * written as zeros and nothing else is touched.
+ */
+moe_status moe_ffn_backward(const void *x, const int32_t *topk_idx, const float *topk_w,
+                            const void *W1, const void *W3, const void *W2,
+                            const void *Ws1, const void *Ws3, const void *Ws2,
+                            const void *dy, void *dx, float *dW1, float *dW3, float *dW2,
+                            float *dWs1, float *dWs3, float *dWs2, float *dtopk_w,
+                            int64_t T, int D, int F, int E, int k, moe_dtype dtype,
+                            void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_ffn_backward plus per-stage timing: events[0] before the permute,
+ * events[1] after it, [2] after the gate/up recompute, [3] after the dh
+ * stage, [4] after the per-row dx products, [5] after the W1/W3 gradients,
+ * [6] after the W2 gradient, [7] after dtopk_w and the dx combine (eight
+ * caller-created hipEvent_t on `stream`).  events == NULL behaves exactly
+ * like moe_ffn_backward.
+ */
+moe_status moe_ffn_backward_timed(const void *x, const int32_t *topk_idx, const float *topk_w,
+                                  const void *W1, const void *W3, const void *W2,
+                                  const void *Ws1, const void *Ws3, const void *Ws2,
+                                  const void *dy, void *dx, float *dW1, float *dW3, float *dW2,
+                                  float *dWs1, float *dWs3, float *dWs2, float *dtopk_w,
+                                  int64_t T, int D, int F, int E, int k, moe_dtype dtype,
+                                  void *workspace, size_t ws_bytes, hipStream_t stream,
+                                  hipEvent_t events[8]);
+
 #ifdef __cplusplus
 }
 #endif

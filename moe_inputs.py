@@ -140,6 +140,20 @@ def make_inputs(w: Workload | int, seed: int | None = None, T: int | None = None
     return out
 
 
+def add_output_grad(inp: dict, seed: int | None = None) -> dict:
+    """Draw the incoming gradient dy [T, D] ~ N(0, 1) for a backward pass,
+    from its own stream (seed + 7919, so the forward inputs are unchanged),
+    stored like x.  Adds ``dy`` (and ``dy_bits`` for bf16) to ``inp``."""
+    w = inp["workload"]
+    seed = inp["seed"] + 7919 if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    vals, bits = _store(rng.standard_normal((inp["T"], w.D), dtype=np.float32), w.dtype)
+    inp["dy"] = vals
+    if bits is not None:
+        inp["dy_bits"] = bits
+    return inp
+
+
 def input_digest(inp: dict) -> str:
     """sha256 over the stored bytes of every input tensor, in a fixed order."""
     h = hashlib.sha256()

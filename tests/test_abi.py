@@ -120,3 +120,49 @@ def test_permute_rejects_bad_arguments_on_host():
 def test_device_error_rejects_null():
     v = ctypes.c_int32()
     assert L.lib().moe_ffn_get_device_error(None, None, ctypes.byref(v)) == L.MOE_ERR_INVALID_ARG
+
+
+def test_backward_layout_is_aligned_and_sized():
+    import torch
+    lay = L.backward_workspace_layout(32768, 768, 1536, 8, 2, True, torch.bfloat16)
+    R = 32768 * 3
+    for key in ("err", "counts", "offsets", "tile_off", "perm", "inv", "hist", "gu", "dgu", "hw",
+                "dxr", "dwpart"):
+        assert lay[key] % 256 == 0
+    assert lay["gu"] + R * 2 * 1536 * 2 <= lay["dgu"]
+    assert lay["dgu"] + R * 2 * 1536 * 2 <= lay["hw"]
+    assert lay["hw"] + R * 1536 * 2 <= lay["dxr"]
+    assert lay["dxr"] + R * 768 * 2 <= lay["dwpart"]
+    assert lay["dwpart"] + R * (1536 // 64) * 4 <= lay["total"]
+    assert L.lib().moe_ffn_backward_workspace_size(32768, 768, 1536, 8, 2, 1, L.MOE_BF16) == lay["total"]
+
+
+def _bwd(**over):
+    a = dict(x=FAKE, idx=FAKE, w=FAKE, W1=FAKE, W3=FAKE, W2=FAKE, Ws1=None, Ws3=None, Ws2=None,
+             dy=FAKE, dx=FAKE, dW1=FAKE, dW3=FAKE, dW2=FAKE, dWs1=None, dWs3=None, dWs2=None,
+             dtw=FAKE, T=16, D=64, F=128, E=4, k=2, dt=L.MOE_BF16, ws=FAKE, nbytes=1 << 40)
+    a.update(over)
+    return L.lib().moe_ffn_backward(
+        a["x"], a["idx"], a["w"], a["W1"], a["W3"], a["W2"], a["Ws1"], a["Ws3"], a["Ws2"], a["dy"],
+        a["dx"], a["dW1"], a["dW3"], a["dW2"], a["dWs1"], a["dWs3"], a["dWs2"], a["dtw"], a["T"],
+        a["D"], a["F"], a["E"], a["k"], a["dt"], a["ws"], a["nbytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k=5), L.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), L.MOE_ERR_INVALID_ARG),
+    (dict(dt=3), L.MOE_ERR_INVALID_ARG),
+    (dict(dy=None), L.MOE_ERR_INVALID_ARG),
+    (dict(dx=None), L.MOE_ERR_INVALID_ARG),
+    (dict(dW2=None), L.MOE_ERR_INVALID_ARG),
+    (dict(dtw=None), L.MOE_ERR_INVALID_ARG),
+    (dict(dx=FAKE + 8), L.MOE_ERR_INVALID_ARG),
+    (dict(dW1=FAKE + 4), L.MOE_ERR_INVALID_ARG),
+    (dict(Ws1=FAKE, Ws3=FAKE, Ws2=FAKE), L.MOE_ERR_INVALID_ARG),     # shared weights without their gradients
+    (dict(dWs1=FAKE, dWs3=FAKE, dWs2=FAKE), L.MOE_ERR_INVALID_ARG),  # gradients without shared weights
+    (dict(D=96), L.MOE_ERR_UNSUPPORTED),
+    (dict(nbytes=1024), L.MOE_ERR_WORKSPACE),
+    (dict(ws=FAKE + 64), L.MOE_ERR_INVALID_ARG),
+])
+def test_backward_rejects_bad_arguments_on_host(over, status):
+    assert _bwd(**over) == status
