@@ -49,7 +49,7 @@ class WsLayout(ctypes.Structure):
 class BwdWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("total", "err", "counts", "offsets", "tile_off", "tile_off64", "perm", "inv", "hist",
-                 "gu", "dgu", "hw", "dxr", "dwpart")] + \
+                 "gu", "dgu", "hw", "dxr", "dwpart", "w2t", "w13t")] + \
                [("tile_rows", ctypes.c_int32), ("hist_blocks", ctypes.c_int32)]
 
     def as_dict(self):
@@ -233,7 +233,7 @@ def backward(x, topk_idx, topk_w, W1, W3, W2, shared, dy, out=None, workspace=No
     Returns dx [T,D] (x's dtype), dW1/dW3 [E,D,F], dW2 [E,F,D], dWs1/dWs3
     [D,F], dWs2 [F,D] (None without a shared expert) and dtopk_w [T,k], all
     fp32 except dx.  ``out`` may supply any of these tensors.  ``events``: a
-    ctypes array of eight hipEvent_t handles (moe_ffn_backward_timed)."""
+    ctypes array of nine hipEvent_t handles (moe_ffn_backward_timed)."""
     if topk_idx.dtype != torch.int32 or topk_w.dtype != torch.float32:
         raise TypeError("topk_idx must be int32 and topk_w float32")
     for t in (x, topk_idx, topk_w, W1, W3, W2, dy, *(shared or ())):

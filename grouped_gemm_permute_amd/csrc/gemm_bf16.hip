@@ -17,6 +17,20 @@
 //              W2 product of the same page's section 10.3; the combine applies
 //              the routing weight (its step 4).
 //
+// and, for the backward (the same page's Part A section 8: recompute the
+// gate and up products, then the chain rule through silu(g) * u):
+//
+//  gate_up:    gu[p] = [g | u] rounded to bf16 (g in columns 0..F-1, u in
+//              F..2F-1): the up GEMM with the activation left out.
+//  dh:         dh' = dy[tok(p)] . W2t[grp] with W2t[grp] = W2[grp]^T ([D, F]),
+//              then per element, with g, u read back from gu and w the row's
+//              routing weight (1 on shared rows):
+//                h = silu(g) u,  dg = w dh' u silu'(g),  du = w dh' silu(g)
+//                dgu[p] = [dg | du],  hw[p] = w h   (bf16)
+//                dwpart[p][b] = sum over the 64 columns of block b of dh' h (fp32)
+//  The backward's dx rows are the down mode run with K = 2F over the
+//  transposed, stacked [W1^T ; W3^T] and A = dgu.
+//
 // Tile engine (256 threads = 4 wavefronts, one per SIMD):
 //  * the MFMA computes the transposed tile C^T = W^T . X^T: its A operand is
 //    a 32-feature block of the weights, its B operand a 32-token block of
@@ -67,20 +81,35 @@ static_assert(TT == 256 && TF == 256 && BK == 32 && NT == 256, "index math below
 // chunk hit 16 distinct bank groups.
 __device__ __forceinline__ int swz_x(int row) { return (row >> 2) & 3; }
 
-struct GemmArgs {
-    GroupArgs g;
-    const uint16_t* a;        // up: x [T, D]; down: h [R, F]
-    const uint16_t* b0;       // up: W1 [E, D, F]; down: W2 [E, F, D]
-    const uint16_t* b1;       // up: W3; down: unused
-    const uint16_t* bs0;      // shared expert: up Ws1, down Ws2
-    const uint16_t* bs1;      // up Ws3
-    void* out;                // up: h bf16 [R, F]; down: Y bf16 [R, D]
-    int D, F;
-    int n_tiles;              // column tiles
+// Kernel modes.
+enum : int {
+    M_UP = 0,      // x gathered . [W1 | W3] -> h = silu(g) u
+    M_DOWN = 1,    // rows . W2 -> Y (also the backward's dx rows)
+    M_GU = 2,      // x gathered . [W1 | W3] -> [g | u]
+    M_DH = 3,      // dy gathered . W2t -> dgu, hw, dwpart
 };
 
-template <bool UP>
+struct GemmArgs {
+    GroupArgs g;
+    const uint16_t* a;        // up, gu: x [T, D]; down: h [R, F]; dh: dy [T, D]
+    const uint16_t* b0;       // up, gu: W1 [E, D, F]; down: W2 [E, F, D]; dh: W2t [E, D, F]
+    const uint16_t* b1;       // up, gu: W3; otherwise unused
+    const uint16_t* bs0;      // shared expert: Ws1 / Ws2 / Ws2t
+    const uint16_t* bs1;      // up, gu: Ws3
+    void* out;                // up: h [R, F]; down: Y [R, D]; gu: gu [R, 2F]; dh: dgu [R, 2F]
+    int D, F;
+    int n_tiles;              // column tiles
+    // dh only
+    const float* topk_w;      // [S] routing weight of each slot
+    const uint16_t* gu;       // [R, 2F] recomputed g and u
+    uint16_t* hw;             // [R, F] w * h
+    float* dwpart;            // [R, F / 64] partial sums of dh' * h
+};
+
+template <int MODE>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs a) {
+    constexpr bool UP = MODE != M_DOWN;         // A gathered by token, K = D, N = F
+    constexpr bool PAIR = MODE == M_UP || MODE == M_GU;   // g / u column pairs from W1, W3
     // Four stage buffers as separate LDS objects: every access names its
     // buffer statically, so the compiler knows reads of one buffer do not
     // alias the asynchronous global_load_lds writes into the others.
@@ -148,7 +177,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
         const int cl = (lane & 31) ^ swz_tr(kr);
         int col;
         const uint16_t* base;
-        if (UP) {
+        if (PAIR) {
             const int kind = (cl >> 2) & 1;
             col = nt * (TF / 2) + 32 * (cl >> 3) + 8 * (cl & 3);
             base = shared ? (kind ? a.bs1 : a.bs0) : (kind ? a.b1 : a.b0) + grp * gstride;
@@ -301,7 +330,66 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     // feature's offset in its 32-block (g in mi = 0, u in mi = 1); down:
     // output column = MFMA feature.  Tile rows 64 q .. 64 q + 63 are staged in
     // stage buffer q, 16-byte chunks XOR-swizzled by the row's low 4 bits.
-    constexpr int OCOLS = UP ? TF / 2 : TF;     // output columns of the tile
+    if constexpr (MODE == M_DH) {
+        // Element v of acc[mi][nj] on lane l: token 32 nj + l%32, column
+        // nt*256 + 64 w + 32 mi + 8 (v/4) + 4 (l/32) + v%4; each lane handles
+        // four consecutive columns at a time.  The wavefront's 64 columns are
+        // one dwpart block; the two lane halves holding a token's columns are
+        // added with one cross-lane exchange.
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        const int F = a.F;
+        const int nbk = F / 64;
+        const int blk = nt * 4 + wave;
+        if (nt * TF + 64 * wave >= F) return;     // F % 64 == 0: a wavefront's columns exist or not together
+#pragma unroll
+        for (int nj = 0; nj < 8; ++nj) {
+            const int t = 32 * nj + (lane & 31);
+            const bool ok = t < valid_rows;
+            const int64_t p = tile_r0 + min(t, valid_rows - 1);
+            const float w = shared ? 1.f : a.topk_w[a.g.perm[p]];
+            const uint16_t* gr = a.gu + p * 2 * F;
+            uint16_t* dg_row = (uint16_t*)a.out + p * 2 * F;
+            uint16_t* hw_row = a.hw + p * F;
+            float part = 0.f;
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+                const f32x16_t& c = acc[mi][nj];
+#pragma unroll
+                for (int vg = 0; vg < 4; ++vg) {
+                    const int f0 = nt * TF + 64 * wave + 32 * mi + 8 * vg + 4 * (lane >> 5);
+                    const uint2 graw = *(const uint2*)(gr + f0);
+                    const uint2 uraw = *(const uint2*)(gr + F + f0);
+                    const float gv[4] = {__uint_as_float(graw.x << 16), __uint_as_float(graw.x & 0xffff0000u),
+                                         __uint_as_float(graw.y << 16), __uint_as_float(graw.y & 0xffff0000u)};
+                    const float uv[4] = {__uint_as_float(uraw.x << 16), __uint_as_float(uraw.x & 0xffff0000u),
+                                         __uint_as_float(uraw.y << 16), __uint_as_float(uraw.y & 0xffff0000u)};
+                    float dg[4], du[4], hv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float dhp = c[4 * vg + i];
+                        const float sg = __builtin_amdgcn_rcpf(
+                            1.0f + __builtin_amdgcn_exp2f(-gv[i] * 1.4426950408889634f));
+                        const float act = gv[i] * sg;
+                        const float h = act * uv[i];
+                        part = fmaf(dhp, h, part);
+                        const float dh = w * dhp;
+                        dg[i] = dh * uv[i] * (sg * (1.0f + gv[i] * (1.0f - sg)));
+                        du[i] = dh * act;
+                        hv[i] = w * h;
+                    }
+                    if (ok) {
+                        *(uint2*)(dg_row + f0) = make_uint2(pack_bf16(dg[0], dg[1]), pack_bf16(dg[2], dg[3]));
+                        *(uint2*)(dg_row + F + f0) = make_uint2(pack_bf16(du[0], du[1]), pack_bf16(du[2], du[3]));
+                        *(uint2*)(hw_row + f0) = make_uint2(pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3]));
+                    }
+                }
+            }
+            part += __shfl_xor(part, 32);
+            if (ok && lane < 32) a.dwpart[p * nbk + blk] = part;
+        }
+        return;
+    }
+    constexpr int OCOLS = MODE == M_UP ? TF / 2 : TF;   // output columns of the tile
     constexpr int OROW = OCOLS * 2;             // bytes per staged row
     constexpr int OCH = OROW / 16;              // 16-byte chunks per row
     static_assert(64 * OROW <= STAGE_BYTES, "a stage buffer holds 64 staged rows");
@@ -316,7 +404,20 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
         const int t = 32 * nj + (lane & 31);
         char* rowp = orow(t);
         const int sw = t & 15;
-        if (UP) {
+        if (MODE == M_GU) {
+            // g (mi = 0) to staged columns 32 w + ..., u (mi = 1) to 128 + 32 w + ...
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+                const f32x16_t& c = acc[mi][nj];
+#pragma unroll
+                for (int vg = 0; vg < 4; ++vg) {
+                    const int v = 4 * vg;
+                    const int ch = 16 * mi + 4 * wave + vg;
+                    *(uint2*)(rowp + ((ch ^ sw) << 4) + 8 * (lane >> 5)) =
+                        make_uint2(pack_bf16(c[v], c[v + 1]), pack_bf16(c[v + 2], c[v + 3]));
+                }
+            }
+        } else if (MODE == M_UP) {
             const f32x16_t& g = acc[0][nj];
             const f32x16_t& u = acc[1][nj];
 #pragma unroll
@@ -344,12 +445,16 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     __syncthreads();
     constexpr int ROWS_PER_PASS = NT / OCH;
     const int c = tid % OCH;
-    const int col = nt * OCOLS + 8 * c;
+    // gate_up: staged columns 0..127 are g, 128..255 u, of h columns nt*128 + ...
+    const int col = MODE == M_GU ? (c < 16 ? nt * 128 + 8 * c : N + nt * 128 + 8 * (c - 16))
+                                 : nt * OCOLS + 8 * c;
+    const int ldo = MODE == M_GU ? 2 * N : N;
+    const bool col_ok = MODE == M_GU ? nt * 128 + 8 * (c & 15) < N : col < N;
 #pragma unroll 4
     for (int r = tid / OCH; r < TT; r += ROWS_PER_PASS) {
         if (r >= valid_rows) break;
         const u32x4_t v = *(const u32x4_t*)(orow(r) + ((c ^ (r & 15)) << 4));
-        if (col < N) *(u32x4_t*)((uint16_t*)a.out + (tile_r0 + r) * (int64_t)N + col) = v;
+        if (col_ok) *(u32x4_t*)((uint16_t*)a.out + (tile_r0 + r) * (int64_t)ldo + col) = v;
     }
 }
 
@@ -366,7 +471,7 @@ hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* 
     GemmArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, h, D, F, (F + TF / 2 - 1) / (TF / 2)};
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<true><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    grouped_gemm_bf16_kernel<M_UP><<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -375,7 +480,27 @@ hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, c
     GemmArgs a{g, (const uint16_t*)h, (const uint16_t*)W2, nullptr, (const uint16_t*)Ws2, nullptr,
                Y, D, F, (D + TF - 1) / TF};
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<false><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    grouped_gemm_bf16_kernel<M_DOWN><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_gate_up_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
+                                   const void* Ws1, const void* Ws3, void* gu, int D, int F,
+                                   hipStream_t s) {
+    GemmArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
+               (const uint16_t*)Ws1, (const uint16_t*)Ws3, gu, D, F, (F + TF / 2 - 1) / (TF / 2)};
+    const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
+    grouped_gemm_bf16_kernel<M_GU><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dh_bf16(const GroupArgs& g, const float* topk_w, const void* dy,
+                              const void* W2t, const void* Ws2t, const void* gu, void* dgu, void* hw,
+                              float* dwpart, int D, int F, hipStream_t s) {
+    GemmArgs a{g, (const uint16_t*)dy, (const uint16_t*)W2t, nullptr, (const uint16_t*)Ws2t, nullptr,
+               dgu, D, F, (F + TF - 1) / TF, topk_w, (const uint16_t*)gu, (uint16_t*)hw, dwpart};
+    const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
+    grouped_gemm_bf16_kernel<M_DH><<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -1,8 +1,8 @@
 // moe_bwd.hip -- host side of the backward entry points declared in
 // include/moe_ffn.h: argument validation, workspace carving and the launch
 // order
-//   permute -> gate/up recompute -> dh stage -> per-row dx -> dW1/dW3 -> dW2
-//   -> dtopk_w and the dx combine
+//   permute -> (bf16: weight transposes) -> gate/up recompute -> dh stage
+//   -> per-row dx -> dW1/dW3 -> dW2 -> dtopk_w and the dx combine
 // on the caller's stream, with no host synchronisation.  A shape the kernels
 // do not implement is an error, never a switch to another path ("Triton MoE
 // Kernels & Memory Checkpointing", Part A section 9).
@@ -51,6 +51,11 @@ moe_status make_bwd_layout(int64_t T, int D, int F, int E, int k, int has_shared
     L->hw = take(esize * (size_t)R * (size_t)F);
     L->dxr = take(esize * (size_t)R * (size_t)D);
     L->dwpart = take(sizeof(float) * (size_t)R * (size_t)bwd_dw_blocks(F));
+    // bf16: transposed weights for the engine's [K, N] weight tiles
+    const size_t G = (size_t)E + (has_shared ? 1 : 0);
+    const bool tr = dt == MOE_BF16;
+    L->w2t = take(tr ? 2 * G * (size_t)D * (size_t)F : 0);
+    L->w13t = take(tr ? 2 * G * 2 * (size_t)F * (size_t)D : 0);
     L->total = off;
     L->tile_rows = dt == MOE_BF16 ? kBf16TileRows : kF32TileRows;
     L->hist_blocks = nb;
@@ -122,27 +127,54 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
     if (e == hipSuccess) e = mark(1);
     const BwdArgs a{GroupArgs{offsets, tile_off, perm, S, T, E, k, E + (has_shared ? 1 : 0)},
                     topk_w, D, F, bf16};
-    if (T > 0) {
-        if (e == hipSuccess) e = launch_bwd_gate_up(a, x, W1, W3, Ws1, Ws3, gu, stream);
+    if (T > 0 && bf16) {
+        // W2 -> W2t [E(+1), D, F]; W1, W3 -> W13t [E(+1), 2F, D] (W1^T rows first)
+        uint16_t* w2t = (uint16_t*)(ws + L.w2t);
+        uint16_t* w13t = (uint16_t*)(ws + L.w13t);
+        const int64_t df = (int64_t)D * F;
+        if (e == hipSuccess) e = launch_transpose_bf16(W2, E, F, D, w2t, df, F, 0, stream);
+        if (e == hipSuccess) e = launch_transpose_bf16(W1, E, D, F, w13t, 2 * df, D, 0, stream);
+        if (e == hipSuccess) e = launch_transpose_bf16(W3, E, D, F, w13t, 2 * df, D, F, stream);
+        if (has_shared) {
+            if (e == hipSuccess) e = launch_transpose_bf16(Ws2, 1, F, D, w2t + E * df, df, F, 0, stream);
+            if (e == hipSuccess)
+                e = launch_transpose_bf16(Ws1, 1, D, F, w13t + 2 * E * df, 2 * df, D, 0, stream);
+            if (e == hipSuccess)
+                e = launch_transpose_bf16(Ws3, 1, D, F, w13t + 2 * E * df, 2 * df, D, F, stream);
+        }
         if (e == hipSuccess) e = mark(2);
-        if (e == hipSuccess) e = launch_bwd_dh(a, dy, W2, Ws2, gu, dgu, hw, dwpart, stream);
+        if (e == hipSuccess) e = launch_bwd_gate_up_bf16(a.g, x, W1, W3, Ws1, Ws3, gu, D, F, stream);
         if (e == hipSuccess) e = mark(3);
-        if (e == hipSuccess) e = launch_bwd_dx_rows(a, dgu, W1, W3, Ws1, Ws3, dxr, stream);
+        if (e == hipSuccess)
+            e = launch_bwd_dh_bf16(a.g, topk_w, dy, w2t, has_shared ? w2t + E * df : nullptr, gu, dgu,
+                                   hw, dwpart, D, F, stream);
         if (e == hipSuccess) e = mark(4);
+        if (e == hipSuccess)
+            e = launch_down_bf16(a.g, dgu, w13t, has_shared ? w13t + 2 * E * df : nullptr, dxr, D,
+                                 2 * F, stream);
+        if (e == hipSuccess) e = mark(5);
+    } else if (T > 0) {
+        if (e == hipSuccess) e = mark(2);
+        if (e == hipSuccess) e = launch_bwd_gate_up(a, x, W1, W3, Ws1, Ws3, gu, stream);
+        if (e == hipSuccess) e = mark(3);
+        if (e == hipSuccess) e = launch_bwd_dh(a, dy, W2, Ws2, gu, dgu, hw, dwpart, stream);
+        if (e == hipSuccess) e = mark(4);
+        if (e == hipSuccess) e = launch_bwd_dx_rows(a, dgu, W1, W3, Ws1, Ws3, dxr, stream);
+        if (e == hipSuccess) e = mark(5);
     } else {
-        for (int i = 2; i <= 4 && e == hipSuccess; ++i) e = mark(i);
+        for (int i = 2; i <= 5 && e == hipSuccess; ++i) e = mark(i);
     }
     // weight gradients: every element written, zero for a group without rows
     if (e == hipSuccess) e = launch_bwd_dw13(a, x, dgu, dW1, dW3, dWs1, dWs3, stream);
-    if (e == hipSuccess) e = mark(5);
-    if (e == hipSuccess) e = launch_bwd_dw2(a, hw, dy, dW2, dWs2, stream);
     if (e == hipSuccess) e = mark(6);
+    if (e == hipSuccess) e = launch_bwd_dw2(a, hw, dy, dW2, dWs2, stream);
+    if (e == hipSuccess) e = mark(7);
     if (T > 0) {
         if (e == hipSuccess) e = launch_bwd_dtopk(a, inv, dwpart, dtopk_w, stream);
         if (e == hipSuccess)
             e = launch_combine(dxr, inv, nullptr, dx, T, D, k, has_shared, bf16, stream);
     }
-    if (e == hipSuccess) e = mark(7);
+    if (e == hipSuccess) e = mark(8);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -49,4 +49,22 @@ hipError_t launch_bwd_dw2(const BwdArgs& a, const void* hw, const void* dy, floa
 hipError_t launch_bwd_dtopk(const BwdArgs& a, const int32_t* inv, const float* dwpart,
                             float* dtopk_w, hipStream_t s);
 
+// bf16 MFMA versions (gemm_bf16.hip), same results up to summation order.
+// gate_up: as launch_bwd_gate_up.  dh: as launch_bwd_dh with the transposed
+// down weights W2t [E, D, F] (Ws2t [D, F]).  The dx rows run as
+// launch_down_bf16 with F := 2F over the stacked transposes [W1^T ; W3^T]
+// ([E, 2F, D]) and A = dgu.  Needs D, F multiples of 64.
+hipError_t launch_bwd_gate_up_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
+                                   const void* Ws1, const void* Ws3, void* gu, int D, int F,
+                                   hipStream_t s);
+hipError_t launch_bwd_dh_bf16(const GroupArgs& g, const float* topk_w, const void* dy,
+                              const void* W2t, const void* Ws2t, const void* gu, void* dgu, void* hw,
+                              float* dwpart, int D, int F, hipStream_t s);
+
+// dst[b][dst_row0 + c][r] = src[b][r][c] for b < batches, r < rows, c < cols
+// (bf16, rows and cols multiples of 64); dst rows hold dst_ld elements and
+// dst batches are dst_batch_stride elements apart.
+hipError_t launch_transpose_bf16(const void* src, int64_t batches, int rows, int cols, void* dst,
+                                 int64_t dst_batch_stride, int dst_ld, int dst_row0, hipStream_t s);
+
 }  // namespace moe

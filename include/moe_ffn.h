@@ -235,6 +235,8 @@ typedef struct moe_bwd_ws_layout {
     size_t hw;          /* [R, F]  w * h per row, dtype of the call */
     size_t dxr;         /* [R, D]  each row's contribution to dx, dtype of the call */
     size_t dwpart;      /* fp32 [R, ceil(F/64)] partial sums of dy . o per 64 columns */
+    size_t w2t;         /* bf16 [E(+1), D, F] W2 (and Ws2) transposed; empty for fp32 */
+    size_t w13t;        /* bf16 [E(+1), 2F, D] W1^T stacked over W3^T (and shared); empty for fp32 */
     int32_t tile_rows;  /* row-tile height of tile_off */
     int32_t hist_blocks;/* slot blocks of the multi-block permute (0: single block) */
 } moe_bwd_ws_layout;
@@ -289,11 +291,12 @@ moe_status moe_ffn_backward(const void *x, const int32_t *topk_idx, const float 
 
 /*
  * moe_ffn_backward plus per-stage timing: events[0] before the permute,
- * events[1] after it, [2] after the gate/up recompute, [3] after the dh
- * stage, [4] after the per-row dx products, [5] after the W1/W3 gradients,
- * [6] after the W2 gradient, [7] after dtopk_w and the dx combine (eight
- * caller-created hipEvent_t on `stream`).  events == NULL behaves exactly
- * like moe_ffn_backward.
+ * [1] after it, [2] after the weight transposes (bf16; none for fp32), [3]
+ * after the gate/up recompute, [4] after the dh stage, [5] after the
+ * per-row dx products, [6] after the W1/W3 gradients, [7] after the W2
+ * gradient, [8] after dtopk_w and the dx combine (nine caller-created
+ * hipEvent_t on `stream`).  events == NULL behaves exactly like
+ * moe_ffn_backward.
  */
 moe_status moe_ffn_backward_timed(const void *x, const int32_t *topk_idx, const float *topk_w,
                                   const void *W1, const void *W3, const void *W2,
@@ -302,7 +305,7 @@ moe_status moe_ffn_backward_timed(const void *x, const int32_t *topk_idx, const 
                                   float *dWs1, float *dWs3, float *dWs2, float *dtopk_w,
                                   int64_t T, int D, int F, int E, int k, moe_dtype dtype,
                                   void *workspace, size_t ws_bytes, hipStream_t stream,
-                                  hipEvent_t events[8]);
+                                  hipEvent_t events[9]);
 
 #ifdef __cplusplus
 }
