@@ -48,9 +48,10 @@ class WsLayout(ctypes.Structure):
 
 class BwdWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("total", "err", "counts", "offsets", "tile_off", "tile_off64", "perm", "inv", "hist",
-                 "gu", "dgu", "hw", "dxr", "dwpart", "w2t", "w13t")] + \
-               [("tile_rows", ctypes.c_int32), ("hist_blocks", ctypes.c_int32)]
+                ("total", "err", "counts", "offsets", "tile_off", "chunk_off", "perm", "inv", "hist",
+                 "gu", "dgu", "hw", "dxr", "dwpart", "w2t", "w13t", "partial", "zeros")] + \
+               [("tile_rows", ctypes.c_int32), ("hist_blocks", ctypes.c_int32),
+                ("chunk_rows", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -1,0 +1,324 @@
+// gemm_bf16_wgrad.hip -- the backward's weight gradients on bf16 MFMA.
+//
+// For every group (routed expert, then the shared expert) the gradient of
+// a weight matrix is a sum over the group's rows of outer products,
+//
+//   [dW1 | dW3][grp] = sum_p x[tok(p)]^T [dg | du][p]      (M = D, N = 2F)
+//   dW2[grp]         = sum_p (w h)[p]^T dy[tok(p)]         (M = F, N = D)
+//
+// the outer products of the gate/up gradients with the inputs that "Triton
+// MoE Kernels & Memory Checkpointing" (Part A, section 8) names, and the
+// same for W2.  The contraction runs over rows, so both operands arrive as
+// [rows, features] and both are read from LDS with ds_read_b64_tr_b16.
+//
+// Work: each group's rows are cut into chunks of KC rows (the permute's
+// second tile prefix, chunk_off); a workgroup computes one 256 x 256 tile
+// of one chunk's partial sum in fp32 and stores it to a partial buffer
+// [chunks, M, N]; wgrad_reduce then adds a group's chunk partials in chunk
+// order (fixed summation order, no atomics) and writes the fp32 gradient,
+// zero for a group without rows.
+//
+// Tile engine: 256 threads = 4 wavefronts; the MFMA's A operand is 32
+// N-features (wavefront w owns N features 64 w .. 64 w + 63), its B operand
+// 32 M-features (all 256 for every wavefront), so each lane ends with four
+// consecutive N values of one M row and stores 16 bytes.  K step 32 rows,
+// a 4-stage ring of 32 KiB stages (M tile, then N tile, each 32 rows x 512
+// bytes, XOR-swizzled in 16-byte chunks as the forward's weight tiles),
+// filled with global_load_lds.  Gathered rows (x and dy read through the
+// token index) take their token from an LDS table of the chunk.  Rows past
+// the chunk's end read the M operand's last row and a zero row for the N
+// operand, so they add nothing.
+#include "mfma_common.h"
+#include "moe_bwd_internal.h"
+
+namespace moe {
+namespace {
+
+using namespace mfma;
+
+constexpr int TM = 256, TN = 256, BK = 32, NT = 256;
+constexpr int ROW = 512;                       // bytes per k row of a 256-feature tile
+constexpr int TILE_BYTES = BK * ROW;           // 16 KiB
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // M tile, then N tile
+constexpr int KC_MAX = kWgradChunkRows;
+
+struct WgradArgs {
+    GroupArgs g;              // tile_off: the chunk prefix (KC rows per chunk)
+    const uint16_t* am;       // M operand rows [., M]
+    const uint16_t* bn;       // N operand rows [., N]
+    bool gather_m, gather_n;  // operand row = the row's token (else the row itself)
+    int M, N, KC;
+    int m_tiles, n_tiles;
+    float* partial;           // [chunks, M, N]
+    const uint16_t* zeros;    // >= 16 bytes of zeros
+};
+
+__global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
+    __shared__ __attribute__((aligned(1024))) char st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st3[STAGE_BYTES];
+    __shared__ int32_t tok[KC_MAX];
+
+    const int per_chunk = a.m_tiles * a.n_tiles;
+    const int bid = xcd_remap_work(blockIdx.x, a.g.tile_off[a.g.G] * per_chunk);
+    if (bid < 0) return;
+    const int ck = bid / per_chunk;
+    const int rem = bid - ck * per_chunk;
+    const int tm = rem / a.n_tiles, tn = rem - tm * a.n_tiles;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    if (ck >= a.g.tile_off[a.g.G]) return;
+    const TileGroup tg = find_tile_group(a.g, ck, a.KC, lane);
+    const bool shared = tg.grp >= a.g.E;
+    const int64_t r0 = tg.tile_r0;
+    const int valid = tg.valid_rows;
+    if (valid <= 0) return;
+
+    for (int i = tid; i < valid; i += NT) {
+        const int64_t p = r0 + i;
+        tok[i] = shared ? (int32_t)(p - a.g.S) : a.g.perm[p] / a.g.k;
+    }
+    __syncthreads();
+
+    // ---- loads: DMA instruction j (0..3) of wavefront w fills k rows
+    // 8 w + 2 j, +1 of each tile; lane -> k row 8 w + 2 j + lane/32,
+    // physical chunk lane%32 holding logical chunk cl = phys ^ swz_tr(k),
+    // i.e. features 8 cl .. 8 cl + 7.
+    const int M = a.M, N = a.N;
+    int64_t m_col[4], n_col[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int kr = 8 * wave + 2 * j + (lane >> 5);
+        const int cl = (lane & 31) ^ swz_tr(kr);
+        int m = tm * TM + 8 * cl, n = tn * TN + 8 * cl;
+        if (m >= M) m = 0;                 // a valid address; its sums are never stored
+        if (n >= N) n = 0;
+        m_col[j] = m;
+        n_col[j] = n;
+    }
+    int tok_pf[4];                         // tokens of the next stage's rows
+    auto fetch_tok = [&](int kt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = kt * BK + 8 * wave + 2 * j + (lane >> 5);
+            tok_pf[j] = tok[min(i, valid - 1)];
+        }
+    };
+    auto issue = [&](int kt, char* st) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int kr = 8 * wave + 2 * j + (lane >> 5);
+            const int i = kt * BK + kr;
+            const int64_t own = r0 + min(i, valid - 1);
+            const int64_t rm = a.gather_m ? (int64_t)tok_pf[j] : own;
+            const int64_t rn = a.gather_n ? (int64_t)tok_pf[j] : own;
+            const char* sm = (const char*)(a.am + rm * M + m_col[j]);
+            const char* sn = i < valid ? (const char*)(a.bn + rn * N + n_col[j]) : (const char*)a.zeros;
+            load_lds16(sm, st + (8 * wave + 2 * j) * ROW);
+            load_lds16(sn, st + TILE_BYTES + (8 * wave + 2 * j) * ROW);
+        }
+    };
+
+    // ---- MFMA operand read offsets: lane = 16 G + s of k16 slice ks reads
+    // k = 16 ks + 8 (G / 2) + 4 r + s / 4 (r = 0, 1), feature base + 16 (G % 2)
+    // + 4 (s % 4) of a 32-feature block.
+    const int G = lane >> 4, sl = lane & 15;
+    auto tr_off = [&](int tile, int R, int r) {
+        const int k = 8 * (G >> 1) + 4 * r + (sl >> 2);
+        return tile + k * ROW + (((R >> 3) ^ swz_tr(k)) << 4) + 8 * ((R >> 2) & 1);
+    };
+    int n_off[2][2], m_off[8][2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+            n_off[mi][r] = tr_off(TILE_BYTES, 64 * wave + 32 * mi + 16 * (G & 1) + 4 * (sl & 3), r);
+#pragma unroll
+        for (int nj = 0; nj < 8; ++nj)
+            m_off[nj][r] = tr_off(0, 32 * nj + 16 * (G & 1) + 4 * (sl & 3), r);
+    }
+
+    f32x16_t acc[2][8];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 8; ++nj) acc[mi][nj] = f32x16_t{};
+
+    struct Frags {
+        bf16x8_t n[2][2], m[2][8];      // [k16 slice][block]
+    };
+    auto read_frags = [&](const char* st, Frags& f) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+                f.n[ks][mi] = cat_bf16(read_tr(st + n_off[mi][0] + ks * 16 * ROW),
+                                       read_tr(st + n_off[mi][1] + ks * 16 * ROW));
+#pragma unroll
+            for (int nj = 0; nj < 8; ++nj)
+                f.m[ks][nj] = cat_bf16(read_tr(st + m_off[nj][0] + ks * 16 * ROW),
+                                       read_tr(st + m_off[nj][1] + ks * 16 * ROW));
+        }
+    };
+    auto mfmas = [&](const Frags& f) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int nj = 0; nj < 8; ++nj)
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.n[ks][mi], f.m[ks][nj],
+                                                                          acc[mi][nj], 0, 0, 0);
+    };
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+
+    // ---- 4-stage ring, one stage of operands in registers ahead (as the
+    // forward engine): step s waits for stage s+1, issues stage s+3 into the
+    // buffer of stage s-1, reads stage s+1's operands and runs stage s's
+    // MFMAs.  The tokens for the next issue are read from LDS during the
+    // step and waited for at the next step's barrier.
+    const int KT = (valid + BK - 1) / BK;
+    constexpr int PER_STAGE = 8;
+    auto step = [&](Frags& fc, Frags& fn, const char* nxt, char* dma, int kl) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(PER_STAGE, 0));
+        __builtin_amdgcn_s_barrier();
+        fence();
+        issue(kl, dma);
+        fetch_tok(min(kl + 1, KT - 1));
+        read_frags(nxt, fn);
+        mfmas(fc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        fence();
+    };
+    Frags fa, fb;
+    fetch_tok(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    issue(0, st0);
+    fetch_tok(min(1, KT - 1));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    issue(min(1, KT - 1), st1);
+    fetch_tok(min(2, KT - 1));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    issue(min(2, KT - 1), st2);
+    fetch_tok(min(3, KT - 1));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * PER_STAGE, 15));   // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    fence();
+    read_frags(st0, fa);
+    fence();
+    int kt = 0;
+    for (; kt + 4 <= KT; kt += 4) {
+        step(fa, fb, st1, st3, min(kt + 3, KT - 1));
+        step(fb, fa, st2, st0, min(kt + 4, KT - 1));
+        step(fa, fb, st3, st1, min(kt + 5, KT - 1));
+        step(fb, fa, st0, st2, min(kt + 6, KT - 1));
+    }
+    if (kt < KT) {
+        step(fa, fb, st1, st3, KT - 1);
+        if (kt + 1 < KT) {
+            step(fb, fa, st2, st0, KT - 1);
+            if (kt + 2 < KT) step(fa, fb, st3, st1, KT - 1);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+
+    // ---- partial tile: element v of acc[mi][nj] on lane l is M row
+    // tm*256 + 32 nj + l%32, N columns tn*256 + 64 w + 32 mi + 8 (v/4) + 4 (l/32) + 0..3.
+    float* out = a.partial + (int64_t)ck * M * N;
+#pragma unroll
+    for (int nj = 0; nj < 8; ++nj) {
+        const int m = tm * TM + 32 * nj + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int vg = 0; vg < 4; ++vg) {
+                const int n0 = tn * TN + 64 * wave + 32 * mi + 8 * vg + 4 * (lane >> 5);
+                if (n0 >= N) continue;
+                const f32x16_t& c = acc[mi][nj];
+                *(float4*)(out + (int64_t)m * N + n0) =
+                    make_float4(c[4 * vg], c[4 * vg + 1], c[4 * vg + 2], c[4 * vg + 3]);
+            }
+    }
+}
+
+// out[grp][m][n] = sum over the group's chunks c (ascending) of
+// partial[c][m][n]; columns n < split go to out0 ([M, split] per group),
+// the rest to out1 ([M, N - split] per group); the shared group writes
+// out0_sh / out1_sh.  Four columns per thread.
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restrict__ partial,
+                                                          const int32_t* __restrict__ chunk_off,
+                                                          int E, int M, int N, int split,
+                                                          float* __restrict__ out0,
+                                                          float* __restrict__ out1,
+                                                          float* __restrict__ out0_sh,
+                                                          float* __restrict__ out1_sh) {
+    const int grp = blockIdx.y;
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= (int64_t)M * N) return;
+    const int m = (int)(e / N), n = (int)(e - (int64_t)m * N);
+    const int c0 = chunk_off[grp], c1 = chunk_off[grp + 1];
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = c0; c < c1; ++c) {
+        const float4 v = *(const float4*)(partial + ((int64_t)c * M + m) * N + n);
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const bool sh = grp == E;
+    if (n < split) {
+        float* d = sh ? out0_sh : out0 + (int64_t)grp * M * split;
+        *(float4*)(d + (int64_t)m * split + n) = s;
+    } else {
+        const int w = N - split;
+        float* d = sh ? out1_sh : out1 + (int64_t)grp * M * w;
+        *(float4*)(d + (int64_t)m * w + n - split) = s;
+    }
+}
+
+__global__ void zero_fill_kernel(uint32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+
+int64_t wgrad_chunks_upper(int64_t R, int G, int KC) { return (R + KC - 1) / KC + G; }
+
+hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t s) {
+    const int n = (int)(bytes / 4);
+    if (n <= 0) return hipSuccess;
+    zero_fill_kernel<<<(n + 255) / 256, 256, 0, s>>>((uint32_t*)p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_bf16(const GroupArgs& chunks, int KC, const void* am, bool gather_m,
+                             const void* bn, bool gather_n, int M, int N, float* partial,
+                             const void* zeros, int split, float* out0, float* out1,
+                             float* out0_sh, float* out1_sh, int64_t R, hipStream_t s) {
+    if (KC % BK || KC > KC_MAX || M % 64 || N % 64) return hipErrorInvalidValue;
+    WgradArgs a{chunks, (const uint16_t*)am, (const uint16_t*)bn, gather_m, gather_n, M, N, KC,
+                (M + TM - 1) / TM, (N + TN - 1) / TN, partial, (const uint16_t*)zeros};
+    const int64_t blocks = wgrad_chunks_upper(R, chunks.G, KC) * a.m_tiles * a.n_tiles;
+    if (R > 0) {
+        wgrad_bf16_kernel<<<grid_for_work(blocks), NT, 0, s>>>(a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid((unsigned)(((int64_t)M * N / 4 + 255) / 256), (unsigned)chunks.G);
+    wgrad_reduce_kernel<<<grid, 256, 0, s>>>(partial, chunks.tile_off, chunks.E, M, N, split, out0,
+                                             out1, out0_sh, out1_sh);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -42,7 +42,7 @@ moe_status make_bwd_layout(int64_t T, int D, int F, int E, int k, int has_shared
     L->counts = take(sizeof(int32_t) * (size_t)E);
     L->offsets = take(sizeof(int32_t) * (size_t)(E + 1));
     L->tile_off = take(sizeof(int32_t) * (size_t)(E + 2));
-    L->tile_off64 = take(sizeof(int32_t) * (size_t)(E + 2));
+    L->chunk_off = take(sizeof(int32_t) * (size_t)(E + 2));
     L->perm = take(sizeof(int32_t) * (size_t)S);
     L->inv = take(sizeof(int32_t) * (size_t)S);
     L->hist = take(sizeof(int32_t) * (size_t)(E + 1) * (size_t)nb);
@@ -56,7 +56,11 @@ moe_status make_bwd_layout(int64_t T, int D, int F, int E, int k, int has_shared
     const bool tr = dt == MOE_BF16;
     L->w2t = take(tr ? 2 * G * (size_t)D * (size_t)F : 0);
     L->w13t = take(tr ? 2 * G * 2 * (size_t)F * (size_t)D : 0);
+    const size_t MN = (size_t)D * 2 * (size_t)F;          // the larger of D x 2F and F x D
+    L->partial = take(tr ? sizeof(float) * (size_t)wgrad_chunks_upper(R, (int)G, kWgradChunkRows) * MN : 0);
+    L->zeros = take(tr ? 256 : 0);
     L->total = off;
+    L->chunk_rows = tr ? kWgradChunkRows : 0;
     L->tile_rows = dt == MOE_BF16 ? kBf16TileRows : kF32TileRows;
     L->hist_blocks = nb;
     return MOE_OK;
@@ -106,7 +110,7 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
     int32_t* counts = (int32_t*)(ws + L.counts);
     int32_t* offsets = (int32_t*)(ws + L.offsets);
     int32_t* tile_off = (int32_t*)(ws + L.tile_off);
-    int32_t* tile_off64 = (int32_t*)(ws + L.tile_off64);
+    int32_t* chunk_off = (int32_t*)(ws + L.chunk_off);
     int32_t* perm = (int32_t*)(ws + L.perm);
     int32_t* inv = (int32_t*)(ws + L.inv);
     int32_t* hist = (int32_t*)(ws + L.hist);
@@ -123,7 +127,8 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
     hipError_t e = mark(0);
     if (e == hipSuccess)
         e = launch_permute(topk_idx, S, E, L.tile_rows, has_shared ? T : 0, counts, offsets,
-                           tile_off, perm, inv, err, hist, L.hist_blocks, stream, 64, tile_off64);
+                           tile_off, perm, inv, err, hist, L.hist_blocks, stream,
+                           bf16 ? L.chunk_rows : 0, bf16 ? chunk_off : nullptr);
     if (e == hipSuccess) e = mark(1);
     const BwdArgs a{GroupArgs{offsets, tile_off, perm, S, T, E, k, E + (has_shared ? 1 : 0)},
                     topk_w, D, F, bf16};
@@ -165,10 +170,26 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
         for (int i = 2; i <= 5 && e == hipSuccess; ++i) e = mark(i);
     }
     // weight gradients: every element written, zero for a group without rows
-    if (e == hipSuccess) e = launch_bwd_dw13(a, x, dgu, dW1, dW3, dWs1, dWs3, stream);
-    if (e == hipSuccess) e = mark(6);
-    if (e == hipSuccess) e = launch_bwd_dw2(a, hw, dy, dW2, dWs2, stream);
-    if (e == hipSuccess) e = mark(7);
+    if (bf16) {
+        const GroupArgs chunks{offsets, chunk_off, perm, S, T, E, k, E + (has_shared ? 1 : 0)};
+        float* partial = (float*)(ws + L.partial);
+        void* zeros = ws + L.zeros;
+        const int64_t R = S + (has_shared ? T : 0);
+        if (e == hipSuccess) e = launch_zero_fill(zeros, 256, stream);
+        if (e == hipSuccess)
+            e = launch_wgrad_bf16(chunks, L.chunk_rows, x, true, dgu, false, D, 2 * F, partial, zeros,
+                                  F, dW1, dW3, dWs1, dWs3, R, stream);
+        if (e == hipSuccess) e = mark(6);
+        if (e == hipSuccess)
+            e = launch_wgrad_bf16(chunks, L.chunk_rows, hw, false, dy, true, F, D, partial, zeros, D,
+                                  dW2, nullptr, dWs2, nullptr, R, stream);
+        if (e == hipSuccess) e = mark(7);
+    } else {
+        if (e == hipSuccess) e = launch_bwd_dw13(a, x, dgu, dW1, dW3, dWs1, dWs3, stream);
+        if (e == hipSuccess) e = mark(6);
+        if (e == hipSuccess) e = launch_bwd_dw2(a, hw, dy, dW2, dWs2, stream);
+        if (e == hipSuccess) e = mark(7);
+    }
     if (T > 0) {
         if (e == hipSuccess) e = launch_bwd_dtopk(a, inv, dwpart, dtopk_w, stream);
         if (e == hipSuccess)

@@ -61,6 +61,24 @@ hipError_t launch_bwd_dh_bf16(const GroupArgs& g, const float* topk_w, const voi
                               const void* W2t, const void* Ws2t, const void* gu, void* dgu, void* hw,
                               float* dwpart, int D, int F, hipStream_t s);
 
+// Weight gradients on bf16 MFMA (gemm_bf16_wgrad.hip).  Each group's rows
+// are cut into chunks of KC rows (chunks.tile_off: the chunk prefix of the
+// permute, KC rows per tile); every chunk's partial sum
+//   sum over its rows p of A[p]^T B[p]   (A [., M] row p or its token's row,
+//                                         B [., N] likewise)
+// goes to partial [chunks, M, N] in fp32, and the groups' chunk partials
+// are added in chunk order: columns n < split into out0 [G', M, split],
+// the rest into out1 [G', M, N - split] (the shared group into out0_sh /
+// out1_sh).  zeros: at least 16 zero bytes.  Needs M, N multiples of 64,
+// KC a multiple of 32 no larger than kWgradChunkRows.
+constexpr int kWgradChunkRows = 4096;
+int64_t wgrad_chunks_upper(int64_t R, int G, int KC);
+hipError_t launch_wgrad_bf16(const GroupArgs& chunks, int KC, const void* am, bool gather_m,
+                             const void* bn, bool gather_n, int M, int N, float* partial,
+                             const void* zeros, int split, float* out0, float* out1,
+                             float* out0_sh, float* out1_sh, int64_t R, hipStream_t s);
+hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t s);
+
 // dst[b][dst_row0 + c][r] = src[b][r][c] for b < batches, r < rows, c < cols
 // (bf16, rows and cols multiples of 64); dst rows hold dst_ld elements and
 // dst batches are dst_batch_stride elements apart.

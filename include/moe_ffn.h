@@ -229,7 +229,9 @@ moe_status moe_ffn_get_device_error(const void *workspace, hipStream_t stream, i
  * rows as in the forward (R = T*k + T*[shared]). */
 typedef struct moe_bwd_ws_layout {
     size_t total;       /* bytes the workspace must hold */
-    size_t err, counts, offsets, tile_off, tile_off64, perm, inv, hist;   /* the permute's, as forward */
+    size_t err, counts, offsets, tile_off;   /* the permute's, as forward */
+    size_t chunk_off;   /* int32 [E+2] prefix of ceil(rows / chunk_rows), shared group last (bf16) */
+    size_t perm, inv, hist;
     size_t gu;          /* [R, 2F] recomputed gate (columns 0..F-1) and up (F..2F-1), dtype of the call */
     size_t dgu;         /* [R, 2F] gradients of the gate and up products, dtype of the call */
     size_t hw;          /* [R, F]  w * h per row, dtype of the call */
@@ -237,8 +239,11 @@ typedef struct moe_bwd_ws_layout {
     size_t dwpart;      /* fp32 [R, ceil(F/64)] partial sums of dy . o per 64 columns */
     size_t w2t;         /* bf16 [E(+1), D, F] W2 (and Ws2) transposed; empty for fp32 */
     size_t w13t;        /* bf16 [E(+1), 2F, D] W1^T stacked over W3^T (and shared); empty for fp32 */
+    size_t partial;     /* fp32 [chunks, max(D*2F, F*D)] per-chunk weight-gradient partial sums (bf16) */
+    size_t zeros;       /* 256 zero bytes (bf16) */
     int32_t tile_rows;  /* row-tile height of tile_off */
     int32_t hist_blocks;/* slot blocks of the multi-block permute (0: single block) */
+    int32_t chunk_rows; /* rows per weight-gradient chunk (bf16; 0 for fp32) */
 } moe_bwd_ws_layout;
 
 /* Fill *layout for a backward call of these sizes.  Returns MOE_OK,

@@ -61,6 +61,8 @@ def _load():
                                                  P, i64, P, ci]
         lib.moe_oracle_backward.restype = ci
         lib.moe_oracle_backward.argtypes = [P] * 10 + [i64, i64, i64, ci, ci] + [P] * 8 + [ci]
+        lib.moe_oracle_backward_groups.restype = ci
+        lib.moe_oracle_backward_groups.argtypes = [P] * 10 + [i64, i64, i64, ci, ci, P, ci] + [P] * 6 + [ci]
         lib.moe_oracle_forward_permuted.restype = i64
         lib.moe_oracle_forward_permuted.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i64, ci,
                                                     ci, P, P, P, P, P, P, P, ci]
@@ -178,6 +180,32 @@ def backward(x, topk_idx, topk_w, W1, W3, W2, shared, dy, nthreads=1) -> dict:
     if rc != 0:
         raise MemoryError("oracle allocation failed")
     return out
+
+
+def backward_weight_grads(x, topk_idx, topk_w, W1, W3, W2, shared, dy, groups, nthreads=1) -> dict:
+    """The weight gradients of the listed groups only (0..E-1 routed, E the
+    shared expert), fp64, computed as ``backward`` does: {group: (dW1, dW3,
+    dW2)}."""
+    x = _f64(x)
+    T, D = x.shape
+    E, _, F = W1.shape
+    k = topk_idx.shape[1]
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    w = _f64(topk_w)
+    W1, W3, W2 = _f64(W1), _f64(W3), _f64(W2)
+    Ws1, Ws3, Ws2 = _shared(shared)
+    dy = _f64(dy)
+    g = np.ascontiguousarray(groups, dtype=np.int32)
+    dW1, dW3, dW2 = np.zeros((E, D, F)), np.zeros((E, D, F)), np.zeros((E, F, D))
+    sh = Ws1 is not None
+    dWs = (np.zeros((D, F)), np.zeros((D, F)), np.zeros((F, D))) if sh else (None, None, None)
+    rc = _load().moe_oracle_backward_groups(
+        _ptr(x), _ptr(idx), _ptr(w), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1), _ptr(Ws3), _ptr(Ws2),
+        _ptr(dy), T, D, F, E, k, _ptr(g), g.size, _ptr(dW1), _ptr(dW3), _ptr(dW2), _ptr(dWs[0]),
+        _ptr(dWs[1]), _ptr(dWs[2]), nthreads)
+    if rc != 0:
+        raise MemoryError("oracle allocation failed")
+    return {int(e): ((dW1[e], dW3[e], dW2[e]) if e < E else dWs) for e in g}
 
 
 def backward_flops(T: int, D: int, F: int, k: int, shared: bool) -> int:

@@ -175,6 +175,7 @@ typedef struct {
     int64_t S;
     double *h_out, *Y_out;     /* sorted-row results [S(+T), F] and [S(+T), D] */
     /* backward */
+    const int32_t *groups;
     const double *dy;
     double *dx, *dW1, *dW3, *dW2, *dWs1, *dWs3, *dWs2, *dw;
     /* work split */
@@ -424,14 +425,16 @@ static void *bwd_token_worker(void *arg)
     return NULL;
 }
 
-/* Groups [lo, hi) of 0..E (E: the shared expert): the weight gradients. */
+/* Groups [lo, hi) of 0..E (E: the shared expert), or of the list J->groups
+ * when given: the weight gradients. */
 static void *bwd_expert_worker(void *arg)
 {
     job_t *J = (job_t *)arg;
     const int64_t D = J->D, F = J->F;
     double *sc = malloc(sizeof(double) * 6 * F);
     if (!sc) { J->status = -1; return NULL; }
-    for (int64_t grp = J->lo; grp < J->hi; ++grp) {
+    for (int64_t gi = J->lo; gi < J->hi; ++gi) {
+        const int64_t grp = J->groups ? J->groups[gi] : gi;
         const int shared = grp == J->E;
         const double *A1 = shared ? J->Ws1 : J->W1 + grp * D * F;
         const double *A3 = shared ? J->Ws3 : J->W3 + grp * D * F;
@@ -475,4 +478,28 @@ int moe_oracle_backward(const double *x, const int32_t *idx, const double *w,
     J.dWs1 = dWs1; J.dWs3 = dWs3; J.dWs2 = dWs2; J.dw = dw;
     if (T > 0 && run_jobs(&J, T, nthreads, bwd_token_worker)) return -1;
     return run_jobs(&J, E + (Ws1 ? 1 : 0), nthreads, bwd_expert_worker);
+}
+
+/*
+ * The weight gradients of the listed groups only (ngroups entries of
+ * 0..E, E meaning the shared expert), as moe_oracle_backward computes them;
+ * the other groups' gradients are not touched.  Returns 0, or -1 on
+ * allocation failure.
+ */
+int moe_oracle_backward_groups(const double *x, const int32_t *idx, const double *w,
+                               const double *W1, const double *W3, const double *W2,
+                               const double *Ws1, const double *Ws3, const double *Ws2,
+                               const double *dy, int64_t T, int64_t D, int64_t F, int E, int k,
+                               const int32_t *groups, int ngroups,
+                               double *dW1, double *dW3, double *dW2,
+                               double *dWs1, double *dWs3, double *dWs2, int nthreads)
+{
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.x = x; J.idx = idx; J.w = w; J.W1 = W1; J.W3 = W3; J.W2 = W2;
+    J.Ws1 = Ws1; J.Ws3 = Ws3; J.Ws2 = Ws2;
+    J.T = T; J.D = D; J.F = F; J.E = E; J.k = k;
+    J.dy = dy; J.dW1 = dW1; J.dW3 = dW3; J.dW2 = dW2;
+    J.dWs1 = dWs1; J.dWs3 = dWs3; J.dWs2 = dWs2; J.groups = groups;
+    return run_jobs(&J, ngroups, nthreads, bwd_expert_worker);
 }

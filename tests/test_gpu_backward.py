@@ -56,6 +56,7 @@ CASES = [
     (1111, 64, 128, 16, 4, False, "bf16", "zipf"),      # empty / tiny experts
     (2500, 64, 192, 8, 2, True, "bf16", "uniform"),     # multi-block permute
     (200, 192, 320, 5, 1, False, "bf16", "uniform"),    # k = 1, column tails
+    (9000, 64, 128, 4, 2, True, "bf16", "zipf"),        # groups over one 4096-row gradient chunk
 ]
 
 
@@ -109,3 +110,29 @@ def test_backward_invalid_ids_and_empty_batch():
     for n in ("dW1", "dW3", "dW2", "dWs1", "dWs3", "dWs2"):
         assert torch.count_nonzero(g0[n]).item() == 0, n
     assert g0["dx"].shape == (0, 64) and g0["dtopk_w"].shape == (0, 2)
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_backward_workload_sampled(cfg):
+    """Full-size workloads in the configuration the benchmark times: dx and
+    dtopk_w on sampled tokens (both depend only on their own token, so the
+    oracle runs on those tokens alone) and the weight gradients of the
+    smallest expert (the oracle sums all of its rows)."""
+    w = moe_inputs.WORKLOADS[cfg]
+    inp = moe_inputs.add_output_grad(moe_inputs.make_inputs(cfg))
+    say(f"backward workload {w.name}")
+    g = gpu_backward(inp)
+    rng = np.random.default_rng(200 + cfg)
+    tokens = np.unique(np.concatenate([np.arange(4), np.arange(w.T - 4, w.T),
+                                       rng.choice(w.T, 16, replace=False)]))
+    sub = {n: inp[n][tokens] for n in ("x", "topk_idx", "topk_w", "dy")}
+    ref = oracle.backward(sub["x"], sub["topk_idx"], sub["topk_w"], inp["W1"], inp["W3"], inp["W2"],
+                          host_shared(inp), sub["dy"], nthreads=NTHREADS)
+    check_close(to_f64(g["dx"])[tokens], ref["dx"], w.dtype, f"{w.name} dx")
+    check_close(to_f64(g["dtopk_w"])[tokens], ref["dw"], w.dtype, f"{w.name} dtopk_w")
+    counts = np.bincount(inp["topk_idx"].reshape(-1), minlength=w.E)
+    e = int(np.argmin(counts))
+    wg = oracle.backward_weight_grads(inp["x"], inp["topk_idx"], inp["topk_w"], inp["W1"], inp["W3"],
+                                      inp["W2"], host_shared(inp), inp["dy"], [e], nthreads=NTHREADS)[e]
+    for name, ref_e in zip(("dW1", "dW3", "dW2"), wg):
+        check_close(to_f64(g[name][e]), ref_e, w.dtype, f"{w.name} {name}[{e}] ({counts[e]} rows)")

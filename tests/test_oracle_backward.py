@@ -233,3 +233,16 @@ def test_planted_backward_mistake_is_caught(name, tmp_path, monkeypatch):
     finally:
         oracle._lib = saved
     assert caught, f"no pin failed for planted mistake {name}"
+
+
+def test_group_subset_matches_full_backward():
+    rng = np.random.default_rng(8)
+    p = _problem(rng, 30, 6, 8, 5, 2, shared=True)
+    g = _grads(p)
+    sub = oracle.backward_weight_grads(p["x"], p["idx"], p["w"], p["W1"], p["W3"], p["W2"], p["sh"],
+                                       p["dy"], [3, 5, 0])
+    for e in (0, 3):
+        for got, ref in zip(sub[e], (g["dW1"][e], g["dW3"][e], g["dW2"][e])):
+            np.testing.assert_array_equal(got, ref)
+    for got, ref in zip(sub[5], (g["dWs1"], g["dWs3"], g["dWs2"])):
+        np.testing.assert_array_equal(got, ref)
