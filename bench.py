@@ -36,6 +36,8 @@ METRIC = "MoE FFN fwd TFLOP/s + % bf16 MFMA peak, 32k tok D768 F1536 E8 top-2"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 STAGES = ("permute", "up_swiglu", "down", "combine")
+BWD_METRIC = "MoE FFN bwd TFLOP/s (gate/up recomputed), 32k tok D768 F1536 E8 top-2"
+BWD_STAGES = ("permute", "transpose", "gate_up", "dh", "dx_rows", "dw13", "dw2", "dtopk_combine")
 KERNEL_SOURCES = {             # the source each stage's kernel is built from
     "permute": "grouped_gemm_permute_amd/csrc/permute.hip",
     "up_swiglu": "grouped_gemm_permute_amd/csrc/gemm_bf16.hip",
@@ -168,6 +170,146 @@ def cpu_baseline(inp, w, target_s):
                       f"fp64 permuted oracle path, {threads} threads"}
 
 
+def bwd_stage_work(w, counts):
+    """Algorithmic FLOPs and compulsory bytes of the backward's kernels
+    (16 D F FLOP per row in total: the recomputed gate and up products 4, dh
+    2, the per-row dx 4, dW1/dW3 4, dW2 2)."""
+    b = 2 if w.dtype == "bf16" else 4
+    rows = w.T * w.k + (w.T if w.shared else 0)
+    groups = int(sum(1 for c in counts if c > 0)) + (1 if w.shared else 0)
+    D, F, T = w.D, w.F, w.T
+    wb = D * F * b
+    return {
+        "gate_up": {"flop": 4 * D * F * rows, "bytes": T * D * b + 2 * wb * groups + rows * 2 * F * b},
+        "dh": {"flop": 2 * D * F * rows,
+               "bytes": T * D * b + wb * groups + rows * 2 * F * b * 2 + rows * F * b},
+        "dx_rows": {"flop": 4 * D * F * rows, "bytes": rows * 2 * F * b + 2 * wb * groups + rows * D * b},
+        "dw13": {"flop": 4 * D * F * rows, "bytes": T * D * b + rows * 2 * F * b + 2 * D * F * 4 * groups},
+        "dw2": {"flop": 2 * D * F * rows, "bytes": rows * F * b + T * D * b + D * F * 4 * groups},
+    }
+
+
+def bwd_cpu_baseline(inp, w, target_s):
+    import numpy as np
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    sh = (inp["Ws1"], inp["Ws3"], inp["Ws2"]) if w.shared else None
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.backward(inp["x"][:n], inp["topk_idx"][:n], inp["topk_w"][:n], inp["W1"], inp["W3"],
+                        inp["W2"], sh, inp["dy"][:n], nthreads=threads)
+        return time.perf_counter() - t0
+
+    n0 = min(w.T, 8 * threads)
+    t0 = run(n0)
+    n = int(min(w.T, max(n0, target_s / max(t0, 1e-6) * n0)))
+    t = run(n)
+    flop = 16 * w.D * w.F * (n * w.k + (n if w.shared else 0))
+    return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(t, 3),
+            "sample": f"first {n} of {w.T} tokens of the same workload (same weights, routing and dy), "
+                      f"fp64 oracle backward, {threads} threads"}
+
+
+def run_backward(args):
+    """One step = one moe_ffn_backward call over the workload's inputs and a
+    seeded dy, inputs resident in HBM (rotated like the forward's)."""
+    import numpy as np
+    import torch
+
+    import grouped_gemm_permute_amd as gg
+    import moe_inputs
+
+    w = moe_inputs.WORKLOADS[args.workload]
+    log(f"backward workload {w.name}: drawing inputs")
+    inp = moe_inputs.add_output_grad(moe_inputs.make_inputs(args.workload))
+    counts = np.bincount(inp["topk_idx"].reshape(-1), minlength=w.E)
+    torch.cuda.set_device(0)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(inp[name]).cuda()
+
+    base = {n: dev(n) for n in ("x", "W1", "W3", "W2", "dy")}
+    if w.shared:
+        base.update({n: dev(n) for n in ("Ws1", "Ws3", "Ws2")})
+    base["idx"] = torch.from_numpy(inp["topk_idx"]).cuda()
+    base["w"] = torch.from_numpy(inp["topk_w"]).cuda()
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    R = max(2, math.ceil(args.rotate_bytes / set_bytes))
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(R - 1)]
+    lay = gg.backward_workspace_layout(w.T, w.D, w.F, w.E, w.k, w.shared, dt)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device="cuda")
+    out = None
+    log(f"{R} rotated input sets of {set_bytes / 1e6:.1f} MB; workspace {ws.numel() / 1e6:.1f} MB")
+
+    def step(i, events=None):
+        nonlocal out
+        s = sets[i % R]
+        sh = (s["Ws1"], s["Ws3"], s["Ws2"]) if w.shared else None
+        out = gg.backward(s["x"], s["idx"], s["w"], s["W1"], s["W3"], s["W2"], sh, s["dy"], out=out,
+                          workspace=ws, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    hip = HipEvents()
+    evs = [hip.create(9) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    stage_ms = {st: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs]))
+                for j, st in enumerate(BWD_STAGES)}
+    for e in evs:
+        hip.destroy(e)
+    log(f"timed {args.steps} backward steps: {ms_per_step:.4f} ms/step; stages {stage_ms}")
+    rows = w.T * w.k + (w.T if w.shared else 0)
+    flop = 16 * w.D * w.F * rows
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    work = bwd_stage_work(w, counts)
+    dom = max(work, key=lambda st: stage_ms[st])
+    sec = stage_ms[dom] * 1e-3
+    mfma_bound = work[dom]["flop"] / work[dom]["bytes"] > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3
+    if mfma_bound:
+        ach = work[dom]["flop"] / sec / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    else:
+        ach = work[dom]["bytes"] / sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof.update({"traffic": None, "kernel": dom, "launch_ms": round(stage_ms[dom], 5),
+                 "algorithmic": work[dom]["flop"] if mfma_bound else work[dom]["bytes"]})
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("timing the CPU oracle backward baseline")
+        cpu = bwd_cpu_baseline(inp, w, args.cpu_seconds)
+    res = {
+        "metric": BWD_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "F": w.F, "E": w.E, "k": w.k,
+                   "shared_expert": w.shared, "routing": w.routing, "pass": "backward",
+                   "rotated_sets": R},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "expert_rows": counts.tolist(),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration(nbytes, steps):
     """A plain copy of known size: reads and writes nbytes per launch."""
     import torch
@@ -196,6 +338,8 @@ def main():
                     help="target length of the CPU-oracle baseline sample; 0 skips it")
     ap.add_argument("--rotate-bytes", type=float, default=512e6,
                     help="rotate input copies until their total exceeds this many bytes")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moe_ffn_backward (dx, weight gradients, dtopk_w) instead of the forward")
     ap.add_argument("--copy-bytes", type=float, default=0,
                     help="only run a plain device-to-device copy of this many bytes --steps times "
                          "(the reference kernel for scaling HBM byte counters); prints its timing")
@@ -207,6 +351,9 @@ def main():
         print(f"bench.py measures one GPU only (this path has no multi-GPU implementation); "
               f"got --gpus {args.gpus}", file=sys.stderr)
         sys.exit(2)
+    if args.backward:
+        run_backward(args)
+        return
 
     import numpy as np
     import torch

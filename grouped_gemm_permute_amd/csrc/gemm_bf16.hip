@@ -335,34 +335,65 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
         // nt*256 + 64 w + 32 mi + 8 (v/4) + 4 (l/32) + v%4; each lane handles
         // four consecutive columns at a time.  The wavefront's 64 columns are
         // one dwpart block; the two lane halves holding a token's columns are
-        // added with one cross-lane exchange.
+        // added with one cross-lane exchange.  g, u and the routing weights
+        // are loaded a token block ahead; dg, du and w h go through LDS (two
+        // buffers of 32 rows, 16-byte chunks XOR-swizzled by the row) so that
+        // the stores write whole 512-byte row segments.
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        __syncthreads();                         // every wavefront is done with the stage buffers
         const int F = a.F;
         const int nbk = F / 64;
         const int blk = nt * 4 + wave;
-        if (nt * TF + 64 * wave >= F) return;     // F % 64 == 0: a wavefront's columns exist or not together
+        const bool cols_ok = nt * TF + 64 * wave < F;   // F % 64 == 0: all or none of a wavefront's
+        int64_t prow[8];
+        float wrow[8];
 #pragma unroll
-        for (int nj = 0; nj < 8; ++nj) {
-            const int t = 32 * nj + (lane & 31);
-            const bool ok = t < valid_rows;
-            const int64_t p = tile_r0 + min(t, valid_rows - 1);
-            const float w = shared ? 1.f : a.topk_w[a.g.perm[p]];
-            const uint16_t* gr = a.gu + p * 2 * F;
-            uint16_t* dg_row = (uint16_t*)a.out + p * 2 * F;
-            uint16_t* hw_row = a.hw + p * F;
+        for (int nj = 0; nj < 8; ++nj) prow[nj] = tile_r0 + min(32 * nj + (lane & 31), valid_rows - 1);
+        if (shared) {
+#pragma unroll
+            for (int nj = 0; nj < 8; ++nj) wrow[nj] = 1.f;
+        } else {
+            int32_t slot[8];
+#pragma unroll
+            for (int nj = 0; nj < 8; ++nj) slot[nj] = a.g.perm[prow[nj]];
+#pragma unroll
+            for (int nj = 0; nj < 8; ++nj) wrow[nj] = a.topk_w[slot[nj]];
+        }
+        const int fl = nt * TF + 64 * wave + 4 * (lane >> 5);   // + 32 mi + 8 vg
+        const int fc = cols_ok ? fl : 0;                        // a readable column for idle wavefronts
+        struct GU {
+            uint2 g[2][4], u[2][4];   // [mi][vg]
+        };
+        auto load_block = [&](int nj, GU& b) {
+            const uint16_t* gr = a.gu + prow[nj] * 2 * F;
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int vg = 0; vg < 4; ++vg) {
+                    b.g[mi][vg] = *(const uint2*)(gr + fc + 32 * mi + 8 * vg);
+                    b.u[mi][vg] = *(const uint2*)(gr + F + fc + 32 * mi + 8 * vg);
+                }
+        };
+        // staging: buffer q holds [dg 256 | du 256] (1 KiB rows) in stage
+        // buffer 2q and w h (512-byte rows) in stage buffer 2q + 1
+        auto stage_dgdu = [&](int q) -> char* { return q ? st2 : st0; };
+        auto stage_hw = [&](int q) -> char* { return q ? st3 : st1; };
+        const int r_l = lane & 31;
+        auto finish_block = [&](int nj, const GU& b) {
+            char* sdg = stage_dgdu(nj & 1) + r_l * 1024;
+            char* shw = stage_hw(nj & 1) + r_l * 512;
+            const float w = wrow[nj];
             float part = 0.f;
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi) {
                 const f32x16_t& c = acc[mi][nj];
 #pragma unroll
                 for (int vg = 0; vg < 4; ++vg) {
-                    const int f0 = nt * TF + 64 * wave + 32 * mi + 8 * vg + 4 * (lane >> 5);
-                    const uint2 graw = *(const uint2*)(gr + f0);
-                    const uint2 uraw = *(const uint2*)(gr + F + f0);
-                    const float gv[4] = {__uint_as_float(graw.x << 16), __uint_as_float(graw.x & 0xffff0000u),
-                                         __uint_as_float(graw.y << 16), __uint_as_float(graw.y & 0xffff0000u)};
-                    const float uv[4] = {__uint_as_float(uraw.x << 16), __uint_as_float(uraw.x & 0xffff0000u),
-                                         __uint_as_float(uraw.y << 16), __uint_as_float(uraw.y & 0xffff0000u)};
+                    const uint2 gq = b.g[mi][vg], uq = b.u[mi][vg];
+                    const float gv[4] = {__uint_as_float(gq.x << 16), __uint_as_float(gq.x & 0xffff0000u),
+                                         __uint_as_float(gq.y << 16), __uint_as_float(gq.y & 0xffff0000u)};
+                    const float uv[4] = {__uint_as_float(uq.x << 16), __uint_as_float(uq.x & 0xffff0000u),
+                                         __uint_as_float(uq.y << 16), __uint_as_float(uq.y & 0xffff0000u)};
                     float dg[4], du[4], hv[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -377,15 +408,59 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
                         du[i] = dh * act;
                         hv[i] = w * h;
                     }
-                    if (ok) {
-                        *(uint2*)(dg_row + f0) = make_uint2(pack_bf16(dg[0], dg[1]), pack_bf16(dg[2], dg[3]));
-                        *(uint2*)(dg_row + F + f0) = make_uint2(pack_bf16(du[0], du[1]), pack_bf16(du[2], du[3]));
-                        *(uint2*)(hw_row + f0) = make_uint2(pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3]));
-                    }
+                    const int ch = 8 * wave + 4 * mi + vg;          // 16-byte chunk of the tile row
+                    const int off = 8 * (lane >> 5);
+                    *(uint2*)(sdg + ((ch ^ r_l) << 4) + off) =
+                        make_uint2(pack_bf16(dg[0], dg[1]), pack_bf16(dg[2], dg[3]));
+                    *(uint2*)(sdg + (((32 + ch) ^ r_l) << 4) + off) =
+                        make_uint2(pack_bf16(du[0], du[1]), pack_bf16(du[2], du[3]));
+                    *(uint2*)(shw + ((ch ^ r_l) << 4) + off) =
+                        make_uint2(pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3]));
                 }
             }
             part += __shfl_xor(part, 32);
-            if (ok && lane < 32) a.dwpart[p * nbk + blk] = part;
+            if (cols_ok && 32 * nj + r_l < valid_rows && lane < 32) a.dwpart[prow[nj] * nbk + blk] = part;
+        };
+        // rows 32 nj .. 32 nj + 31 of the staged block go out as whole 16-byte
+        // chunks: [dg | du] 64 chunks per row, w h 32 chunks per row
+        auto store_block = [&](int nj) {
+            const char* sdg = stage_dgdu(nj & 1);
+            const char* shw = stage_hw(nj & 1);
+            const int c = tid & 63;
+            const int col = nt * TF + 8 * (c & 31);
+            if (col < F) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = (tid >> 6) + 4 * i;
+                    if (32 * nj + r >= valid_rows) break;
+                    const int64_t p = tile_r0 + 32 * nj + r;
+                    const u32x4_t v = *(const u32x4_t*)(sdg + r * 1024 + ((c ^ r) << 4));
+                    *(u32x4_t*)((uint16_t*)a.out + p * 2 * F + (c < 32 ? 0 : F) + col) = v;
+                }
+            }
+            const int c2 = tid & 31;
+            const int col2 = nt * TF + 8 * c2;
+            if (col2 < F) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = (tid >> 5) + 8 * i;
+                    if (32 * nj + r >= valid_rows) break;
+                    const int64_t p = tile_r0 + 32 * nj + r;
+                    const u32x4_t v = *(const u32x4_t*)(shw + r * 512 + ((c2 ^ r) << 4));
+                    *(u32x4_t*)(a.hw + p * F + col2) = v;
+                }
+            }
+        };
+        GU b0, b1;
+        load_block(0, b0);
+        load_block(1, b1);
+#pragma unroll
+        for (int nj = 0; nj < 8; ++nj) {
+            GU& cur = (nj & 1) ? b1 : b0;
+            finish_block(nj, cur);
+            if (nj + 2 < 8) load_block(nj + 2, cur);
+            __syncthreads();
+            store_block(nj);
         }
         return;
     }

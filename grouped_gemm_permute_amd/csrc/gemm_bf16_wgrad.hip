@@ -14,9 +14,10 @@
 // Work: each group's rows are cut into chunks of KC rows (the permute's
 // second tile prefix, chunk_off); a workgroup computes one 256 x 256 tile
 // of one chunk's partial sum in fp32 and stores it to a partial buffer
-// [chunks, M, N]; wgrad_reduce then adds a group's chunk partials in chunk
-// order (fixed summation order, no atomics) and writes the fp32 gradient,
-// zero for a group without rows.
+// [chunks, M, N] (a group of one chunk writes its gradient directly);
+// wgrad_reduce then adds a group's chunk partials in chunk order (fixed
+// summation order, no atomics) and writes the fp32 gradient, zero for a
+// group without rows.
 //
 // Tile engine: 256 threads = 4 wavefronts; the MFMA's A operand is 32
 // N-features (wavefront w owns N features 64 w .. 64 w + 63), its B operand
@@ -51,6 +52,8 @@ struct WgradArgs {
     int m_tiles, n_tiles;
     float* partial;           // [chunks, M, N]
     const uint16_t* zeros;    // >= 16 bytes of zeros
+    int split;                // output columns n < split -> out0, others -> out1
+    float *out0, *out1, *out0_sh, *out1_sh;
 };
 
 __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
@@ -234,9 +237,11 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
-    // ---- partial tile: element v of acc[mi][nj] on lane l is M row
+    // ---- the tile: element v of acc[mi][nj] on lane l is M row
     // tm*256 + 32 nj + l%32, N columns tn*256 + 64 w + 32 mi + 8 (v/4) + 4 (l/32) + 0..3.
-    float* out = a.partial + (int64_t)ck * M * N;
+    // A group of one chunk writes its gradient directly; otherwise the
+    // chunk's partial goes to the partial buffer for wgrad_reduce.
+    const bool single = a.g.tile_off[tg.grp + 1] - a.g.tile_off[tg.grp] == 1;
 #pragma unroll
     for (int nj = 0; nj < 8; ++nj) {
         const int m = tm * TM + 32 * nj + (lane & 31);
@@ -248,14 +253,26 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
                 const int n0 = tn * TN + 64 * wave + 32 * mi + 8 * vg + 4 * (lane >> 5);
                 if (n0 >= N) continue;
                 const f32x16_t& c = acc[mi][nj];
-                *(float4*)(out + (int64_t)m * N + n0) =
-                    make_float4(c[4 * vg], c[4 * vg + 1], c[4 * vg + 2], c[4 * vg + 3]);
+                const float4 v = make_float4(c[4 * vg], c[4 * vg + 1], c[4 * vg + 2], c[4 * vg + 3]);
+                float* dst;
+                if (!single) {
+                    dst = a.partial + ((int64_t)ck * M + m) * N + n0;
+                } else if (n0 < a.split) {
+                    dst = (shared ? a.out0_sh : a.out0 + (int64_t)tg.grp * M * a.split) +
+                          (int64_t)m * a.split + n0;
+                } else {
+                    const int w = N - a.split;
+                    dst = (shared ? a.out1_sh : a.out1 + (int64_t)tg.grp * M * w) + (int64_t)m * w +
+                          n0 - a.split;
+                }
+                *(float4*)dst = v;
             }
     }
 }
 
 // out[grp][m][n] = sum over the group's chunks c (ascending) of
-// partial[c][m][n]; columns n < split go to out0 ([M, split] per group),
+// partial[c][m][n] for groups of several chunks (zero for a group without
+// rows; one-chunk groups are written by the GEMM); columns n < split go to out0 ([M, split] per group),
 // the rest to out1 ([M, N - split] per group); the shared group writes
 // out0_sh / out1_sh.  Four columns per thread.
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restrict__ partial,
@@ -270,6 +287,7 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restri
     if (e >= (int64_t)M * N) return;
     const int m = (int)(e / N), n = (int)(e - (int64_t)m * N);
     const int c0 = chunk_off[grp], c1 = chunk_off[grp + 1];
+    if (c1 - c0 == 1) return;              // written directly by its only chunk
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c = c0; c < c1; ++c) {
         const float4 v = *(const float4*)(partial + ((int64_t)c * M + m) * N + n);
@@ -295,6 +313,15 @@ __global__ void zero_fill_kernel(uint32_t* p, int n) {
 
 int64_t wgrad_chunks_upper(int64_t R, int G, int KC) { return (R + KC - 1) / KC + G; }
 
+int wgrad_chunk_rows(int64_t R, int D, int F) {
+    // about three rounds of workgroups over the 256 CUs for the W1/W3
+    // gradient, chunks of 512 .. kWgradChunkRows rows (multiples of 256)
+    const int64_t tiles = (int64_t)((D + TM - 1) / TM) * ((2 * F + TN - 1) / TN);
+    const int64_t want = (R * tiles + 3 * 256 - 1) / (3 * 256);
+    const int64_t kc = (want + 255) / 256 * 256;
+    return (int)(kc < 512 ? 512 : kc > KC_MAX ? KC_MAX : kc);
+}
+
 hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t s) {
     const int n = (int)(bytes / 4);
     if (n <= 0) return hipSuccess;
@@ -308,7 +335,8 @@ hipError_t launch_wgrad_bf16(const GroupArgs& chunks, int KC, const void* am, bo
                              float* out0_sh, float* out1_sh, int64_t R, hipStream_t s) {
     if (KC % BK || KC > KC_MAX || M % 64 || N % 64) return hipErrorInvalidValue;
     WgradArgs a{chunks, (const uint16_t*)am, (const uint16_t*)bn, gather_m, gather_n, M, N, KC,
-                (M + TM - 1) / TM, (N + TN - 1) / TN, partial, (const uint16_t*)zeros};
+                (M + TM - 1) / TM, (N + TN - 1) / TN, partial, (const uint16_t*)zeros,
+                split, out0, out1, out0_sh, out1_sh};
     const int64_t blocks = wgrad_chunks_upper(R, chunks.G, KC) * a.m_tiles * a.n_tiles;
     if (R > 0) {
         wgrad_bf16_kernel<<<grid_for_work(blocks), NT, 0, s>>>(a);

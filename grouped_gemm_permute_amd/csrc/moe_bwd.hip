@@ -57,10 +57,11 @@ moe_status make_bwd_layout(int64_t T, int D, int F, int E, int k, int has_shared
     L->w2t = take(tr ? 2 * G * (size_t)D * (size_t)F : 0);
     L->w13t = take(tr ? 2 * G * 2 * (size_t)F * (size_t)D : 0);
     const size_t MN = (size_t)D * 2 * (size_t)F;          // the larger of D x 2F and F x D
-    L->partial = take(tr ? sizeof(float) * (size_t)wgrad_chunks_upper(R, (int)G, kWgradChunkRows) * MN : 0);
+    const int kc = wgrad_chunk_rows(R, D, F);
+    L->partial = take(tr ? sizeof(float) * (size_t)wgrad_chunks_upper(R, (int)G, kc) * MN : 0);
     L->zeros = take(tr ? 256 : 0);
     L->total = off;
-    L->chunk_rows = tr ? kWgradChunkRows : 0;
+    L->chunk_rows = tr ? kc : 0;
     L->tile_rows = dt == MOE_BF16 ? kBf16TileRows : kF32TileRows;
     L->hist_blocks = nb;
     return MOE_OK;

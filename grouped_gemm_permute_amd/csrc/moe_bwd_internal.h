@@ -66,13 +66,16 @@ hipError_t launch_bwd_dh_bf16(const GroupArgs& g, const float* topk_w, const voi
 // permute, KC rows per tile); every chunk's partial sum
 //   sum over its rows p of A[p]^T B[p]   (A [., M] row p or its token's row,
 //                                         B [., N] likewise)
-// goes to partial [chunks, M, N] in fp32, and the groups' chunk partials
-// are added in chunk order: columns n < split into out0 [G', M, split],
+// goes to partial [chunks, M, N] in fp32 (a one-chunk group writes its
+// result directly), and the groups' chunk partials are added in chunk
+// order: columns n < split into out0 [G', M, split],
 // the rest into out1 [G', M, N - split] (the shared group into out0_sh /
 // out1_sh).  zeros: at least 16 zero bytes.  Needs M, N multiples of 64,
 // KC a multiple of 32 no larger than kWgradChunkRows.
 constexpr int kWgradChunkRows = 4096;
 int64_t wgrad_chunks_upper(int64_t R, int G, int KC);
+// Chunk height for R rows (512 .. kWgradChunkRows, a multiple of 256).
+int wgrad_chunk_rows(int64_t R, int D, int F);
 hipError_t launch_wgrad_bf16(const GroupArgs& chunks, int KC, const void* am, bool gather_m,
                              const void* bn, bool gather_n, int M, int N, float* partial,
                              const void* zeros, int split, float* out0, float* out1,
