@@ -310,6 +310,89 @@ def run_backward(args):
     print(json.dumps(res), flush=True)
 
 
+def time_forward(w, variant, steps, warmup, rotate_bytes=512e6):
+    """Wall time per forward call of workload w (inputs rotated as in the
+    main bench), in ms."""
+    import numpy as np
+    import torch
+
+    import grouped_gemm_permute_amd as gg
+    import moe_inputs
+
+    inp = moe_inputs.make_inputs(w, seed=4242)
+    dt = torch.bfloat16
+
+    def dev(name):
+        return torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(dt).cuda()
+
+    base = {n: dev(n) for n in ("x", "W1", "W3", "W2")}
+    base["idx"] = torch.from_numpy(inp["topk_idx"]).cuda()
+    base["w"] = torch.from_numpy(inp["topk_w"]).cuda()
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    R = max(2, math.ceil(rotate_bytes / set_bytes))
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(R - 1)]
+    ws = gg.alloc_workspace(w.T, w.D, w.F, w.E, w.k, False, dt, variant)
+    y = torch.empty((w.T, w.D), dtype=dt, device="cuda")
+
+    def step(i):
+        s = sets[i % R]
+        gg.forward(s["x"], s["idx"], s["w"], s["W1"], s["W3"], s["W2"], None, y=y, variant=variant,
+                   workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del sets, ws, y
+    return ms
+
+
+def run_sweep(args):
+    """The fused-vs-unfused measurement variants of "Chinchilla scaling,
+    MoE, and fused Triton kernels" (verification section): sweep the
+    expansion ratio F/D at a fixed per-expert token count t, and sweep t at a
+    fixed F/D, timing the unfused (h through HBM) and fused (h on chip)
+    forwards.  Each point prints one JSON line with both times, the measured
+    speedup, the traffic model's speedup and the arithmetic intensity.
+
+    Traffic model for the SwiGLU expert in bf16 (two up matrices and one
+    down matrix, each read once per expert): unfused 4tD + 4tF + 6DF bytes,
+    fused 4tD + 6DF, so speedup ~ 1 + 4tF / (4tD + 6DF); intensity of the
+    unfused layer 6tDF / (4tD + 4tF + 6DF) FLOP/B (the page's single-matrix
+    forms are 4tD + 4tF + 4DF, 1 + tF/(tD + DF) and tFD/(tD + FD))."""
+    import moe_inputs
+
+    E, k = 16, 2
+    if args.sweep == "fd":
+        D, t = 1024, 512
+        points = [(D, F, t) for F in (512, 1024, 2048, 4096, 8192)]
+    else:
+        D, F = 1024, 4096
+        points = [(D, F, t) for t in (64, 128, 256, 512, 1024, 2048)]
+    for D, F, t in points:
+        T = t * E // k
+        w = moe_inputs.Workload(f"sweep_{args.sweep}_T{T}_D{D}_F{F}_E{E}_top{k}", T, D, F, E, k, False,
+                                "bf16", "uniform")
+        un = time_forward(w, "unfused", args.steps, args.warmup, args.rotate_bytes)
+        fu = time_forward(w, "fused", args.steps, args.warmup, args.rotate_bytes)
+        flop = 6 * D * F * T * k
+        b_un = E * (4 * t * D + 4 * t * F + 6 * D * F)
+        b_fu = E * (4 * t * D + 6 * D * F)
+        print(json.dumps({
+            "sweep": args.sweep, "T": T, "D": D, "F": F, "E": E, "k": k, "t_per_expert": t,
+            "F_over_D": F / D, "unfused_ms": round(un, 5), "fused_ms": round(fu, 5),
+            "speedup_measured": round(un / fu, 3), "speedup_model": round(b_un / b_fu, 3),
+            "unfused_tflops": round(flop / un / 1e9, 1), "fused_tflops": round(flop / fu / 1e9, 1),
+            "intensity_unfused_flop_per_byte": round(6 * t * D * F / (4 * t * D + 4 * t * F + 6 * D * F), 1),
+            "intensity_fused_flop_per_byte": round(6 * t * D * F / (4 * t * D + 6 * D * F), 1),
+            "ridge_flop_per_byte": round(PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3, 1),
+        }), flush=True)
+
+
 def copy_calibration(nbytes, steps):
     """A plain copy of known size: reads and writes nbytes per launch."""
     import torch
@@ -340,6 +423,9 @@ def main():
                     help="rotate input copies until their total exceeds this many bytes")
     ap.add_argument("--backward", action="store_true",
                     help="time moe_ffn_backward (dx, weight gradients, dtopk_w) instead of the forward")
+    ap.add_argument("--sweep", choices=("fd", "t"), default=None,
+                    help="fused vs unfused forward over F/D at fixed tokens per expert (fd) or over "
+                         "tokens per expert at fixed F/D (t); one JSON line per point")
     ap.add_argument("--copy-bytes", type=float, default=0,
                     help="only run a plain device-to-device copy of this many bytes --steps times "
                          "(the reference kernel for scaling HBM byte counters); prints its timing")
@@ -353,6 +439,9 @@ def main():
         sys.exit(2)
     if args.backward:
         run_backward(args)
+        return
+    if args.sweep:
+        run_sweep(args)
         return
 
     import numpy as np
