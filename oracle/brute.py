@@ -36,3 +36,22 @@ def moe_forward(x, topk_idx, topk_w, W1, W3, W2, shared=None):
             acc = acc + float(topk_w[t, j]) * expert(x[t], W1[e], W3[e], W2[e])
         y[t] = acc
     return y
+
+
+def router(x, gate_w, k):
+    """Top-k routing of "Chinchilla scaling, MoE, and fused Triton kernels"
+    (section "PyTorch MoE implementation"): logits = x @ gate_w, the k largest
+    logits of each token in descending order, routing weights = softmax over
+    those k logits.  fp64 throughout.  Equal logits are taken in ascending
+    expert order (the page leaves ties to torch.topk; this is the reading).
+    Returns (topk_idx int32 [T,k], topk_w float64 [T,k], logits [T,E])."""
+    x = np.asarray(x, np.float64)
+    logits = x @ np.asarray(gate_w, np.float64)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-logits[t, e], e))
+        idx[t] = order[:k]
+    sel = np.take_along_axis(logits, idx.astype(np.int64), axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return idx, z / z.sum(axis=1, keepdims=True), logits

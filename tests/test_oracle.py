@@ -261,3 +261,39 @@ def test_zipf_routing_is_skewed_toward_low_ids():
     counts = np.bincount(inp["topk_idx"].reshape(-1), minlength=8)
     assert np.all(np.diff(counts) < 0)           # p_e ~ (e+1)^-1.2 sampled without replacement
     assert counts.sum() == 2 * 8192
+
+
+# ---------------------------------------------------------------- router
+
+def test_router_matches_textbook_topk_and_softmax():
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((50, 12))
+    gw = rng.standard_normal((12, 7))
+    idx, w, logits = brute.router(x, gw, 3)
+    # logits: plain matrix product, computed independently
+    np.testing.assert_allclose(logits, np.einsum("td,de->te", x, gw), rtol=1e-13, atol=1e-13)
+    # top-k: numpy's stable argsort of the negated logits
+    ref = np.argsort(-logits, axis=1, kind="stable")[:, :3]
+    np.testing.assert_array_equal(idx, ref)
+    # weights: positive, sum to one, ordered like the logits, invariant to a shift of the logits
+    assert np.all(w > 0) and np.allclose(w.sum(1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(np.diff(w, axis=1) <= 0)
+    # a constant added to every logit (a ones column in x, a constant row in gate_w)
+    xs = np.concatenate([x, np.ones((50, 1))], axis=1)
+    gs = np.concatenate([gw, np.full((1, 7), 3.25)], axis=0)
+    idx2, w_shift, _ = brute.router(xs, gs, 3)
+    np.testing.assert_array_equal(idx2, idx)
+    np.testing.assert_allclose(w_shift, w, rtol=1e-13)
+    # closed form for k = 2: w0 = sigmoid(l0 - l1)
+    i2, w2, lg = brute.router(x, gw, 2)
+    l0 = np.take_along_axis(lg, i2[:, :1].astype(np.int64), 1)[:, 0]
+    l1 = np.take_along_axis(lg, i2[:, 1:].astype(np.int64), 1)[:, 0]
+    np.testing.assert_allclose(w2[:, 0], 1 / (1 + np.exp(-(l0 - l1))), rtol=1e-14)
+
+
+def test_router_ties_take_the_lower_expert():
+    x = np.ones((3, 2))
+    gw = np.array([[1.0, 2.0, 2.0, 0.5], [0.0, 0.0, 0.0, 0.0]])   # logits [1, 2, 2, 0.5]
+    idx, w, _ = brute.router(x, gw, 2)
+    np.testing.assert_array_equal(idx, [[1, 2]] * 3)
+    np.testing.assert_allclose(w, 0.5)
