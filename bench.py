@@ -423,6 +423,9 @@ def main():
                     help="rotate input copies until their total exceeds this many bytes")
     ap.add_argument("--backward", action="store_true",
                     help="time moe_ffn_backward (dx, weight gradients, dtopk_w) instead of the forward")
+    ap.add_argument("--routed", action="store_true",
+                    help="time moe_ffn_forward_routed: the top-k router (x @ gate_w, top-k, softmax) "
+                         "feeding the permute, then the same forward")
     ap.add_argument("--sweep", choices=("fd", "t"), default=None,
                     help="fused vs unfused forward over F/D at fixed tokens per expert (fd) or over "
                          "tokens per expert at fixed F/D (t); one JSON line per point")
@@ -453,6 +456,8 @@ def main():
     w = moe_inputs.WORKLOADS[args.workload]
     log(f"workload {w.name}: drawing inputs")
     inp = moe_inputs.make_inputs(args.workload)
+    if args.routed:
+        moe_inputs.add_router(inp)
     counts = np.bincount(inp["topk_idx"].reshape(-1), minlength=w.E)
     torch.cuda.set_device(0)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -467,6 +472,8 @@ def main():
         base.update({n: dev(n) for n in ("Ws1", "Ws3", "Ws2")})
     base["idx"] = torch.from_numpy(inp["topk_idx"]).cuda()
     base["w"] = torch.from_numpy(inp["topk_w"]).cuda()
+    if args.routed:
+        base["gate_w"] = dev("gate_w")
     set_bytes = sum(t.numel() * t.element_size() for t in base.values())
     R = max(2, math.ceil(args.rotate_bytes / set_bytes))
     sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(R - 1)]
@@ -477,6 +484,10 @@ def main():
     def step(i, events=None):
         s = sets[i % R]
         sh = (s["Ws1"], s["Ws3"], s["Ws2"]) if w.shared else None
+        if args.routed:
+            _, ridx, _ = gg.forward_routed(s["x"], s["gate_w"], s["W1"], s["W3"], s["W2"], sh, k=w.k,
+                                           y=y, variant=args.variant, workspace=ws, events=events)
+            return
         gg.forward(s["x"], s["idx"], s["w"], s["W1"], s["W3"], s["W2"], sh, y=y,
                    variant=args.variant, workspace=ws, events=events)
 
@@ -510,6 +521,10 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (host clock, no events), "
         f"{fwd_ms:.4f} ms/step with per-kernel events; stages {stage_ms}")
 
+    if args.routed:
+        # the routing comes from the router; count what it chose
+        sidx, _ = gg.router_topk(sets[0]["x"], sets[0]["gate_w"], w.k)
+        counts = np.bincount(sidx.cpu().numpy().reshape(-1), minlength=w.E)
     flop = w.flops()
     value = flop / (ms_per_step * 1e-3) / 1e12
     work = stage_work(w, counts)
@@ -543,18 +558,21 @@ def main():
     roof["algorithmic"] = work[dom]["flop"] if mfma_bound else work[dom]["bytes"]
 
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not args.routed:
         log("timing the CPU oracle baseline")
         cpu = cpu_baseline(inp, w, args.cpu_seconds)
+    if args.routed:
+        stage_ms["router_permute"] = stage_ms.pop("permute")
 
     out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC + (" (routed: router feeding the permute)" if args.routed else ""),
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "D": w.D, "F": w.F, "E": w.E, "k": w.k,
-                   "shared_expert": w.shared, "routing": w.routing, "variant": args.variant,
-                   "rotated_sets": R},
+                   "shared_expert": w.shared, "routing": "router" if args.routed else w.routing,
+                   "variant": args.variant, "rotated_sets": R},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "hbm_gbs_path": round(path_bytes(w, counts) / (ms_per_step * 1e-3) / 1e9, 1),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},

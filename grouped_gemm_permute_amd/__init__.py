@@ -7,5 +7,5 @@ deterministic unpermute/combine, and the layer's backward.  This package is the 
 torch supplies device memory and streams, nothing else.
 """
 from ._lib import (MoeError, alloc_workspace, backward, backward_workspace_layout,  # noqa: F401
-                   device_error, expert_permute, forward, lib, status_string, tile_rows,
-                   workspace_layout, workspace_size, EXPORTS, LIB_PATH)
+                   device_error, expert_permute, forward, forward_routed, lib, router_topk,
+                   status_string, tile_rows, workspace_layout, workspace_size, EXPORTS, LIB_PATH)

@@ -25,7 +25,8 @@ EXPORTS = (
     "moe_status_string", "moe_ffn_tile_rows", "moe_ffn_workspace_layout", "moe_ffn_workspace_size",
     "moe_ffn_forward", "moe_ffn_forward_timed", "moe_expert_permute", "moe_expert_permute_scratch_size",
     "moe_ffn_get_device_error", "moe_ffn_backward_workspace_layout", "moe_ffn_backward_workspace_size",
-    "moe_ffn_backward", "moe_ffn_backward_timed",
+    "moe_ffn_backward", "moe_ffn_backward_timed", "moe_router_topk", "moe_ffn_forward_routed",
+    "moe_ffn_forward_routed_timed",
 )
 
 
@@ -94,6 +95,13 @@ def lib():
         L.moe_ffn_backward.argtypes = bwd_args
         L.moe_ffn_backward_timed.restype = ci
         L.moe_ffn_backward_timed.argtypes = bwd_args + [P]
+        L.moe_router_topk.restype = ci
+        L.moe_router_topk.argtypes = [P, P, i64, ci, ci, ci, ci, P, P, P]
+        routed = [P] * 11 + [i64, ci, ci, ci, ci, ci, ci, P, sz, P]
+        L.moe_ffn_forward_routed.restype = ci
+        L.moe_ffn_forward_routed.argtypes = routed
+        L.moe_ffn_forward_routed_timed.restype = ci
+        L.moe_ffn_forward_routed_timed.argtypes = routed + [P]
         L.moe_ffn_get_device_error.restype = ci
         L.moe_ffn_get_device_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32)]
         _lib = L
@@ -274,3 +282,42 @@ def backward(x, topk_idx, topk_w, W1, W3, W2, shared, dy, out=None, workspace=No
     else:
         _check(lib().moe_ffn_backward_timed(*args, events), "moe_ffn_backward_timed")
     return o
+
+
+def router_topk(x, gate_w, k, stream=None):
+    """moe_router_topk: (topk_idx int32 [T,k], topk_w fp32 [T,k]) for x [T,D]
+    and gate_w [D,E] of x's dtype."""
+    if not (x.is_contiguous() and gate_w.is_contiguous()) or gate_w.dtype != x.dtype:
+        raise ValueError("x and gate_w must be contiguous and of one dtype")
+    T, D = x.shape
+    E = gate_w.shape[1]
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _check(lib().moe_router_topk(_ptr(x), _ptr(gate_w), T, D, E, k, _dtype_enum(x.dtype), _ptr(idx),
+                                 _ptr(w), _stream(stream)), "moe_router_topk")
+    return idx, w
+
+
+def forward_routed(x, gate_w, W1, W3, W2, shared=None, k=2, y=None, variant="unfused",
+                   workspace=None, stream=None, events=None):
+    """moe_ffn_forward_routed: returns (y, topk_idx, topk_w)."""
+    for t in (x, gate_w, W1, W3, W2, *(shared or ())):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    T, D = x.shape
+    E, _, F = W1.shape
+    Ws1, Ws3, Ws2 = shared if shared is not None else (None, None, None)
+    if y is None:
+        y = torch.empty((T, D), dtype=x.dtype, device=x.device)
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(T, D, F, E, k, shared is not None, x.dtype, variant, x.device)
+    args = (_ptr(x), _ptr(gate_w), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1), _ptr(Ws3), _ptr(Ws2),
+            _ptr(y), _ptr(idx), _ptr(w), T, D, F, E, k, _dtype_enum(x.dtype), _variant_enum(variant),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    if events is None:
+        _check(lib().moe_ffn_forward_routed(*args), "moe_ffn_forward_routed")
+    else:
+        _check(lib().moe_ffn_forward_routed_timed(*args, events), "moe_ffn_forward_routed_timed")
+    return y, idx, w

@@ -9,6 +9,7 @@
 // another path or precision.
 #include "moe_ffn.h"
 #include "moe_internal.h"
+#include "moe_router_internal.h"
 
 #include <stdint.h>
 
@@ -51,7 +52,9 @@ moe_status make_layout(int64_t T, int D, int F, int E, int k, int has_shared, mo
     L->tile_off64 = take(sizeof(int32_t) * (size_t)(E + 2));
     L->perm = take(sizeof(int32_t) * (size_t)S);
     L->inv = take(sizeof(int32_t) * (size_t)S);
-    L->hist = take(sizeof(int32_t) * (size_t)(E + 1) * (size_t)nb);
+    // multi-block permute histogram; kRouterSub columns per block when the
+    // router writes it
+    L->hist = take(sizeof(int32_t) * (size_t)(E + 1) * (size_t)nb * kRouterSub);
     L->h = take(fused ? 0 : esize * (size_t)R * (size_t)F);   // the fused variant keeps h on chip
     L->Y = take(esize * (size_t)R * (size_t)D);
     L->total = off;
@@ -126,12 +129,17 @@ moe_status moe_expert_permute(const int32_t* topk_idx, int64_t T, int k, int E, 
     return MOE_OK;
 }
 
-moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const float* topk_w,
-                                 const void* W1, const void* W3, const void* W2, const void* Ws1,
-                                 const void* Ws3, const void* Ws2, void* y, int64_t T, int D,
-                                 int F, int E, int k, moe_dtype dtype, moe_variant variant,
-                                 void* workspace, size_t ws_bytes, hipStream_t stream,
-                                 hipEvent_t* events) {
+}  // extern "C"
+
+namespace {
+
+// The forward; with gate_w the router writes topk_idx / topk_w first (and,
+// when the permute can take it, the permute's histogram).
+moe_status forward_impl(const void* x, const void* gate_w, const int32_t* topk_idx,
+                        const float* topk_w, const void* W1, const void* W3, const void* W2,
+                        const void* Ws1, const void* Ws3, const void* Ws2, void* y, int64_t T, int D,
+                        int F, int E, int k, moe_dtype dtype, moe_variant variant, void* workspace,
+                        size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
     const int nsh = (Ws1 != nullptr) + (Ws3 != nullptr) + (Ws2 != nullptr);
     if (nsh != 0 && nsh != 3) return MOE_ERR_INVALID_ARG;
     const bool has_shared = nsh == 3;
@@ -166,9 +174,26 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
         return events ? hipEventRecord(events[i], stream) : hipSuccess;
     };
     if (mark(0) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_permute(topk_idx, S, E, L.tile_rows, has_shared ? T : 0, counts, offsets, tile_off,
-                       perm, inv, err, hist, L.hist_blocks, stream, 64, tile_off64) != hipSuccess)
+    if (gate_w) {
+        const bool fine = permute_fine_ok(S, E, kRouterSub);
+        if (launch_router(x, gate_w, T, D, E, k, dtype == MOE_BF16, (int32_t*)topk_idx,
+                          (float*)topk_w, fine ? hist : nullptr, stream) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (fine) {
+            if (launch_permute_from_hist(topk_idx, S, E, L.tile_rows, has_shared ? T : 0, counts,
+                                         offsets, tile_off, perm, inv, err, hist, kRouterSub, stream,
+                                         64, tile_off64) != hipSuccess)
+                return MOE_ERR_HIP;
+        } else if (launch_permute(topk_idx, S, E, L.tile_rows, has_shared ? T : 0, counts, offsets,
+                                  tile_off, perm, inv, err, hist, L.hist_blocks, stream, 64,
+                                  tile_off64) != hipSuccess) {
+            return MOE_ERR_HIP;
+        }
+    } else if (launch_permute(topk_idx, S, E, L.tile_rows, has_shared ? T : 0, counts, offsets,
+                              tile_off, perm, inv, err, hist, L.hist_blocks, stream, 64,
+                              tile_off64) != hipSuccess) {
         return MOE_ERR_HIP;
+    }
     if (mark(1) != hipSuccess) return MOE_ERR_HIP;
 
     GroupArgs g{offsets, tile_off, perm, S, T, E, k, E + (has_shared ? 1 : 0)};
@@ -205,6 +230,63 @@ moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const f
         e = launch_combine(Y, inv, topk_w, y, T, D, k, has_shared, dtype == MOE_BF16, stream);
     if (e == hipSuccess) e = mark(4);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+bool router_shape_ok(int D, int E) {
+    return E <= kRouterMaxExperts && D % 8 == 0 && (int64_t)D * E <= kRouterMaxGateElems;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_ffn_forward_timed(const void* x, const int32_t* topk_idx, const float* topk_w,
+                                 const void* W1, const void* W3, const void* W2, const void* Ws1,
+                                 const void* Ws3, const void* Ws2, void* y, int64_t T, int D,
+                                 int F, int E, int k, moe_dtype dtype, moe_variant variant,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream,
+                                 hipEvent_t* events) {
+    return forward_impl(x, nullptr, topk_idx, topk_w, W1, W3, W2, Ws1, Ws3, Ws2, y, T, D, F, E, k,
+                        dtype, variant, workspace, ws_bytes, stream, events);
+}
+
+moe_status moe_router_topk(const void* x, const void* gate_w, int64_t T, int D, int E, int k,
+                           moe_dtype dtype, int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+    if (T < 0 || D <= 0 || E < 1 || k < 1 || k > E || (dtype != MOE_F32 && dtype != MOE_BF16))
+        return MOE_ERR_INVALID_ARG;
+    if (!router_shape_ok(D, E)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !gate_w || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(gate_w, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return launch_router(x, gate_w, T, D, E, k, dtype == MOE_BF16, topk_idx, topk_w, nullptr,
+                         stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_ffn_forward_routed_timed(const void* x, const void* gate_w, const void* W1,
+                                        const void* W3, const void* W2, const void* Ws1,
+                                        const void* Ws3, const void* Ws2, void* y,
+                                        int32_t* topk_idx, float* topk_w, int64_t T, int D, int F,
+                                        int E, int k, moe_dtype dtype, moe_variant variant,
+                                        void* workspace, size_t ws_bytes, hipStream_t stream,
+                                        hipEvent_t* events) {
+    if (T < 0 || D <= 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+    if (!router_shape_ok(D, E)) return MOE_ERR_UNSUPPORTED;
+    if (T > 0 && !gate_w) return MOE_ERR_INVALID_ARG;
+    if (gate_w && !aligned(gate_w, 4)) return MOE_ERR_INVALID_ARG;
+    return forward_impl(x, T > 0 ? gate_w : nullptr, topk_idx, topk_w, W1, W3, W2, Ws1, Ws3, Ws2, y,
+                        T, D, F, E, k, dtype, variant, workspace, ws_bytes, stream, events);
+}
+
+moe_status moe_ffn_forward_routed(const void* x, const void* gate_w, const void* W1, const void* W3,
+                                  const void* W2, const void* Ws1, const void* Ws3, const void* Ws2,
+                                  void* y, int32_t* topk_idx, float* topk_w, int64_t T, int D,
+                                  int F, int E, int k, moe_dtype dtype, moe_variant variant,
+                                  void* workspace, size_t ws_bytes, hipStream_t stream) {
+    return moe_ffn_forward_routed_timed(x, gate_w, W1, W3, W2, Ws1, Ws3, Ws2, y, topk_idx, topk_w, T,
+                                        D, F, E, k, dtype, variant, workspace, ws_bytes, stream,
+                                        nullptr);
 }
 
 moe_status moe_ffn_forward(const void* x, const int32_t* topk_idx, const float* topk_w,

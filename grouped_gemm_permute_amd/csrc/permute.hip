@@ -230,8 +230,11 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
 // of that expert in earlier blocks) and scatters its slots.  Block 0 also
 // writes counts, offsets, the tile prefixes, the error count and the -1
 // tail of perm.
+// The table may be finer than the scatter blocks: sub columns per block
+// (column c covers slots [c * kPermuteBlockSlots / sub, ...)), as the
+// router writes it.
 __global__ __launch_bounds__(kScatterThreads) void permute_scan_scatter_kernel(
-    const int32_t* __restrict__ idx, int64_t S, int E, const int32_t* __restrict__ hist,
+    const int32_t* __restrict__ idx, int64_t S, int E, const int32_t* __restrict__ hist, int sub,
     TileSpec ta, TileSpec tb, int64_t shared_rows, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
     int32_t* __restrict__ err) {
@@ -242,13 +245,14 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scan_scatter_kernel(
     for (int e = tid; e <= E; e += kScatterThreads) tot[e] = run[e] = 0;
     for (int i = tid; i < (kScatterThreads / 64) * E; i += kScatterThreads) wcnt[i] = 0;
     __syncthreads();
-    const int n = (E + 1) * nb;
+    const int ncol = nb * sub;
+    const int n = (E + 1) * ncol;
     for (int i = tid; i < n; i += kScatterThreads) {
-        const int e = i / nb, bb = i - e * nb;
+        const int e = i / ncol, bb = i - e * ncol;
         const int32_t v = hist[i];
         if (v) {
             atomicAdd(&tot[e], v);
-            if (bb < b) atomicAdd(&run[e], v);
+            if (bb < b * sub) atomicAdd(&run[e], v);
         }
     }
     __syncthreads();
@@ -287,12 +291,34 @@ hipError_t launch_permute(const int32_t* idx, int64_t S, int E, int tile_rows, i
     permute_hist_kernel<<<nblocks, kScatterThreads, 0, s>>>(idx, S, E, hist);
     if ((int64_t)(E + 1) * nblocks <= kFusedScanEntries) {
         permute_scan_scatter_kernel<<<nblocks, kScatterThreads, 0, s>>>(
-            idx, S, E, hist, ta, tb, shared_rows, counts, offsets, perm, inv, err);
+            idx, S, E, hist, 1, ta, tb, shared_rows, counts, offsets, perm, inv, err);
         return hipGetLastError();
     }
     permute_scan_kernel<<<1, kScanThreads, 0, s>>>(hist, nblocks, S, E, ta, tb, shared_rows,
                                                    counts, offsets, perm, err);
     permute_scatter_kernel<<<nblocks, kScatterThreads, 0, s>>>(idx, S, E, hist, perm, inv);
+    return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+bool permute_fine_ok(int64_t S, int E, int sub) {
+    const int nb = permute_hist_blocks(S);
+    return nb > 0 && (int64_t)(E + 1) * nb * sub <= kFusedScanEntries;
+}
+
+hipError_t launch_permute_from_hist(const int32_t* idx, int64_t S, int E, int tile_rows,
+                                    int64_t shared_rows, int32_t* counts, int32_t* offsets,
+                                    int32_t* tile_off, int32_t* perm, int32_t* inv, int32_t* err,
+                                    const int32_t* hist, int sub, hipStream_t s, int tile_rows2,
+                                    int32_t* tile_off2) {
+    const TileSpec ta{tile_rows, tile_off}, tb{tile_rows2 > 0 ? tile_rows2 : 1, tile_off2};
+    const int nb = permute_hist_blocks(S);
+    permute_scan_scatter_kernel<<<nb, kScatterThreads, 0, s>>>(idx, S, E, hist, sub, ta, tb,
+                                                               shared_rows, counts, offsets, perm,
+                                                               inv, err);
     return hipGetLastError();
 }
 

@@ -205,6 +205,58 @@ size_t moe_expert_permute_scratch_size(int64_t T, int k, int E);
 moe_status moe_ffn_get_device_error(const void *workspace, hipStream_t stream, int32_t *out);
 
 /* ------------------------------------------------------------------------
+ * Router in front of the layer.
+ *
+ * The top-k router of "Chinchilla scaling, MoE, and fused Triton kernels"
+ * (section "PyTorch MoE implementation"): logits = x gate_w, the k largest
+ * logits of each token in descending order, and routing weights equal to
+ * the softmax over those k logits.  Equal logits are taken in ascending
+ * expert order.  Arithmetic is fp32 (products of the stored values summed
+ * in fp32; fp32 softmax).
+ * ------------------------------------------------------------------------ */
+
+/*
+ *   x         [T, D]  dtype, 16-byte aligned
+ *   gate_w    [D, E]  dtype
+ *   topk_idx  [T, k]  int32 out: expert of choice j (descending logit)
+ *   topk_w    [T, k]  fp32 out: softmax over the token's k chosen logits
+ *
+ * Returns MOE_OK; MOE_ERR_INVALID_ARG (null or misaligned pointer, T < 0,
+ * D <= 0, E < 1, k < 1, k > E, unknown dtype); MOE_ERR_UNSUPPORTED (E > 64,
+ * D % 8 != 0 or D * E > 16384); MOE_ERR_HIP.  T == 0 launches nothing.
+ */
+moe_status moe_router_topk(const void *x, const void *gate_w, int64_t T, int D, int E, int k,
+                           moe_dtype dtype, int32_t *topk_idx, float *topk_w, hipStream_t stream);
+
+/*
+ * moe_ffn_forward with the router in front: routes x with gate_w [D, E]
+ * (as moe_router_topk), writes the routing to topk_idx / topk_w (caller
+ * buffers, [T, k]) and computes y from it.  When the permute runs as more
+ * than one block, the router also writes the permute's per-block expert
+ * counts, so the permute starts at its scan (no separate histogram pass and
+ * no [T, E] logits in memory).  Same workspace, variants, results and
+ * errors as moe_ffn_forward, plus the router's MOE_ERR_UNSUPPORTED shapes.
+ */
+moe_status moe_ffn_forward_routed(const void *x, const void *gate_w,
+                                  const void *W1, const void *W3, const void *W2,
+                                  const void *Ws1, const void *Ws3, const void *Ws2,
+                                  void *y, int32_t *topk_idx, float *topk_w,
+                                  int64_t T, int D, int F, int E, int k,
+                                  moe_dtype dtype, moe_variant variant,
+                                  void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* moe_ffn_forward_routed with the five stage events of
+ * moe_ffn_forward_timed (events[1] follows the router and the permute). */
+moe_status moe_ffn_forward_routed_timed(const void *x, const void *gate_w,
+                                        const void *W1, const void *W3, const void *W2,
+                                        const void *Ws1, const void *Ws3, const void *Ws2,
+                                        void *y, int32_t *topk_idx, float *topk_w,
+                                        int64_t T, int D, int F, int E, int k,
+                                        moe_dtype dtype, moe_variant variant,
+                                        void *workspace, size_t ws_bytes, hipStream_t stream,
+                                        hipEvent_t events[5]);
+
+/* ------------------------------------------------------------------------
  * Backward pass.
  *
  * The vector-Jacobian product of the layer for an incoming gradient dy:

@@ -154,6 +154,21 @@ def add_output_grad(inp: dict, seed: int | None = None) -> dict:
     return inp
 
 
+def add_router(inp: dict, seed: int | None = None) -> dict:
+    """Draw a router matrix gate_w [D, E] ~ N(0, 1/D) from its own stream
+    (seed + 104729), stored like the weights.  Adds ``gate_w`` (and
+    ``gate_w_bits`` for bf16) to ``inp``."""
+    w = inp["workload"]
+    seed = inp["seed"] + 104729 if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    g = rng.standard_normal((w.D, w.E), dtype=np.float32) / np.float32(np.sqrt(w.D))
+    vals, bits = _store(g, w.dtype)
+    inp["gate_w"] = vals
+    if bits is not None:
+        inp["gate_w_bits"] = bits
+    return inp
+
+
 def input_digest(inp: dict) -> str:
     """sha256 over the stored bytes of every input tensor, in a fixed order."""
     h = hashlib.sha256()

@@ -166,3 +166,20 @@ def _bwd(**over):
 ])
 def test_backward_rejects_bad_arguments_on_host(over, status):
     assert _bwd(**over) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(E=65, k=2), L.MOE_ERR_UNSUPPORTED),            # more experts than one wavefront routes
+    (dict(D=100), L.MOE_ERR_UNSUPPORTED),                # D % 8 != 0
+    (dict(D=1024, E=32), L.MOE_ERR_UNSUPPORTED),         # gate matrix over 16384 entries
+    (dict(k=9), L.MOE_ERR_INVALID_ARG),                  # k > E
+    (dict(x=None), L.MOE_ERR_INVALID_ARG),
+    (dict(idx=FAKE + 2), L.MOE_ERR_INVALID_ARG),
+    (dict(dt=5), L.MOE_ERR_INVALID_ARG),
+    (dict(T=0, x=None, idx=None, w=None), L.MOE_OK),
+])
+def test_router_rejects_bad_arguments_on_host(args, status):
+    a = dict(x=FAKE, g=FAKE, T=16, D=64, E=8, k=2, dt=L.MOE_BF16, idx=FAKE, w=FAKE)
+    a.update(args)
+    assert L.lib().moe_router_topk(a["x"], a["g"], a["T"], a["D"], a["E"], a["k"], a["dt"], a["idx"],
+                                   a["w"], None) == status
