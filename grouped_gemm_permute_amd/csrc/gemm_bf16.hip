@@ -99,6 +99,7 @@ struct GemmArgs {
     void* out;                // up: h [R, F]; down: Y [R, D]; gu: gu [R, 2F]; dh: dgu [R, 2F]
     int D, F;
     int n_tiles;              // column tiles
+    int col_groups;           // column-tile groups (divides n_tiles and 8)
     // dh only
     const float* topk_w;      // [S] routing weight of each slot
     const uint16_t* gu;       // [R, 2F] recomputed g and u
@@ -122,9 +123,26 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     const int N = UP ? a.F : a.D;      // output columns
     const int ldw = N;                 // weight row stride (elements)
 
-    const int bid = xcd_remap_work(blockIdx.x, a.g.tile_off[a.g.G] * a.n_tiles);
-    if (bid < 0) return;
-    const int mt = bid / a.n_tiles, nt = bid - mt * a.n_tiles;
+    // ---- this workgroup's tile.  The column tiles are split into col_groups
+    // groups of ncol; the 8 / col_groups XCDs of group c (XCD x = workgroups
+    // b with b % 8 == x, dispatched round-robin) split its m_tiles x ncol
+    // tiles (row-major) into contiguous, equal ranges.  An XCD thus keeps
+    // one weight slab of ncol column tiles in its L2 while row tiles stream
+    // through; with one group this is xcd_remap_work over all tiles.
+    int mt, nt;
+    {
+        const int m_tiles = a.g.tile_off[a.g.G];
+        const int xpg = 8 / a.col_groups, ncol = a.n_tiles / a.col_groups;
+        const int xcd = blockIdx.x & 7;
+        const int c = xcd / xpg, share = xcd - c * xpg;
+        const int items = m_tiles * ncol;
+        const int per = items / xpg, rem = items - per * xpg;
+        const int i = blockIdx.x >> 3;
+        if (i >= per + (share < rem ? 1 : 0)) return;
+        const int j = share * per + min(share, rem) + i;
+        mt = j / ncol;
+        nt = c * ncol + (j - mt * ncol);
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -533,6 +551,16 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     }
 }
 
+// Column groups for a GEMM with n_tiles column tiles over a K-row weight
+// slab: the smallest split (dividing n_tiles and 8) whose per-XCD slab
+// (n_tiles / groups column tiles of K x 256 bf16) fits in 2.5 MiB of the
+// XCD's 4 MiB L2; one group when none does.
+int column_groups(int n_tiles, int K) {
+    for (int cg = 1; cg <= 8; cg *= 2)
+        if (n_tiles % cg == 0 && (int64_t)(n_tiles / cg) * K * TF * 2 <= (int64_t)5 << 19) return cg;
+    return 1;
+}
+
 int m_tiles_upper(const GroupArgs& g) {
     const int64_t rows = g.S + (g.G > g.E ? g.T : 0);
     return (int)((rows + TT - 1) / TT) + g.G;
@@ -545,6 +573,7 @@ hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* 
                                  hipStream_t s) {
     GemmArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, h, D, F, (F + TF / 2 - 1) / (TF / 2)};
+    a.col_groups = column_groups(a.n_tiles, D);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
     grouped_gemm_bf16_kernel<M_UP><<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();
@@ -554,6 +583,7 @@ hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, c
                             void* Y, int D, int F, hipStream_t s) {
     GemmArgs a{g, (const uint16_t*)h, (const uint16_t*)W2, nullptr, (const uint16_t*)Ws2, nullptr,
                Y, D, F, (D + TF - 1) / TF};
+    a.col_groups = column_groups(a.n_tiles, F);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
     grouped_gemm_bf16_kernel<M_DOWN><<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();
@@ -564,6 +594,7 @@ hipError_t launch_bwd_gate_up_bf16(const GroupArgs& g, const void* x, const void
                                    hipStream_t s) {
     GemmArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, gu, D, F, (F + TF / 2 - 1) / (TF / 2)};
+    a.col_groups = column_groups(a.n_tiles, D);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
     grouped_gemm_bf16_kernel<M_GU><<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();
@@ -573,7 +604,8 @@ hipError_t launch_bwd_dh_bf16(const GroupArgs& g, const float* topk_w, const voi
                               const void* W2t, const void* Ws2t, const void* gu, void* dgu, void* hw,
                               float* dwpart, int D, int F, hipStream_t s) {
     GemmArgs a{g, (const uint16_t*)dy, (const uint16_t*)W2t, nullptr, (const uint16_t*)Ws2t, nullptr,
-               dgu, D, F, (F + TF - 1) / TF, topk_w, (const uint16_t*)gu, (uint16_t*)hw, dwpart};
+               dgu, D, F, (F + TF - 1) / TF, 1, topk_w, (const uint16_t*)gu, (uint16_t*)hw, dwpart};
+    a.col_groups = column_groups(a.n_tiles, D);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
     grouped_gemm_bf16_kernel<M_DH><<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();

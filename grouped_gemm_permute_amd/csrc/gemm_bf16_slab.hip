@@ -68,6 +68,7 @@ __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a)
     // objects so the compiler sees that reads of one do not alias the
     // asynchronous loads into another.
     constexpr int NS = 4 * STAGE_BYTES <= 160 * 1024 ? 4 : 3;
+    constexpr bool HALF = RB >= 7;             // operands read half a stage at a time
     __shared__ __attribute__((aligned(1024))) char st0[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
@@ -202,71 +203,147 @@ __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a)
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(WAIT_N, 0));
         __builtin_amdgcn_s_barrier();
     };
-    auto step = [&](Frags& fc, Frags& fn, const char* nxt, char* dma, int kl) {
-        wait_stage();
-        fence();
-        issue(kl, dma);
-        read_frags(nxt, fn);
-        mfmas(fc);
-        // The in-order wavefront stalls on a load or LDS read while that pipe
-        // is backed up; spread them between the MFMAs (4 RB MFMAs, RB + 4
-        // loads, 4 RB + 8 reads per step): each MFMA is followed by one load
-        // and two reads until those run out.
+    if constexpr (!HALF) {
+        auto step = [&](Frags& fc, Frags& fn, const char* nxt, char* dma, int kl) {
+            wait_stage();
+            fence();
+            issue(kl, dma);
+            read_frags(nxt, fn);
+            mfmas(fc);
+            // The in-order wavefront stalls on a load or LDS read while that pipe
+            // is backed up; spread them between the MFMAs (4 RB MFMAs, RB + 4
+            // loads, 4 RB + 8 reads per step): each MFMA is followed by one load
+            // and two reads until those run out.
 #pragma unroll
-        for (int i = 0; i < 4 * RB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read
-        }
-        fence();
-    };
-    Frags fa, fb;
-#pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-        issue(min(i, KT - 1), i == 0 ? st0 : i == 1 ? st1 : st2);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * PER_STAGE, 15));   // stage 0 landed
-    __builtin_amdgcn_s_barrier();
-    fence();
-    read_frags(st0, fa);
-    fence();
-    int kt = 0;
-    if constexpr (NS == 4) {
-        // buffers rotate with period 4, operand sets with period 2
-        for (; kt + 4 <= KT; kt += 4) {
-            step(fa, fb, st1, st3, min(kt + 3, KT - 1));
-            step(fb, fa, st2, st0, min(kt + 4, KT - 1));
-            step(fa, fb, st3, st1, min(kt + 5, KT - 1));
-            step(fb, fa, st0, st2, min(kt + 6, KT - 1));
-        }
-        if (kt < KT) {
-            step(fa, fb, st1, st3, KT - 1);
-            if (kt + 1 < KT) {
-                step(fb, fa, st2, st0, KT - 1);
-                if (kt + 2 < KT) step(fa, fb, st3, st1, KT - 1);
+            for (int i = 0; i < 4 * RB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read
             }
-        }
-    } else {
-        // buffers rotate with period 3, operand sets with period 2
-        for (; kt + 6 <= KT; kt += 6) {
-            step(fa, fb, st1, st2, min(kt + 2, KT - 1));
-            step(fb, fa, st2, st0, min(kt + 3, KT - 1));
-            step(fa, fb, st0, st1, min(kt + 4, KT - 1));
-            step(fb, fa, st1, st2, min(kt + 5, KT - 1));
-            step(fa, fb, st2, st0, min(kt + 6, KT - 1));
-            step(fb, fa, st0, st1, min(kt + 7, KT - 1));
-        }
-        if (kt < KT) {
-            step(fa, fb, st1, st2, KT - 1);
-            if (kt + 1 < KT) {
-                step(fb, fa, st2, st0, KT - 1);
-                if (kt + 2 < KT) {
-                    step(fa, fb, st0, st1, KT - 1);
-                    if (kt + 3 < KT) {
-                        step(fb, fa, st1, st2, KT - 1);
-                        if (kt + 4 < KT) step(fa, fb, st2, st0, KT - 1);
+            fence();
+        };
+        Frags fa, fb;
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+            issue(min(i, KT - 1), i == 0 ? st0 : i == 1 ? st1 : st2);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * PER_STAGE, 15));   // stage 0 landed
+        __builtin_amdgcn_s_barrier();
+        fence();
+        read_frags(st0, fa);
+        fence();
+        int kt = 0;
+        if constexpr (NS == 4) {
+            // buffers rotate with period 4, operand sets with period 2
+            for (; kt + 4 <= KT; kt += 4) {
+                step(fa, fb, st1, st3, min(kt + 3, KT - 1));
+                step(fb, fa, st2, st0, min(kt + 4, KT - 1));
+                step(fa, fb, st3, st1, min(kt + 5, KT - 1));
+                step(fb, fa, st0, st2, min(kt + 6, KT - 1));
+            }
+            if (kt < KT) {
+                step(fa, fb, st1, st3, KT - 1);
+                if (kt + 1 < KT) {
+                    step(fb, fa, st2, st0, KT - 1);
+                    if (kt + 2 < KT) step(fa, fb, st3, st1, KT - 1);
+                }
+            }
+        } else {
+            // buffers rotate with period 3, operand sets with period 2
+            for (; kt + 6 <= KT; kt += 6) {
+                step(fa, fb, st1, st2, min(kt + 2, KT - 1));
+                step(fb, fa, st2, st0, min(kt + 3, KT - 1));
+                step(fa, fb, st0, st1, min(kt + 4, KT - 1));
+                step(fb, fa, st1, st2, min(kt + 5, KT - 1));
+                step(fa, fb, st2, st0, min(kt + 6, KT - 1));
+                step(fb, fa, st0, st1, min(kt + 7, KT - 1));
+            }
+            if (kt < KT) {
+                step(fa, fb, st1, st2, KT - 1);
+                if (kt + 1 < KT) {
+                    step(fb, fa, st2, st0, KT - 1);
+                    if (kt + 2 < KT) {
+                        step(fa, fb, st0, st1, KT - 1);
+                        if (kt + 3 < KT) {
+                            step(fb, fa, st1, st2, KT - 1);
+                            if (kt + 4 < KT) step(fa, fb, st2, st0, KT - 1);
+                        }
                     }
                 }
             }
+        }
+    } else {
+        // Tall tiles (RB >= 7): the operands of a whole stage do not fit twice in
+        // registers, so a stage is consumed in two halves of 32 k: the second
+        // half of the current stage is read while the MFMAs of its first half
+        // run, and the first half of the next stage while those of its second
+        // half run.  Same stage ring, waits and barrier as above.
+        struct Half {
+            bf16x8_t w[2], x[2][RB];
+        };
+        auto read_half = [&](const char* st, int h, Half& f) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int ks = 2 * h + q;
+                f.w[q] = cat_bf16(read_tr(st + w_off[0] + ks * 16 * W_ROW), read_tr(st + w_off[1] + ks * 16 * W_ROW));
+#pragma unroll
+                for (int j = 0; j < RB; ++j) {
+                    const int row = 32 * j + xl;
+                    const int c = (2 * ks + (lane >> 5)) ^ swz8(row);
+                    f.x[q][j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + row * X_ROW + (c << 4)));
+                }
+            }
+        };
+        auto mfmas_half = [&](const Half& f) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int j = 0; j < RB; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[q], f.x[q][j], acc[j], 0, 0, 0);
+        };
+        auto step_half = [&](Half& f0, Half& f1, const char* cur, const char* nxt, char* dma, int kl) {
+            wait_stage();
+            fence();
+            issue(kl, dma);
+            read_half(cur, 1, f1);
+            mfmas_half(f0);
+            // 2 RB MFMAs, RB + 4 loads, 2 RB + 4 reads: each MFMA followed by a
+            // load and a read until those run out
+#pragma unroll
+            for (int i = 0; i < 2 * RB + 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            }
+            fence();
+            read_half(nxt, 0, f0);
+            mfmas_half(f1);
+#pragma unroll
+            for (int i = 0; i < 2 * RB + 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            fence();
+        };
+        static_assert(!HALF || NS == 3, "tall tiles use three stages");
+        Half h0, h1;
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i) issue(min(i, KT - 1), i == 0 ? st0 : st1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * PER_STAGE, 15));   // stage 0 landed
+        __builtin_amdgcn_s_barrier();
+        fence();
+        read_half(st0, 0, h0);
+        fence();
+        int kt = 0;
+        // stage s in buffer s % 3: step s reads stages s and s + 1 and loads
+        // stage s + 2 into the buffer of stage s - 1
+        for (; kt + 3 <= KT; kt += 3) {
+            step_half(h0, h1, st0, st1, st2, min(kt + 2, KT - 1));
+            step_half(h0, h1, st1, st2, st0, min(kt + 3, KT - 1));
+            step_half(h0, h1, st2, st0, st1, min(kt + 4, KT - 1));
+        }
+        if (kt < KT) {
+            step_half(h0, h1, st0, st1, st2, KT - 1);
+            if (kt + 1 < KT) step_half(h0, h1, st1, st2, st0, KT - 1);
         }
     }
     wait_vmem();
@@ -302,11 +379,22 @@ hipError_t launch_rb(const SlabArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int slab_row_blocks(int64_t rows, int groups) {
-    // a tile of 32 RB rows holds a group of 1.25x the average size
-    const int64_t avg = groups > 0 ? rows / groups : rows;
-    const int64_t rb = (avg * 5 / 4 + 31) / 32;
-    return (int)(rb < 1 ? 1 : (rb > kSlabMaxRowBlocks ? kSlabMaxRowBlocks : rb));
+int slab_row_blocks(int64_t S, int64_t shared_rows, int E, int F) {
+    // A tile of 32 rb rows holds a routed group of 1.25x the average size;
+    // taller while that still leaves more than one round of workgroups (the
+    // shared expert's rows count as a group of their own): every workgroup
+    // pays the same fixed start-up, so a second, nearly empty round would
+    // cost as much as the first.
+    const int64_t want = (E > 0 ? S / E : S) * 5 / 4;
+    const int64_t base = (want + 31) / 32;
+    const int rb0 = (int)(base < 1 ? 1 : (base > kSlabMaxRowBlocks ? kSlabMaxRowBlocks : base));
+    const int64_t cols = (F + TCOL - 1) / TCOL;
+    for (int rb = rb0; rb <= kSlabMaxRowBlocks; ++rb) {
+        const int64_t tr = 32 * rb;
+        const int64_t tiles = (int64_t)E * ((want + tr - 1) / tr) + (shared_rows + tr - 1) / tr;
+        if (tiles * cols <= kSlabRoundTiles) return rb;
+    }
+    return rb0;
 }
 
 hipError_t launch_up_swiglu_bf16_slab(const GroupArgs& g, int rb, const void* x, const void* W1,
@@ -322,6 +410,8 @@ hipError_t launch_up_swiglu_bf16_slab(const GroupArgs& g, int rb, const void* x,
         case 4: return launch_rb<4>(a, s);
         case 5: return launch_rb<5>(a, s);
         case 6: return launch_rb<6>(a, s);
+        case 7: return launch_rb<7>(a, s);
+        case 8: return launch_rb<8>(a, s);
     }
     return hipErrorInvalidValue;
 }

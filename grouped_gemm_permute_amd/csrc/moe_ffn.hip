@@ -65,7 +65,7 @@ moe_status make_layout(int64_t T, int D, int F, int E, int k, int has_shared, mo
     // GEMM runs on 64-row tiles (tile_off64).
     L->small_tiles = (!fused && dt == MOE_BF16 && R < (int64_t)kBf16TileRows * G) ? 1 : 0;
     L->tile_rows = fused ? kFusedTileRows
-                         : (dt == MOE_BF16 ? (L->small_tiles ? 32 * slab_row_blocks(R, G)
+                         : (dt == MOE_BF16 ? (L->small_tiles ? 32 * slab_row_blocks(S, has_shared ? T : 0, E, F)
                                                              : kBf16TileRows)
                                            : kF32TileRows);
     L->hist_blocks = nb;

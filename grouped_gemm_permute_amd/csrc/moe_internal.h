@@ -56,8 +56,12 @@ hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, c
 // a whole typical group (rb from slab_row_blocks), each weight slab streamed
 // once; the down GEMM on 64-row x 64-feature tiles with a 4-deep load ring.
 constexpr int kSmallTileRows = 64;
-constexpr int kSlabMaxRowBlocks = 6;
-int slab_row_blocks(int64_t rows, int groups);
+constexpr int kSlabMaxRowBlocks = 8;
+// Workgroups of one round of the slab kernel (one per compute unit).
+constexpr int kSlabRoundTiles = 256;
+// rb for S routed rows over E experts, shared_rows shared-expert rows (0:
+// none) and F output columns.
+int slab_row_blocks(int64_t S, int64_t shared_rows, int E, int F);
 hipError_t launch_up_swiglu_bf16_slab(const GroupArgs& g, int rb, const void* x, const void* W1,
                                       const void* W3, const void* Ws1, const void* Ws3, void* h,
                                       int D, int F, hipStream_t s);

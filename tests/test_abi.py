@@ -53,6 +53,11 @@ def test_workspace_layout_is_aligned_and_sized():
     # 128 rows per expert on average: up tiles of 160 rows hold a whole group
     assert small["small_tiles"] == 1 and small["tile_rows"] == 160
     assert lay["small_tiles"] == 0 and lay["tile_rows"] == 256
+    # with the shared expert's 512 rows, 160-row tiles would need 12 x 24 up
+    # workgroups (two rounds of 256): the tile grows to 256 rows (10 x 24)
+    assert L.workspace_layout(512, 768, 1536, 8, 2, True, torch.bfloat16)["tile_rows"] == 256
+    # 160 rows per expert on average: 1.25x that is 200 -> 224-row tiles
+    assert L.workspace_layout(640, 128, 256, 8, 2, True, torch.bfloat16)["tile_rows"] == 224
 
 
 def _fwd(**over):

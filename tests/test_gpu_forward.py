@@ -52,6 +52,8 @@ FULL_CASES = [
     (64, 768, 1536, 8, 2, True, "bf16", "uniform"),      # layer shape, tiny batch + shared
     (300, 128, 320, 4, 2, False, "bf16", "uniform"),     # up tiles of 192 rows, one per expert
     (1000, 64, 128, 32, 3, False, "bf16", "zipf"),       # 128-row up tiles, skewed: multi-tile groups
+    (512, 768, 1536, 8, 2, True, "bf16", "uniform"),     # 256-row up tiles (half-stage operand reads)
+    (640, 128, 256, 8, 2, True, "bf16", "zipf"),         # 224-row up tiles, multi-tile groups
 ]
 
 
