@@ -107,6 +107,9 @@ struct GemmArgs {
     float* dwpart;            // [R, F / 64] partial sums of dh' * h
 };
 
+// Target of the dh epilogue's stores for rows and columns outside the tile.
+__device__ __attribute__((aligned(16))) u32x4_t dh_trash[1];
+
 template <int MODE>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs a) {
     constexpr bool UP = MODE != M_DOWN;         // A gathered by token, K = D, N = F
@@ -373,8 +376,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
         // nt*256 + 64 w + 32 mi + 8 (v/4) + 4 (l/32) + v%4; each lane handles
         // four consecutive columns at a time.  The wavefront's 64 columns are
         // one dwpart block; the two lane halves holding a token's columns are
-        // added with one cross-lane exchange.  g, u and the routing weights
-        // are loaded a token block ahead; dg, du and w h go through LDS (two
+        // added with one cross-lane exchange.  g and u are loaded a token
+        // block ahead; dg, du and w h go through LDS (two
         // buffers of 32 rows, 16-byte chunks XOR-swizzled by the row) so that
         // the stores write whole 512-byte row segments.
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
@@ -397,19 +400,45 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
 #pragma unroll
             for (int nj = 0; nj < 8; ++nj) wrow[nj] = a.topk_w[slot[nj]];
         }
-        const int fl = nt * TF + 64 * wave + 4 * (lane >> 5);   // + 32 mi + 8 vg
-        const int fc = cols_ok ? fl : 0;                        // a readable column for idle wavefronts
+        // g, u of the lane's 4 columns nt*256 + 64 w + 32 mi + 8 vg + 4 (l/32) + 0..3
         struct GU {
             uint2 g[2][4], u[2][4];   // [mi][vg]
         };
-        auto load_block = [&](int nj, GU& b) {
-            const uint16_t* gr = a.gu + prow[nj] * 2 * F;
+        // g and u of a 32-row block are loaded as whole 128-byte row segments
+        // (instruction j: rows 8 (j%4) .. +7 of the block, g for j < 4 else u;
+        // lane: row + lane/8, 16-byte chunk lane%8 of the wavefront's 64
+        // columns), then rearranged into the accumulator layout through an
+        // 8 KiB LDS scratch of the wavefront's own (upper halves of stage
+        // buffers 1 and 3; w h is staged in the lower halves), 16-byte chunks
+        // XOR-swizzled by row / 2.
+        struct Raw {
+            u32x4_t v[8];
+        };
+        char* const gus = (wave < 2 ? st1 : st3) + 16384 + (wave & 1) * 8192;
+        const int fc0 = cols_ok ? nt * TF + 64 * wave : 0;   // the wavefront's first column (readable)
+        auto swz_gu = [](int r) { return (r >> 1) & 7; };
+        auto load_raw = [&](int nj, Raw& R) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int row = 8 * (j & 3) + (lane >> 3);
+                const int64_t p = tile_r0 + min(32 * nj + row, valid_rows - 1);
+                R.v[j] = *(const u32x4_t*)(a.gu + p * 2 * F + (j >> 2) * F + fc0 + 8 * (lane & 7));
+            }
+        };
+        auto unpack = [&](const Raw& R, GU& b) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int row = 8 * (j & 3) + (lane >> 3);
+                *(u32x4_t*)(gus + (j >> 2) * 4096 + row * 128 + (((lane & 7) ^ swz_gu(row)) << 4)) = R.v[j];
+            }
+            const int r = lane & 31, h = lane >> 5;
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                 for (int vg = 0; vg < 4; ++vg) {
-                    b.g[mi][vg] = *(const uint2*)(gr + fc + 32 * mi + 8 * vg);
-                    b.u[mi][vg] = *(const uint2*)(gr + F + fc + 32 * mi + 8 * vg);
+                    const int off = r * 128 + (((4 * mi + vg) ^ swz_gu(r)) << 4) + 8 * h;
+                    b.g[mi][vg] = *(const uint2*)(gus + off);
+                    b.u[mi][vg] = *(const uint2*)(gus + 4096 + off);
                 }
         };
         // staging: buffer q holds [dg 256 | du 256] (1 KiB rows) in stage
@@ -457,47 +486,52 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
                 }
             }
             part += __shfl_xor(part, 32);
-            if (cols_ok && 32 * nj + r_l < valid_rows && lane < 32) a.dwpart[prow[nj] * nbk + blk] = part;
+            // both lane halves hold the row's sum and store it (the same value)
+            const bool ok = cols_ok && 32 * nj + r_l < valid_rows;
+            *(ok ? a.dwpart + prow[nj] * nbk + blk : (float*)dh_trash) = part;
         };
         // rows 32 nj .. 32 nj + 31 of the staged block go out as whole 16-byte
         // chunks: [dg | du] 64 chunks per row, w h 32 chunks per row
+        // Every thread issues the same 12 stores per block whatever the
+        // tile's valid rows and columns (the others go to a 16-byte trash
+        // slot), so that the compiler can count the stores issued after a
+        // block's g/u loads and wait for those loads alone.
         auto store_block = [&](int nj) {
             const char* sdg = stage_dgdu(nj & 1);
             const char* shw = stage_hw(nj & 1);
             const int c = tid & 63;
             const int col = nt * TF + 8 * (c & 31);
-            if (col < F) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = (tid >> 6) + 4 * i;
-                    if (32 * nj + r >= valid_rows) break;
-                    const int64_t p = tile_r0 + 32 * nj + r;
-                    const u32x4_t v = *(const u32x4_t*)(sdg + r * 1024 + ((c ^ r) << 4));
-                    *(u32x4_t*)((uint16_t*)a.out + p * 2 * F + (c < 32 ? 0 : F) + col) = v;
-                }
+            for (int i = 0; i < 8; ++i) {
+                const int r = (tid >> 6) + 4 * i;
+                const bool ok = col < F && 32 * nj + r < valid_rows;
+                const int64_t p = tile_r0 + 32 * nj + r;
+                const u32x4_t v = *(const u32x4_t*)(sdg + r * 1024 + ((c ^ r) << 4));
+                *(ok ? (u32x4_t*)((uint16_t*)a.out + p * 2 * F + (c < 32 ? 0 : F) + col) : dh_trash) = v;
             }
             const int c2 = tid & 31;
             const int col2 = nt * TF + 8 * c2;
-            if (col2 < F) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = (tid >> 5) + 8 * i;
-                    if (32 * nj + r >= valid_rows) break;
-                    const int64_t p = tile_r0 + 32 * nj + r;
-                    const u32x4_t v = *(const u32x4_t*)(shw + r * 512 + ((c2 ^ r) << 4));
-                    *(u32x4_t*)(a.hw + p * F + col2) = v;
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int r = (tid >> 5) + 8 * i;
+                const bool ok = col2 < F && 32 * nj + r < valid_rows;
+                const int64_t p = tile_r0 + 32 * nj + r;
+                const u32x4_t v = *(const u32x4_t*)(shw + r * 512 + ((c2 ^ r) << 4));
+                *(ok ? (u32x4_t*)(a.hw + p * F + col2) : dh_trash) = v;
             }
         };
-        GU b0, b1;
-        load_block(0, b0);
-        load_block(1, b1);
+        Raw raw;
+        load_raw(0, raw);
 #pragma unroll
         for (int nj = 0; nj < 8; ++nj) {
-            GU& cur = (nj & 1) ? b1 : b0;
+            GU cur;
+            unpack(raw, cur);
+            if (nj + 1 < 8) load_raw(nj + 1, raw);
             finish_block(nj, cur);
-            if (nj + 2 < 8) load_block(nj + 2, cur);
-            __syncthreads();
+            // the staged block is complete in LDS; a barrier that waits on
+            // LDS only, so block nj + 1's loads stay in flight
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+            __builtin_amdgcn_s_barrier();
             store_block(nj);
         }
         return;
