@@ -47,7 +47,6 @@ struct WgradArgs {
     GroupArgs g;              // tile_off: the chunk prefix (KC rows per chunk)
     const uint16_t* am;       // M operand rows [., M]
     const uint16_t* bn;       // N operand rows [., N]
-    bool gather_m, gather_n;  // operand row = the row's token (else the row itself)
     int M, N, KC;
     int m_tiles, n_tiles;
     float* partial;           // [chunks, M, N]
@@ -56,12 +55,15 @@ struct WgradArgs {
     float *out0, *out1, *out0_sh, *out1_sh;
 };
 
+// GM / GN: the M / N operand's row p is its token's row (x, dy) rather than
+// row p itself.
+template <bool GM, bool GN>
 __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
     __shared__ __attribute__((aligned(1024))) char st0[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st3[STAGE_BYTES];
-    __shared__ int32_t tok[KC_MAX];
+    __shared__ __attribute__((aligned(16))) uint32_t tok[KC_MAX];
 
     const int per_chunk = a.m_tiles * a.n_tiles;
     const int bid = xcd_remap_work(blockIdx.x, a.g.tile_off[a.g.G] * per_chunk);
@@ -75,22 +77,48 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
     if (ck >= a.g.tile_off[a.g.G]) return;
     const TileGroup tg = find_tile_group(a.g, ck, a.KC, lane);
     const bool shared = tg.grp >= a.g.E;
-    const int64_t r0 = tg.tile_r0;
+    const uint32_t r0 = (uint32_t)tg.tile_r0;   // rows < 2^31
     const int valid = tg.valid_rows;
     if (valid <= 0) return;
+    const int KT = (valid + BK - 1) / BK;
 
-    for (int i = tid; i < valid; i += NT) {
-        const int64_t p = r0 + i;
-        tok[i] = shared ? (int32_t)(p - a.g.S) : a.g.perm[p] / a.g.k;
+    // ---- the chunk's token table, padded to KT * BK rows with the last
+    // row's token and stored in issue order: entry ((kt * 2 + h) * 4 + w) * 4
+    // + j holds row kt * BK + 8 w + 2 j + h, so a lane's four DMA rows of a
+    // K step are one 16-byte LDS read.
+    // All of a thread's index loads are issued before the first is used (one
+    // memory round trip rather than one per entry).
+    if (GM || GN) {
+        constexpr int PER = KC_MAX / NT;
+        uint32_t v[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int i = tid + q * NT;
+            const uint32_t p = r0 + (uint32_t)min(i, valid - 1);
+            v[q] = shared ? p - (uint32_t)a.g.S : (i < KT * BK ? (uint32_t)a.g.perm[p] : 0u);
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int i = tid + q * NT;
+            if (i < KT * BK) {
+                const int kt = i >> 5, kr = i & 31;
+                const int e = ((kt * 2 + (kr & 1)) * 4 + (kr >> 3)) * 4 + ((kr >> 1) & 3);
+                tok[e] = shared ? v[q] : v[q] / (uint32_t)a.g.k;
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- loads: DMA instruction j (0..3) of wavefront w fills k rows
     // 8 w + 2 j, +1 of each tile; lane -> k row 8 w + 2 j + lane/32,
     // physical chunk lane%32 holding logical chunk cl = phys ^ swz_tr(k),
-    // i.e. features 8 cl .. 8 cl + 7.
+    // i.e. features 8 cl .. 8 cl + 7.  Row addresses are the row index (32
+    // bits) times the row pitch plus a per-lane column base: one
+    // v_mad_u64_u32 per load, no divergent code on the way to the DMA.
     const int M = a.M, N = a.N;
-    int64_t m_col[4], n_col[4];
+    const uint32_t pitch_m = 2u * (uint32_t)M, pitch_n = 2u * (uint32_t)N;
+    const char* m_base[4];
+    const char* n_base[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int kr = 8 * wave + 2 * j + (lane >> 5);
@@ -98,27 +126,28 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
         int m = tm * TM + 8 * cl, n = tn * TN + 8 * cl;
         if (m >= M) m = 0;                 // a valid address; its sums are never stored
         if (n >= N) n = 0;
-        m_col[j] = m;
-        n_col[j] = n;
+        m_base[j] = (const char*)(a.am + m);
+        n_base[j] = (const char*)(a.bn + n);
     }
-    int tok_pf[4];                         // tokens of the next stage's rows
+    const uint32_t own0 = 8 * wave + (lane >> 5);   // + 2 j: the lane's rows in a K step
+    u32x4_t tok_pf = {0u, 0u, 0u, 0u};   // tokens of the next stage's rows
     auto fetch_tok = [&](int kt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = kt * BK + 8 * wave + 2 * j + (lane >> 5);
-            tok_pf[j] = tok[min(i, valid - 1)];
-        }
+        if (GM || GN)
+            tok_pf = *(const u32x4_t*)&tok[((kt * 2 + (lane >> 5)) * 4 + wave) * 4];
     };
     auto issue = [&](int kt, char* st) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int kr = 8 * wave + 2 * j + (lane >> 5);
-            const int i = kt * BK + kr;
-            const int64_t own = r0 + min(i, valid - 1);
-            const int64_t rm = a.gather_m ? (int64_t)tok_pf[j] : own;
-            const int64_t rn = a.gather_n ? (int64_t)tok_pf[j] : own;
-            const char* sm = (const char*)(a.am + rm * M + m_col[j]);
-            const char* sn = i < valid ? (const char*)(a.bn + rn * N + n_col[j]) : (const char*)a.zeros;
+            const uint32_t i = (uint32_t)(kt * BK) + own0 + 2 * j;
+            const uint32_t own = r0 + min(i, (uint32_t)valid - 1);
+            const uint32_t rm = GM ? tok_pf[j] : own;
+            const uint32_t rn = GN ? tok_pf[j] : own;
+            const char* sm = m_base[j] + (uint64_t)rm * pitch_m;
+            const char* row_n = n_base[j] + (uint64_t)rn * pitch_n;
+            // opaque to the optimiser, so the multiply is not sunk into a
+            // divergent branch (exec-mask writes end a scheduling region)
+            asm volatile("" : "+v"(row_n));
+            const char* sn = i < (uint32_t)valid ? row_n : (const char*)a.zeros;
             load_lds16(sm, st + (8 * wave + 2 * j) * ROW);
             load_lds16(sn, st + TILE_BYTES + (8 * wave + 2 * j) * ROW);
         }
@@ -182,7 +211,6 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
     // buffer of stage s-1, reads stage s+1's operands and runs stage s's
     // MFMAs.  The tokens for the next issue are read from LDS during the
     // step and waited for at the next step's barrier.
-    const int KT = (valid + BK - 1) / BK;
     constexpr int PER_STAGE = 8;
     auto step = [&](Frags& fc, Frags& fn, const char* nxt, char* dma, int kl) {
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(PER_STAGE, 0));
@@ -239,33 +267,56 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
 
     // ---- the tile: element v of acc[mi][nj] on lane l is M row
     // tm*256 + 32 nj + l%32, N columns tn*256 + 64 w + 32 mi + 8 (v/4) + 4 (l/32) + 0..3.
-    // A group of one chunk writes its gradient directly; otherwise the
-    // chunk's partial goes to the partial buffer for wgrad_reduce.
+    // It leaves through LDS in two passes of 128 M rows: block nj of the
+    // pass goes to stage buffer nj % 4 as 32 rows of 256 fp32 (16-byte
+    // chunk c of row r at physical chunk c ^ r), then each wavefront stores
+    // whole 1 KiB rows, one row per instruction.  A group of one chunk writes
+    // its gradient directly; otherwise the chunk's partial goes to the
+    // partial buffer for wgrad_reduce.
+    __syncthreads();   // every wavefront is done with the operand stages
     const bool single = a.g.tile_off[tg.grp + 1] - a.g.tile_off[tg.grp] == 1;
+    char* const stq[4] = {st0, st1, st2, st3};
+    const int n0 = tn * TN + 4 * lane;       // this lane's 4 columns in the store phase
+    const bool col_ok = n0 < N;
+    float* dst_base;
+    int64_t pitch;
+    if (!single) {
+        dst_base = a.partial + (int64_t)ck * M * N + n0;
+        pitch = N;
+    } else if (n0 < a.split) {
+        dst_base = (shared ? a.out0_sh : a.out0 + (int64_t)tg.grp * M * a.split) + n0;
+        pitch = a.split;
+    } else {
+        const int w = N - a.split;
+        dst_base = (shared ? a.out1_sh : a.out1 + (int64_t)tg.grp * M * w) + (n0 - a.split);
+        pitch = w;
+    }
+    const int rl = lane & 31;
 #pragma unroll
-    for (int nj = 0; nj < 8; ++nj) {
-        const int m = tm * TM + 32 * nj + (lane & 31);
-        if (m >= M) continue;
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass) __syncthreads();           // the previous pass's rows are read
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int q = 0; q < 4; ++q) {
+            const int nj = 4 * pass + q;
 #pragma unroll
-            for (int vg = 0; vg < 4; ++vg) {
-                const int n0 = tn * TN + 64 * wave + 32 * mi + 8 * vg + 4 * (lane >> 5);
-                if (n0 >= N) continue;
-                const f32x16_t& c = acc[mi][nj];
-                const float4 v = make_float4(c[4 * vg], c[4 * vg + 1], c[4 * vg + 2], c[4 * vg + 3]);
-                float* dst;
-                if (!single) {
-                    dst = a.partial + ((int64_t)ck * M + m) * N + n0;
-                } else if (n0 < a.split) {
-                    dst = (shared ? a.out0_sh : a.out0 + (int64_t)tg.grp * M * a.split) +
-                          (int64_t)m * a.split + n0;
-                } else {
-                    const int w = N - a.split;
-                    dst = (shared ? a.out1_sh : a.out1 + (int64_t)tg.grp * M * w) + (int64_t)m * w +
-                          n0 - a.split;
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int vg = 0; vg < 4; ++vg) {
+                    const int c = 16 * wave + 8 * mi + 2 * vg + (lane >> 5);
+                    const f32x16_t& v = acc[mi][nj];
+                    *(float4*)(stq[q] + rl * 1024 + ((c ^ rl) << 4)) =
+                        make_float4(v[4 * vg], v[4 * vg + 1], v[4 * vg + 2], v[4 * vg + 3]);
                 }
-                *(float4*)dst = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * wave + i;
+                const float4 row = *(const float4*)(stq[q] + r * 1024 + ((lane ^ r) << 4));
+                const int m = tm * TM + 32 * (4 * pass + q) + r;
+                if (col_ok && m < M) *(float4*)(dst_base + (int64_t)m * pitch) = row;
             }
     }
 }
@@ -334,12 +385,16 @@ hipError_t launch_wgrad_bf16(const GroupArgs& chunks, int KC, const void* am, bo
                              const void* zeros, int split, float* out0, float* out1,
                              float* out0_sh, float* out1_sh, int64_t R, hipStream_t s) {
     if (KC % BK || KC > KC_MAX || M % 64 || N % 64) return hipErrorInvalidValue;
-    WgradArgs a{chunks, (const uint16_t*)am, (const uint16_t*)bn, gather_m, gather_n, M, N, KC,
+    WgradArgs a{chunks, (const uint16_t*)am, (const uint16_t*)bn, M, N, KC,
                 (M + TM - 1) / TM, (N + TN - 1) / TN, partial, (const uint16_t*)zeros,
                 split, out0, out1, out0_sh, out1_sh};
     const int64_t blocks = wgrad_chunks_upper(R, chunks.G, KC) * a.m_tiles * a.n_tiles;
     if (R > 0) {
-        wgrad_bf16_kernel<<<grid_for_work(blocks), NT, 0, s>>>(a);
+        const unsigned grid = grid_for_work(blocks);
+        if (gather_m && gather_n) wgrad_bf16_kernel<true, true><<<grid, NT, 0, s>>>(a);
+        else if (gather_m) wgrad_bf16_kernel<true, false><<<grid, NT, 0, s>>>(a);
+        else if (gather_n) wgrad_bf16_kernel<false, true><<<grid, NT, 0, s>>>(a);
+        else wgrad_bf16_kernel<false, false><<<grid, NT, 0, s>>>(a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
