@@ -57,6 +57,9 @@ CASES = [
     (2500, 64, 192, 8, 2, True, "bf16", "uniform"),     # multi-block permute
     (200, 192, 320, 5, 1, False, "bf16", "uniform"),    # k = 1, column tails
     (9000, 64, 128, 4, 2, True, "bf16", "zipf"),        # groups over one 4096-row gradient chunk
+    (3000, 64, 128, 70, 2, True, "bf16", "uniform"),    # 71 groups: lookups over two 64-group blocks
+    (2000, 64, 128, 1024, 8, False, "bf16", "uniform"), # the expert limit
+    (400, 1024, 1600, 2, 1, True, "bf16", "uniform"),   # wide D and F (F = 25 * 64)
 ]
 
 

@@ -54,6 +54,13 @@ FULL_CASES = [
     (1000, 64, 128, 32, 3, False, "bf16", "zipf"),       # 128-row up tiles, skewed: multi-tile groups
     (512, 768, 1536, 8, 2, True, "bf16", "uniform"),     # 256-row up tiles (half-stage operand reads)
     (640, 128, 256, 8, 2, True, "bf16", "zipf"),         # 224-row up tiles, multi-tile groups
+    # more than 64 groups: the tile -> group lookup spans several 64-group blocks
+    (3000, 128, 192, 100, 4, True, "bf16", "zipf"),      # small-chunk kernels, many empty experts
+    (20000, 64, 128, 70, 2, True, "bf16", "uniform"),    # 256-row engine
+    (2000, 64, 128, 1024, 8, True, "bf16", "uniform"),   # the expert limit (1025 groups)
+    # wide D and F with a 64-column tail (F = 10 * 256 + 64)
+    (96, 2048, 2624, 3, 2, True, "bf16", "uniform"),     # small-chunk kernels
+    (600, 2048, 2624, 2, 1, False, "bf16", "uniform"),   # 256-row engine, 64 K steps
 ]
 
 
@@ -110,6 +117,19 @@ def test_forward_workload_sampled(cfg):
     tokens = tokens[tokens < w.T]
     ref = oracle_y(inp, tokens)
     check_close(to_f64(y)[tokens], ref, w.dtype, w.name)
+
+
+def test_forward_million_tokens_sampled():
+    """2^20 tokens (2^21 routed slots plus the shared expert's 2^20 rows):
+    the many-block permute and row offsets far past 2^16 tiles' worth of
+    rows, checked on sampled tokens (each depends only on its own row)."""
+    T = 1 << 20
+    inp = make_case(T, 64, 128, 8, 2, True, "bf16", "zipf", seed=11)
+    say(f"forward T={T} sampled")
+    y, _ = gpu_forward(inp)
+    rng = np.random.default_rng(5)
+    tokens = np.unique(np.concatenate([np.arange(8), np.arange(T - 8, T), rng.choice(T, 48, replace=False)]))
+    check_close(to_f64(y)[tokens], oracle_y(inp, tokens), "bf16", f"T={T}")
 
 
 def test_forward_intermediates_sampled_rows():
