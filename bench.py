@@ -37,7 +37,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 STAGES = ("permute", "up_swiglu", "down", "combine")
 BWD_METRIC = "MoE FFN bwd TFLOP/s (gate/up recomputed), 32k tok D768 F1536 E8 top-2"
-BWD_STAGES = ("permute", "transpose", "gate_up", "dh", "dx_rows", "dw13", "dw2", "dtopk_combine")
+BWD_STAGES = ("permute", "transpose", "gate_up", "dh", "dx_rows", "dw13", "dw2", "reduce_dtopk_combine")
 KERNEL_SOURCES = {             # the source each stage's kernel is built from
     "permute": "grouped_gemm_permute_amd/csrc/permute.hip",
     "up_swiglu": "grouped_gemm_permute_amd/csrc/gemm_bf16.hip",

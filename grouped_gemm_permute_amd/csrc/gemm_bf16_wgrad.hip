@@ -385,19 +385,23 @@ hipError_t launch_wgrad_bf16(const GroupArgs& chunks, int KC, const void* am, bo
                              const void* zeros, int split, float* out0, float* out1,
                              float* out0_sh, float* out1_sh, int64_t R, hipStream_t s) {
     if (KC % BK || KC > KC_MAX || M % 64 || N % 64) return hipErrorInvalidValue;
+    if (R <= 0) return hipSuccess;
     WgradArgs a{chunks, (const uint16_t*)am, (const uint16_t*)bn, M, N, KC,
                 (M + TM - 1) / TM, (N + TN - 1) / TN, partial, (const uint16_t*)zeros,
                 split, out0, out1, out0_sh, out1_sh};
     const int64_t blocks = wgrad_chunks_upper(R, chunks.G, KC) * a.m_tiles * a.n_tiles;
-    if (R > 0) {
-        const unsigned grid = grid_for_work(blocks);
-        if (gather_m && gather_n) wgrad_bf16_kernel<true, true><<<grid, NT, 0, s>>>(a);
-        else if (gather_m) wgrad_bf16_kernel<true, false><<<grid, NT, 0, s>>>(a);
-        else if (gather_n) wgrad_bf16_kernel<false, true><<<grid, NT, 0, s>>>(a);
-        else wgrad_bf16_kernel<false, false><<<grid, NT, 0, s>>>(a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    const unsigned grid = grid_for_work(blocks);
+    if (gather_m && gather_n) wgrad_bf16_kernel<true, true><<<grid, NT, 0, s>>>(a);
+    else if (gather_m) wgrad_bf16_kernel<true, false><<<grid, NT, 0, s>>>(a);
+    else if (gather_n) wgrad_bf16_kernel<false, true><<<grid, NT, 0, s>>>(a);
+    else wgrad_bf16_kernel<false, false><<<grid, NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_reduce(const float* partial, const GroupArgs& chunks, int M, int N, int split,
+                               float* out0, float* out1, float* out0_sh, float* out1_sh,
+                               hipStream_t s) {
+    if (M % 64 || N % 64) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(((int64_t)M * N / 4 + 255) / 256), (unsigned)chunks.G);
     wgrad_reduce_kernel<<<grid, 256, 0, s>>>(partial, chunks.tile_off, chunks.E, M, N, split, out0,
                                              out1, out0_sh, out1_sh);

@@ -56,7 +56,9 @@ moe_status make_bwd_layout(int64_t T, int D, int F, int E, int k, int has_shared
     const bool tr = dt == MOE_BF16;
     L->w2t = take(tr ? 2 * G * (size_t)D * (size_t)F : 0);
     L->w13t = take(tr ? 2 * G * 2 * (size_t)F * (size_t)D : 0);
-    const size_t MN = (size_t)D * 2 * (size_t)F;          // the larger of D x 2F and F x D
+    // dW1/dW3 partials [chunks, D, 2F], then dW2's [chunks, F, D]: both
+    // GEMMs run before either reduction
+    const size_t MN = 3 * (size_t)D * (size_t)F;
     const int kc = wgrad_chunk_rows(R, D, F);
     L->partial = take(tr ? sizeof(float) * (size_t)wgrad_chunks_upper(R, (int)G, kc) * MN : 0);
     L->zeros = take(tr ? 256 : 0);
@@ -148,6 +150,7 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
             if (e == hipSuccess)
                 e = launch_transpose_bf16(Ws3, 1, D, F, w13t + 2 * E * df, 2 * df, D, F, stream);
         }
+        if (e == hipSuccess) e = launch_zero_fill(ws + L.zeros, 256, stream);
         if (e == hipSuccess) e = mark(2);
         if (e == hipSuccess) e = launch_bwd_gate_up_bf16(a.g, x, W1, W3, Ws1, Ws3, gu, D, F, stream);
         if (e == hipSuccess) e = mark(3);
@@ -171,20 +174,26 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
         for (int i = 2; i <= 5 && e == hipSuccess; ++i) e = mark(i);
     }
     // weight gradients: every element written, zero for a group without rows
+    const GroupArgs chunks{offsets, chunk_off, perm, S, T, E, k, E + (has_shared ? 1 : 0)};
+    float* partial13 = (float*)(ws + L.partial);
+    float* partial2 = partial13 + (bf16 ? wgrad_chunks_upper(S + (has_shared ? T : 0), chunks.G,
+                                                             L.chunk_rows) * 2 * (int64_t)D * F
+                                        : 0);
     if (bf16) {
-        const GroupArgs chunks{offsets, chunk_off, perm, S, T, E, k, E + (has_shared ? 1 : 0)};
-        float* partial = (float*)(ws + L.partial);
-        void* zeros = ws + L.zeros;
+        const void* zeros = ws + L.zeros;
         const int64_t R = S + (has_shared ? T : 0);
-        if (e == hipSuccess) e = launch_zero_fill(zeros, 256, stream);
         if (e == hipSuccess)
-            e = launch_wgrad_bf16(chunks, L.chunk_rows, x, true, dgu, false, D, 2 * F, partial, zeros,
-                                  F, dW1, dW3, dWs1, dWs3, R, stream);
+            e = launch_wgrad_bf16(chunks, L.chunk_rows, x, true, dgu, false, D, 2 * F, partial13,
+                                  zeros, F, dW1, dW3, dWs1, dWs3, R, stream);
         if (e == hipSuccess) e = mark(6);
         if (e == hipSuccess)
-            e = launch_wgrad_bf16(chunks, L.chunk_rows, hw, false, dy, true, F, D, partial, zeros, D,
+            e = launch_wgrad_bf16(chunks, L.chunk_rows, hw, false, dy, true, F, D, partial2, zeros, D,
                                   dW2, nullptr, dWs2, nullptr, R, stream);
         if (e == hipSuccess) e = mark(7);
+        if (e == hipSuccess)
+            e = launch_wgrad_reduce(partial13, chunks, D, 2 * F, F, dW1, dW3, dWs1, dWs3, stream);
+        if (e == hipSuccess)
+            e = launch_wgrad_reduce(partial2, chunks, F, D, D, dW2, nullptr, dWs2, nullptr, stream);
     } else {
         if (e == hipSuccess) e = launch_bwd_dw13(a, x, dgu, dW1, dW3, dWs1, dWs3, stream);
         if (e == hipSuccess) e = mark(6);

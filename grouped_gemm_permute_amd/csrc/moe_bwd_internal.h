@@ -66,12 +66,13 @@ hipError_t launch_bwd_dh_bf16(const GroupArgs& g, const float* topk_w, const voi
 // permute, KC rows per tile); every chunk's partial sum
 //   sum over its rows p of A[p]^T B[p]   (A [., M] row p or its token's row,
 //                                         B [., N] likewise)
-// goes to partial [chunks, M, N] in fp32 (a one-chunk group writes its
-// result directly), and the groups' chunk partials are added in chunk
-// order: columns n < split into out0 [G', M, split],
-// the rest into out1 [G', M, N - split] (the shared group into out0_sh /
-// out1_sh).  zeros: at least 16 zero bytes.  Needs M, N multiples of 64,
-// KC a multiple of 32 no larger than kWgradChunkRows.
+// goes to partial [chunks, M, N] in fp32 (launch_wgrad_bf16; a one-chunk
+// group writes its result directly), and launch_wgrad_reduce adds the
+// groups' chunk partials in chunk order: columns n < split into out0
+// [G', M, split], the rest into out1 [G', M, N - split] (the shared group
+// into out0_sh / out1_sh), zero for a group without rows.  zeros: at least
+// 16 zero bytes.  Needs M, N multiples of 64, KC a multiple of 32 no larger
+// than kWgradChunkRows.
 constexpr int kWgradChunkRows = 4096;
 int64_t wgrad_chunks_upper(int64_t R, int G, int KC);
 // Chunk height for R rows (512 .. kWgradChunkRows, a multiple of 256).
@@ -80,6 +81,9 @@ hipError_t launch_wgrad_bf16(const GroupArgs& chunks, int KC, const void* am, bo
                              const void* bn, bool gather_n, int M, int N, float* partial,
                              const void* zeros, int split, float* out0, float* out1,
                              float* out0_sh, float* out1_sh, int64_t R, hipStream_t s);
+hipError_t launch_wgrad_reduce(const float* partial, const GroupArgs& chunks, int M, int N, int split,
+                               float* out0, float* out1, float* out0_sh, float* out1_sh,
+                               hipStream_t s);
 hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t s);
 
 // dst[b][dst_row0 + c][r] = src[b][r][c] for b < batches, r < rows, c < cols

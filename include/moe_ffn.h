@@ -291,7 +291,7 @@ typedef struct moe_bwd_ws_layout {
     size_t dwpart;      /* fp32 [R, ceil(F/64)] partial sums of dy . o per 64 columns */
     size_t w2t;         /* bf16 [E(+1), D, F] W2 (and Ws2) transposed; empty for fp32 */
     size_t w13t;        /* bf16 [E(+1), 2F, D] W1^T stacked over W3^T (and shared); empty for fp32 */
-    size_t partial;     /* fp32 [chunks, max(D*2F, F*D)] per-chunk weight-gradient partial sums (bf16) */
+    size_t partial;     /* fp32 [chunks, D*2F] per-chunk dW1/dW3 partial sums, then [chunks, F*D] dW2's (bf16) */
     size_t zeros;       /* 256 zero bytes (bf16) */
     int32_t tile_rows;  /* row-tile height of tile_off */
     int32_t hist_blocks;/* slot blocks of the multi-block permute (0: single block) */
@@ -350,10 +350,10 @@ moe_status moe_ffn_backward(const void *x, const int32_t *topk_idx, const float 
  * moe_ffn_backward plus per-stage timing: events[0] before the permute,
  * [1] after it, [2] after the weight transposes (bf16; none for fp32), [3]
  * after the gate/up recompute, [4] after the dh stage, [5] after the
- * per-row dx products, [6] after the W1/W3 gradients, [7] after the W2
- * gradient, [8] after dtopk_w and the dx combine (nine caller-created
- * hipEvent_t on `stream`).  events == NULL behaves exactly like
- * moe_ffn_backward.
+ * per-row dx products, [6] after the W1/W3 gradient GEMM, [7] after the W2
+ * gradient GEMM, [8] after the weight gradients' chunk reductions (bf16),
+ * dtopk_w and the dx combine (nine caller-created hipEvent_t on `stream`).
+ * events == NULL behaves exactly like moe_ffn_backward.
  */
 moe_status moe_ffn_backward_timed(const void *x, const int32_t *topk_idx, const float *topk_w,
                                   const void *W1, const void *W3, const void *W2,
