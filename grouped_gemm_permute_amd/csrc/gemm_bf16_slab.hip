@@ -75,13 +75,15 @@ __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a)
     __shared__ __attribute__((aligned(1024))) char st3[NS == 4 ? STAGE_BYTES : 16];
 
     const int K = a.D, N = a.F;
+    // the group lookup's loads go out with the tile count's (one round trip)
+    const GroupBlock gblock = load_group_block(a.g, 0, threadIdx.x & 63);
     const int total = a.g.tile_off[a.g.G];
     const int id = xcd_remap_work(blockIdx.x, total * a.n_tiles);
     if (id < 0) return;
     const int mt = id / a.n_tiles, nt = id - mt * a.n_tiles;     // m-major
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const TileGroup tg = find_tile_group(a.g, mt, TT, lane);
+    const TileGroup tg = find_tile_group(a.g, mt, TT, lane, gblock);
     const int grp = tg.grp;
     const bool shared = grp >= a.g.E;
     const int64_t tile_r0 = tg.tile_r0;

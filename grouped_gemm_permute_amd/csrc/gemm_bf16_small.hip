@@ -66,6 +66,8 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallAr
 
     const int K = UP ? a.D : a.F;
     const int N = UP ? a.F : a.D;
+    // the group lookup's loads go out with the tile count's (one round trip)
+    const GroupBlock gblock = load_group_block(a.g, 0, threadIdx.x & 63);
     const int total = a.g.tile_off[a.g.G];
     const int id = xcd_remap_work(blockIdx.x, total * a.n_tiles);
     if (id < 0) return;
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallAr
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wf = wave >> 1, wt = wave & 1;
-    const TileGroup tg = find_tile_group(a.g, mt, TT, lane);
+    const TileGroup tg = find_tile_group(a.g, mt, TT, lane, gblock);
     const int grp = tg.grp;
     const bool shared = grp >= a.g.E;
     const int64_t tile_r0 = tg.tile_r0;

@@ -100,21 +100,35 @@ struct TileGroup {
     int valid_rows;   // rows of tile mt that exist (<= tile_rows)
 };
 
+// The group table's first 64 entries (tile starts, row ranges), one group
+// per lane.  The loads need nothing but the table, so a kernel can issue them
+// at entry, beside the read that decides its tile.
+struct GroupBlock {
+    int to, o0, o1;
+};
+
+__device__ __forceinline__ GroupBlock load_group_block(const GroupArgs& ga, int base, int lane) {
+    const int g = base + lane;
+    const bool in = g < ga.G;
+    GroupBlock b;
+    b.to = in ? ga.tile_off[g] : 0x7fffffff;
+    b.o0 = (in && g < ga.E) ? ga.offsets[g] : 0;
+    b.o1 = (in && g < ga.E) ? ga.offsets[g + 1] : 0;
+    return b;
+}
+
+// first: load_group_block(ga, 0, lane); later 64-group blocks are loaded here.
 __device__ __forceinline__ TileGroup find_tile_group(const GroupArgs& ga, int mt, int tile_rows,
-                                                     int lane) {
+                                                     int lane, const GroupBlock& first) {
     int grp = 0, tile0 = 0, o0v = 0, o1v = 0;
     for (int base = 0; base < ga.G; base += 64) {
-        const int g = base + lane;
-        const bool in = g < ga.G;
-        const int to = in ? ga.tile_off[g] : 0x7fffffff;
-        const int o0 = (in && g < ga.E) ? ga.offsets[g] : 0;
-        const int o1 = (in && g < ga.E) ? ga.offsets[g + 1] : 0;
-        const int n = __popcll(__ballot(to <= mt));
+        const GroupBlock b = base == 0 ? first : load_group_block(ga, base, lane);
+        const int n = __popcll(__ballot(b.to <= mt));
         if (n == 0) break;                  // owner is the last group of the previous block
         grp = base + n - 1;
-        tile0 = __builtin_amdgcn_readlane(to, n - 1);
-        o0v = __builtin_amdgcn_readlane(o0, n - 1);
-        o1v = __builtin_amdgcn_readlane(o1, n - 1);
+        tile0 = __builtin_amdgcn_readlane(b.to, n - 1);
+        o0v = __builtin_amdgcn_readlane(b.o0, n - 1);
+        o1v = __builtin_amdgcn_readlane(b.o1, n - 1);
         if (n < 64) break;
     }
     TileGroup t;
@@ -125,6 +139,11 @@ __device__ __forceinline__ TileGroup find_tile_group(const GroupArgs& ga, int mt
     t.tile_r0 = t.row0 + (int64_t)(mt - tile0) * tile_rows;
     t.valid_rows = (int)min((int64_t)tile_rows, t.row0 + t.rows - t.tile_r0);
     return t;
+}
+
+__device__ __forceinline__ TileGroup find_tile_group(const GroupArgs& ga, int mt, int tile_rows,
+                                                     int lane) {
+    return find_tile_group(ga, mt, tile_rows, lane, load_group_block(ga, 0, lane));
 }
 
 }  // namespace mfma
