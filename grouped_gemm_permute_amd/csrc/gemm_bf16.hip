@@ -31,16 +31,20 @@
 //  The backward's dx rows are the down mode run with K = 2F over the
 //  transposed, stacked [W1^T ; W3^T] and A = dgu.
 //
-// Tile engine (256 threads = 4 wavefronts, one per SIMD):
+// Tile engine (up, gate_up, down: 512 threads = 8 wavefronts, two per SIMD;
+// dh: 256 threads = 4 wavefronts, one per SIMD):
 //  * the MFMA computes the transposed tile C^T = W^T . X^T: its A operand is
 //    a 32-feature block of the weights, its B operand a 32-token block of
 //    rows, so each lane ends with 4 consecutive output features of one token
 //    and stores 8 bytes at a time;
 //  * workgroup tile 256 tokens x 256 MFMA features (up: 128 W1 + 128 W3
 //    columns of the same 128 outputs); wavefront w owns features
-//    64 w .. 64 w + 63 of all 256 tokens: 2 x 8 v_mfma_f32_32x32x16_bf16
-//    accumulators.  Spreading the wavefronts over the features rather than
-//    2 x 2 halves the slow transposed weight reads per MFMA;
+//    64 (w % 4) .. +63 of tokens 128 (w / 4) .. +127 with eight wavefronts
+//    (2 x 4 v_mfma_f32_32x32x16_bf16 accumulators), of all 256 tokens with
+//    four (2 x 8).  Two wavefronts per SIMD let one issue MFMAs while the
+//    other waits to issue a load into a busy memory pipe (3-4% off the up
+//    GEMM, measured); spreading them over the features rather than 2 x 2
+//    halves the slow transposed weight reads per MFMA;
 //  * K step 32; both tiles go global -> LDS with global_load_lds (16 bytes
 //    per lane, no registers) into a ring of 4 stages (4 x 32 KiB): up to
 //    three stages are in flight while one computes;
@@ -68,14 +72,13 @@ using namespace mfma;
 constexpr int TT = kBf16TileRows;   // 256 tokens (rows) per tile
 constexpr int TF = 256;             // MFMA features per tile (up: 128 g + 128 u)
 constexpr int BK = 32;
-constexpr int NT = 256;
 constexpr int X_ROW = BK * 2;                        // 64 B per token row
 constexpr int X_BYTES = TT * X_ROW;                  // 16 KiB token tile
 constexpr int W_ROW = TF * 2;                        // 512 B per k row
 constexpr int W_BYTES = BK * W_ROW;                  // 16 KiB weight tile
 constexpr int STAGE_BYTES = X_BYTES + W_BYTES;       // 32 KiB
 
-static_assert(TT == 256 && TF == 256 && BK == 32 && NT == 256, "index math below assumes these");
+static_assert(TT == 256 && TF == 256 && BK == 32, "index math below assumes these");
 
 // 64-byte token rows (4 chunks): 16 consecutive rows read at one logical
 // chunk hit 16 distinct bank groups.
@@ -88,6 +91,16 @@ enum : int {
     M_GU = 2,      // x gathered . [W1 | W3] -> [g | u]
     M_DH = 3,      // dy gathered . W2t -> dgu, hw, dwpart
 };
+
+// Wavefronts per workgroup.  Up, gate/up and down run two per SIMD, each
+// owning 64 MFMA features of 128 rows (128 accumulator registers), so that
+// while one stalls issuing its global -> LDS loads the other keeps the SIMD's
+// MFMA pipe fed; dh, whose epilogue is laid out per 64-column wavefront over
+// all 256 rows, runs one per SIMD over 64 features of 256 rows.
+template <int MODE>
+constexpr int waves_of() {
+    return MODE == M_DH ? 4 : 8;
+}
 
 struct GemmArgs {
     GroupArgs g;
@@ -111,9 +124,13 @@ struct GemmArgs {
 __device__ __attribute__((aligned(16))) u32x4_t dh_trash[1];
 
 template <int MODE>
-__global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_kernel(const GemmArgs a) {
     constexpr bool UP = MODE != M_DOWN;         // A gathered by token, K = D, N = F
     constexpr bool PAIR = MODE == M_UP || MODE == M_GU;   // g / u column pairs from W1, W3
+    constexpr int NW = waves_of<MODE>();
+    constexpr int NT = 64 * NW;
+    constexpr int NJ = 32 / NW;        // 32-row blocks per wavefront
+    constexpr int XJ = 16 / NW;        // DMA instructions per wavefront per operand tile
     // Four stage buffers as separate LDS objects: every access names its
     // buffer statically, so the compiler knows reads of one buffer do not
     // alias the asynchronous global_load_lds writes into the others.
@@ -148,6 +165,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int fw = wave & 3;           // MFMA features 64 fw .. 64 fw + 63
+    const int rw = wave >> 2;          // rows 32 NJ rw .. 32 NJ rw + 32 NJ - 1 (NW = 8)
 
     // ---- the group owning row tile mt, and the tile's rows.
     if (mt >= a.g.tile_off[a.g.G]) return;
@@ -158,43 +177,43 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     const int valid_rows = tg.valid_rows;
     if (valid_rows <= 0) return;       // only if tile_off disagrees with offsets
 
-    // ---- token tile sources: DMA instruction j (0..3) of wavefront w fills
-    // rows 64 w + 16 j .. +15; lane -> row 64 w + 16 j + lane/4, physical
+    // ---- token tile sources: DMA instruction j (0..XJ-1) of wavefront w fills
+    // rows 16 XJ w + 16 j .. +15; lane -> row 16 XJ w + 16 j + lane/4, physical
     // chunk lane%4 holding logical chunk (lane%4) ^ swz_x(row).  Routed rows of
     // the up GEMM gather token perm[p] / k (all index loads in flight at
     // once); shared rows read token p - S; the down GEMM reads row p of h.
-    const char* x_src[4];
+    const char* x_src[XJ];
     {
-        int64_t src_row[4];
+        int64_t src_row[XJ];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            src_row[j] = tile_r0 + min(64 * wave + 16 * j + (lane >> 2), valid_rows - 1);
+        for (int j = 0; j < XJ; ++j)
+            src_row[j] = tile_r0 + min(16 * XJ * wave + 16 * j + (lane >> 2), valid_rows - 1);
         if (UP && !shared) {
-            int32_t slot[4];
+            int32_t slot[XJ];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) slot[j] = a.g.perm[src_row[j]];
+            for (int j = 0; j < XJ; ++j) slot[j] = a.g.perm[src_row[j]];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) src_row[j] = slot[j] / a.g.k;
+            for (int j = 0; j < XJ; ++j) src_row[j] = slot[j] / a.g.k;
         } else if (UP) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) src_row[j] -= a.g.S;
+            for (int j = 0; j < XJ; ++j) src_row[j] -= a.g.S;
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 64 * wave + 16 * j + (lane >> 2);
+        for (int j = 0; j < XJ; ++j) {
+            const int row = 16 * XJ * wave + 16 * j + (lane >> 2);
             x_src[j] = (const char*)(a.a + src_row[j] * (int64_t)K + 8 * ((lane & 3) ^ swz_x(row)));
         }
     }
-    // ---- weight tile sources: DMA instruction j (0..3) of wavefront w fills
-    // k rows 8 w + 2 j, +1; lane -> k row 8 w + 2 j + lane/32, physical chunk
+    // ---- weight tile sources: DMA instruction j (0..XJ-1) of wavefront w fills
+    // k rows 2 XJ w + 2 j, +1; lane -> k row 2 XJ w + 2 j + lane/32, physical chunk
     // lane%32 holding logical chunk cl = phys ^ swz_tr(k) = MFMA features
     // 8 cl .. 8 cl + 7.  Up: wavefront block wb = cl / 8, g when (cl / 4) is
     // even, u when odd, output column 32 wb + 8 (cl % 4) of the tile's 128.
     const int64_t gstride = (int64_t)a.D * a.F;
-    const char* w_src[4];
+    const char* w_src[XJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int kr = 8 * wave + 2 * j + (lane >> 5);
+    for (int j = 0; j < XJ; ++j) {
+        const int kr = 2 * XJ * wave + 2 * j + (lane >> 5);
         const int cl = (lane & 31) ^ swz_tr(kr);
         int col;
         const uint16_t* base;
@@ -213,11 +232,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
 
     auto issue = [&](int kt, char* st) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            load_lds16(x_src[j] + (int64_t)kt * X_ROW, st + (64 * wave + 16 * j) * X_ROW);
+        for (int j = 0; j < XJ; ++j)
+            load_lds16(x_src[j] + (int64_t)kt * X_ROW, st + (16 * XJ * wave + 16 * j) * X_ROW);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            load_lds16(w_src[j] + kt * w_step, st + X_BYTES + (8 * wave + 2 * j) * W_ROW);
+        for (int j = 0; j < XJ; ++j)
+            load_lds16(w_src[j] + kt * w_step, st + X_BYTES + (2 * XJ * wave + 2 * j) * W_ROW);
     };
 
     // ---- MFMA operand read offsets (bytes within a stage).
@@ -231,24 +250,24 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int k = 8 * (G >> 1) + 4 * r + (sl >> 2);
-            const int R = 64 * wave + 32 * mi + 16 * (G & 1) + 4 * (sl & 3);
+            const int R = 64 * fw + 32 * mi + 16 * (G & 1) + 4 * (sl & 3);
             w_off[mi][r] = X_BYTES + k * W_ROW + (((R >> 3) ^ swz_tr(k)) << 4) + 8 * ((R >> 2) & 1);
         }
     // Token operand (B): lane reads row 32 nj + lane%32, logical chunk
     // 2 ks + lane/32; rows 32 nj + l and l share swz_x, so one offset serves
     // all eight blocks.
     const int xr = lane & 31;
-    const int x_base = xr * X_ROW;
+    const int x_base = (32 * NJ * rw + xr) * X_ROW;
     const int x_sw = swz_x(xr);
 
-    f32x16_t acc[2][8];
+    f32x16_t acc[2][NJ];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < 8; ++nj) acc[mi][nj] = f32x16_t{};
+        for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = f32x16_t{};
 
     struct Frags {
-        bf16x8_t w[2][2], x[2][8];      // [k16 slice][block]
+        bf16x8_t w[2][2], x[2][NJ];     // [k16 slice][block]
     };
     auto read_frags = [&](const char* st, Frags& f) {
 #pragma unroll
@@ -259,7 +278,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
                                        read_tr(st + w_off[mi][1] + ks * 16 * W_ROW));
             const int c = ((2 * ks + (lane >> 5)) ^ x_sw) << 4;
 #pragma unroll
-            for (int nj = 0; nj < 8; ++nj)
+            for (int nj = 0; nj < NJ; ++nj)
                 f.x[ks][nj] = __builtin_bit_cast(
                     bf16x8_t, *(const u32x4_t*)(st + x_base + nj * 32 * X_ROW + c));
         }
@@ -268,7 +287,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int nj = 0; nj < 8; ++nj)
+            for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi)
                     acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[ks][mi], f.x[ks][nj],
@@ -283,14 +302,14 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     //   barrier;
     //   issue the loads of stage s+3 into the buffer of stage s-1;
     //   read stage s+1's operands into fn;
-    //   32 MFMAs on fc -- the reads of fn land under them.
+    //   the MFMAs on fc -- the reads of fn land under them.
     // The buffer of stage s-1 is free at step s: its operands were read in
     // step s-2 and consumed by the MFMAs of step s-1, which every wavefront
     // finished before arriving at this barrier.  Loads past the last stage
     // re-read the last stage (into buffers never computed on), so the number
     // of loads per stage stays fixed.
     const int KT = K / BK;
-    constexpr int PER_STAGE = 8;       // global_load_lds per wavefront per stage
+    constexpr int PER_STAGE = 2 * XJ;  // global_load_lds per wavefront per stage
     auto wait_stage = [] {
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(PER_STAGE, 0));
         __builtin_amdgcn_s_barrier();
@@ -302,38 +321,40 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
         read_frags(nxt, fn);
         mfmas(fc);
         // A wavefront issues in order and stalls on a load or LDS read while
-        // that pipe is backed up, so bursts of either would idle the MFMAs
-        // (32 MFMAs, 8 loads, 24 reads per step).  K = D (up, gate_up): the
-        // loads go out one per 2 MFMAs in the first half of the step, so
-        // they land well before the next step's wait (~1% off the forward at
-        // 32k tokens); K = F (down, dh): one per 4 MFMAs over the whole step
-        // (the front-loaded order measured 1.6% slower there).
-        if constexpr (UP) {
+        // that pipe is backed up, so bursts of either would idle its MFMAs.
+        // Eight wavefronts (16 MFMAs, 4 loads, 16 reads each per step): one
+        // load per 4 MFMAs over the whole step, a read after every MFMA (the
+        // front-loaded and the compiler's own orders measured 1-4% slower).
+        // Four (dh: 32 MFMAs, 8 loads, 24 reads): the loads one per 2 MFMAs
+        // in the first half of the step, so they land well before the next
+        // step's wait.
+        if constexpr (NW == 8) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
         }
         fence();
@@ -366,12 +387,13 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     // ---- epilogue, staged through LDS so that every store instruction
     // writes whole row segments (16 bytes per lane, 256 or 512 contiguous
     // bytes per row) instead of 8-byte pieces of 32 rows.  acc[mi][nj]
-    // element v of lane l: token 32 nj + l%32, MFMA feature
-    // 64 w + 32 mi + 8 (v/4) + 4 (l/32) + v%4.  Up: h column 32 w + the
+    // element v of lane l: token 32 NJ rw + 32 nj + l%32, MFMA feature
+    // 64 fw + 32 mi + 8 (v/4) + 4 (l/32) + v%4.  Up: h column 32 fw + the
     // feature's offset in its 32-block (g in mi = 0, u in mi = 1); down:
     // output column = MFMA feature.  Tile rows 64 q .. 64 q + 63 are staged in
     // stage buffer q, 16-byte chunks XOR-swizzled by the row's low 4 bits.
     if constexpr (MODE == M_DH) {
+        static_assert(NW == 4, "the dh epilogue lays out one wavefront per 64 columns of 256 rows");
         // Element v of acc[mi][nj] on lane l: token 32 nj + l%32, column
         // nt*256 + 64 w + 32 mi + 8 (v/4) + 4 (l/32) + v%4; each lane handles
         // four consecutive columns at a time.  The wavefront's 64 columns are
@@ -547,19 +569,19 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // this wavefront's loads and LDS reads done
     __syncthreads();                                // ... and every other wavefront's
 #pragma unroll
-    for (int nj = 0; nj < 8; ++nj) {
-        const int t = 32 * nj + (lane & 31);
+    for (int nj = 0; nj < NJ; ++nj) {
+        const int t = 32 * NJ * rw + 32 * nj + (lane & 31);
         char* rowp = orow(t);
         const int sw = t & 15;
         if (MODE == M_GU) {
-            // g (mi = 0) to staged columns 32 w + ..., u (mi = 1) to 128 + 32 w + ...
+            // g (mi = 0) to staged columns 32 fw + ..., u (mi = 1) to 128 + 32 fw + ...
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi) {
                 const f32x16_t& c = acc[mi][nj];
 #pragma unroll
                 for (int vg = 0; vg < 4; ++vg) {
                     const int v = 4 * vg;
-                    const int ch = 16 * mi + 4 * wave + vg;
+                    const int ch = 16 * mi + 4 * fw + vg;
                     *(uint2*)(rowp + ((ch ^ sw) << 4) + 8 * (lane >> 5)) =
                         make_uint2(pack_bf16(c[v], c[v + 1]), pack_bf16(c[v + 2], c[v + 3]));
                 }
@@ -570,7 +592,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
 #pragma unroll
             for (int vg = 0; vg < 4; ++vg) {
                 const int v = 4 * vg;
-                const int c = 4 * wave + vg;
+                const int c = 4 * fw + vg;
                 *(uint2*)(rowp + ((c ^ sw) << 4) + 8 * (lane >> 5)) =
                     make_uint2(pack_bf16(silu_mul(g[v], u[v]), silu_mul(g[v + 1], u[v + 1])),
                                pack_bf16(silu_mul(g[v + 2], u[v + 2]), silu_mul(g[v + 3], u[v + 3])));
@@ -582,7 +604,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_bf16_kernel(const GemmArgs
 #pragma unroll
                 for (int vg = 0; vg < 4; ++vg) {
                     const int v = 4 * vg;
-                    const int ch = 8 * wave + 4 * mi + vg;
+                    const int ch = 8 * fw + 4 * mi + vg;
                     *(uint2*)(rowp + ((ch ^ sw) << 4) + 8 * (lane >> 5)) =
                         make_uint2(pack_bf16(c[v], c[v + 1]), pack_bf16(c[v + 2], c[v + 3]));
                 }
@@ -629,7 +651,7 @@ hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* 
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, h, D, F, (F + TF / 2 - 1) / (TF / 2)};
     a.col_groups = column_groups(a.n_tiles, D);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<M_UP><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    grouped_gemm_bf16_kernel<M_UP><<<grid_for_work(blocks), 64 * waves_of<M_UP>(), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -639,7 +661,7 @@ hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, c
                Y, D, F, (D + TF - 1) / TF};
     a.col_groups = column_groups(a.n_tiles, F);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<M_DOWN><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    grouped_gemm_bf16_kernel<M_DOWN><<<grid_for_work(blocks), 64 * waves_of<M_DOWN>(), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -650,7 +672,7 @@ hipError_t launch_bwd_gate_up_bf16(const GroupArgs& g, const void* x, const void
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, gu, D, F, (F + TF / 2 - 1) / (TF / 2)};
     a.col_groups = column_groups(a.n_tiles, D);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<M_GU><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    grouped_gemm_bf16_kernel<M_GU><<<grid_for_work(blocks), 64 * waves_of<M_GU>(), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -661,7 +683,7 @@ hipError_t launch_bwd_dh_bf16(const GroupArgs& g, const float* topk_w, const voi
                dgu, D, F, (F + TF - 1) / TF, 1, topk_w, (const uint16_t*)gu, (uint16_t*)hw, dwpart};
     a.col_groups = column_groups(a.n_tiles, D);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<M_DH><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    grouped_gemm_bf16_kernel<M_DH><<<grid_for_work(blocks), 64 * waves_of<M_DH>(), 0, s>>>(a);
     return hipGetLastError();
 }
 
