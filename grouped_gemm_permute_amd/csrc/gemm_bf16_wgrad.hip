@@ -19,10 +19,11 @@
 // summation order, no atomics) and writes the fp32 gradient, zero for a
 // group without rows.
 //
-// Tile engine: 256 threads = 4 wavefronts; the MFMA's A operand is 32
-// N-features (wavefront w owns N features 64 w .. 64 w + 63), its B operand
-// 32 M-features (all 256 for every wavefront), so each lane ends with four
-// consecutive N values of one M row and stores 16 bytes.  K step 32 rows,
+// Tile engine: 512 threads = 8 wavefronts, two per SIMD (one issues MFMAs
+// while the other is held issuing a load); the MFMA's A operand is 32
+// N-features, its B operand 32 M-features; wavefront w owns N features
+// 64 (w % 4) .. +63 of M features 128 (w / 4) .. +127, so each lane ends
+// with four consecutive N values of one M row.  K step 32 rows,
 // a 4-stage ring of 32 KiB stages (M tile, then N tile, each 32 rows x 512
 // bytes, XOR-swizzled in 16-byte chunks as the forward's weight tiles),
 // filled with global_load_lds.  Gathered rows (x and dy read through the
@@ -37,7 +38,7 @@ namespace {
 
 using namespace mfma;
 
-constexpr int TM = 256, TN = 256, BK = 32, NT = 256;
+constexpr int TM = 256, TN = 256, BK = 32, NT = 512;
 constexpr int ROW = 512;                       // bytes per k row of a 256-feature tile
 constexpr int TILE_BYTES = BK * ROW;           // 16 KiB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // M tile, then N tile
@@ -73,6 +74,8 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
     const int tm = rem / a.n_tiles, tn = rem - tm * a.n_tiles;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int fw = wave & 3;           // N features 64 fw .. 64 fw + 63
+    const int rw = wave >> 2;          // M features 128 rw .. 128 rw + 127
 
     if (ck >= a.g.tile_off[a.g.G]) return;
     const TileGroup tg = find_tile_group(a.g, ck, a.KC, lane);
@@ -83,9 +86,9 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
     const int KT = (valid + BK - 1) / BK;
 
     // ---- the chunk's token table, padded to KT * BK rows with the last
-    // row's token and stored in issue order: entry ((kt * 2 + h) * 4 + w) * 4
-    // + j holds row kt * BK + 8 w + 2 j + h, so a lane's four DMA rows of a
-    // K step are one 16-byte LDS read.
+    // row's token and stored in issue order: entry ((kt * 2 + h) * 8 + w) * 2
+    // + j holds row kt * BK + 4 w + 2 j + h, so a lane's two DMA rows of a
+    // K step are one 8-byte LDS read.
     // All of a thread's index loads are issued before the first is used (one
     // memory round trip rather than one per entry).
     if (GM || GN) {
@@ -102,26 +105,26 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
             const int i = tid + q * NT;
             if (i < KT * BK) {
                 const int kt = i >> 5, kr = i & 31;
-                const int e = ((kt * 2 + (kr & 1)) * 4 + (kr >> 3)) * 4 + ((kr >> 1) & 3);
+                const int e = ((kt * 2 + (kr & 1)) * 8 + (kr >> 2)) * 2 + ((kr >> 1) & 1);
                 tok[e] = shared ? v[q] : v[q] / (uint32_t)a.g.k;
             }
         }
         __syncthreads();
     }
 
-    // ---- loads: DMA instruction j (0..3) of wavefront w fills k rows
-    // 8 w + 2 j, +1 of each tile; lane -> k row 8 w + 2 j + lane/32,
+    // ---- loads: DMA instruction j (0, 1) of wavefront w fills k rows
+    // 4 w + 2 j, +1 of each tile; lane -> k row 4 w + 2 j + lane/32,
     // physical chunk lane%32 holding logical chunk cl = phys ^ swz_tr(k),
     // i.e. features 8 cl .. 8 cl + 7.  Row addresses are the row index (32
     // bits) times the row pitch plus a per-lane column base: one
     // v_mad_u64_u32 per load, no divergent code on the way to the DMA.
     const int M = a.M, N = a.N;
     const uint32_t pitch_m = 2u * (uint32_t)M, pitch_n = 2u * (uint32_t)N;
-    const char* m_base[4];
-    const char* n_base[4];
+    const char* m_base[2];
+    const char* n_base[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int kr = 8 * wave + 2 * j + (lane >> 5);
+    for (int j = 0; j < 2; ++j) {
+        const int kr = 4 * wave + 2 * j + (lane >> 5);
         const int cl = (lane & 31) ^ swz_tr(kr);
         int m = tm * TM + 8 * cl, n = tn * TN + 8 * cl;
         if (m >= M) m = 0;                 // a valid address; its sums are never stored
@@ -129,27 +132,27 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
         m_base[j] = (const char*)(a.am + m);
         n_base[j] = (const char*)(a.bn + n);
     }
-    const uint32_t own0 = 8 * wave + (lane >> 5);   // + 2 j: the lane's rows in a K step
-    u32x4_t tok_pf = {0u, 0u, 0u, 0u};   // tokens of the next stage's rows
+    const uint32_t own0 = 4 * wave + (lane >> 5);   // + 2 j: the lane's rows in a K step
+    uint2 tok_pf = {0u, 0u};           // tokens of the next stage's rows
     auto fetch_tok = [&](int kt) {
-        if (GM || GN)
-            tok_pf = *(const u32x4_t*)&tok[((kt * 2 + (lane >> 5)) * 4 + wave) * 4];
+        if (GM || GN) tok_pf = *(const uint2*)&tok[((kt * 2 + (lane >> 5)) * 8 + wave) * 2];
     };
     auto issue = [&](int kt, char* st) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
             const uint32_t i = (uint32_t)(kt * BK) + own0 + 2 * j;
             const uint32_t own = r0 + min(i, (uint32_t)valid - 1);
-            const uint32_t rm = GM ? tok_pf[j] : own;
-            const uint32_t rn = GN ? tok_pf[j] : own;
+            const uint32_t tk = j ? tok_pf.y : tok_pf.x;
+            const uint32_t rm = GM ? tk : own;
+            const uint32_t rn = GN ? tk : own;
             const char* sm = m_base[j] + (uint64_t)rm * pitch_m;
             const char* row_n = n_base[j] + (uint64_t)rn * pitch_n;
             // opaque to the optimiser, so the multiply is not sunk into a
             // divergent branch (exec-mask writes end a scheduling region)
             asm volatile("" : "+v"(row_n));
             const char* sn = i < (uint32_t)valid ? row_n : (const char*)a.zeros;
-            load_lds16(sm, st + (8 * wave + 2 * j) * ROW);
-            load_lds16(sn, st + TILE_BYTES + (8 * wave + 2 * j) * ROW);
+            load_lds16(sm, st + (4 * wave + 2 * j) * ROW);
+            load_lds16(sn, st + TILE_BYTES + (4 * wave + 2 * j) * ROW);
         }
     };
 
@@ -161,25 +164,25 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
         const int k = 8 * (G >> 1) + 4 * r + (sl >> 2);
         return tile + k * ROW + (((R >> 3) ^ swz_tr(k)) << 4) + 8 * ((R >> 2) & 1);
     };
-    int n_off[2][2], m_off[8][2];
+    int n_off[2][2], m_off[4][2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
-            n_off[mi][r] = tr_off(TILE_BYTES, 64 * wave + 32 * mi + 16 * (G & 1) + 4 * (sl & 3), r);
+            n_off[mi][r] = tr_off(TILE_BYTES, 64 * fw + 32 * mi + 16 * (G & 1) + 4 * (sl & 3), r);
 #pragma unroll
-        for (int nj = 0; nj < 8; ++nj)
-            m_off[nj][r] = tr_off(0, 32 * nj + 16 * (G & 1) + 4 * (sl & 3), r);
+        for (int nj = 0; nj < 4; ++nj)
+            m_off[nj][r] = tr_off(0, 128 * rw + 32 * nj + 16 * (G & 1) + 4 * (sl & 3), r);
     }
 
-    f32x16_t acc[2][8];
+    f32x16_t acc[2][4];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < 8; ++nj) acc[mi][nj] = f32x16_t{};
+        for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x16_t{};
 
     struct Frags {
-        bf16x8_t n[2][2], m[2][8];      // [k16 slice][block]
+        bf16x8_t n[2][2], m[2][4];      // [k16 slice][block]
     };
     auto read_frags = [&](const char* st, Frags& f) {
 #pragma unroll
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
                 f.n[ks][mi] = cat_bf16(read_tr(st + n_off[mi][0] + ks * 16 * ROW),
                                        read_tr(st + n_off[mi][1] + ks * 16 * ROW));
 #pragma unroll
-            for (int nj = 0; nj < 8; ++nj)
+            for (int nj = 0; nj < 4; ++nj)
                 f.m[ks][nj] = cat_bf16(read_tr(st + m_off[nj][0] + ks * 16 * ROW),
                                        read_tr(st + m_off[nj][1] + ks * 16 * ROW));
         }
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int nj = 0; nj < 8; ++nj)
+            for (int nj = 0; nj < 4; ++nj)
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi)
                     acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.n[ks][mi], f.m[ks][nj],
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
     // buffer of stage s-1, reads stage s+1's operands and runs stage s's
     // MFMAs.  The tokens for the next issue are read from LDS during the
     // step and waited for at the next step's barrier.
-    constexpr int PER_STAGE = 8;
+    constexpr int PER_STAGE = 4;
     auto step = [&](Frags& fc, Frags& fn, const char* nxt, char* dma, int kl) {
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(PER_STAGE, 0));
         __builtin_amdgcn_s_barrier();
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
         read_frags(nxt, fn);
         mfmas(fc);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
             __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
@@ -230,6 +233,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         fence();
     };
@@ -266,16 +270,17 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
     // ---- the tile: element v of acc[mi][nj] on lane l is M row
-    // tm*256 + 32 nj + l%32, N columns tn*256 + 64 w + 32 mi + 8 (v/4) + 4 (l/32) + 0..3.
-    // It leaves through LDS in two passes of 128 M rows: block nj of the
-    // pass goes to stage buffer nj % 4 as 32 rows of 256 fp32 (16-byte
-    // chunk c of row r at physical chunk c ^ r), then each wavefront stores
-    // whole 1 KiB rows, one row per instruction.  A group of one chunk writes
+    // tm*256 + 128 rw + 32 nj + l%32, N columns tn*256 + 64 fw + 32 mi + 8 (v/4) + 4 (l/32) + 0..3.
+    // It leaves through LDS in two passes of 128 M rows, pass p holding the
+    // rows of the wavefronts with rw = p: their block nj goes to stage buffer
+    // nj as 32 rows of 256 fp32 (16-byte chunk c of row r at physical chunk
+    // c ^ r), then every wavefront stores 16 whole 1 KiB rows, one row per
+    // instruction.  A group of one chunk writes
     // its gradient directly; otherwise the chunk's partial goes to the
     // partial buffer for wgrad_reduce.
     __syncthreads();   // every wavefront is done with the operand stages
     const bool single = a.g.tile_off[tg.grp + 1] - a.g.tile_off[tg.grp] == 1;
-    char* const stq[4] = {st0, st1, st2, st3};
+    auto stq = [&](int q) -> char* { return q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3; };
     const int n0 = tn * TN + 4 * lane;       // this lane's 4 columns in the store phase
     const bool col_ok = n0 < N;
     float* dst_base;
@@ -295,29 +300,29 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(const WgradArgs a) {
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
         if (pass) __syncthreads();           // the previous pass's rows are read
+        if (rw == pass) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int nj = 4 * pass + q;
+            for (int nj = 0; nj < 4; ++nj)
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+                for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-                for (int vg = 0; vg < 4; ++vg) {
-                    const int c = 16 * wave + 8 * mi + 2 * vg + (lane >> 5);
-                    const f32x16_t& v = acc[mi][nj];
-                    *(float4*)(stq[q] + rl * 1024 + ((c ^ rl) << 4)) =
-                        make_float4(v[4 * vg], v[4 * vg + 1], v[4 * vg + 2], v[4 * vg + 3]);
-                }
+                    for (int vg = 0; vg < 4; ++vg) {
+                        const int c = 16 * fw + 8 * mi + 2 * vg + (lane >> 5);
+                        const f32x16_t& v = acc[mi][nj];
+                        *(float4*)(stq(nj) + rl * 1024 + ((c ^ rl) << 4)) =
+                            make_float4(v[4 * vg], v[4 * vg + 1], v[4 * vg + 2], v[4 * vg + 3]);
+                    }
         }
         __syncthreads();
+        // wavefront w: rows 16 (w % 2) .. +15 of stage buffer w / 2
+        char* const sq = stq(wave >> 1);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int r = 8 * wave + i;
-                const float4 row = *(const float4*)(stq[q] + r * 1024 + ((lane ^ r) << 4));
-                const int m = tm * TM + 32 * (4 * pass + q) + r;
-                if (col_ok && m < M) *(float4*)(dst_base + (int64_t)m * pitch) = row;
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * (wave & 1) + i;
+            const float4 row = *(const float4*)(sq + r * 1024 + ((lane ^ r) << 4));
+            const int m = tm * TM + 128 * pass + 32 * (wave >> 1) + r;
+            if (col_ok && m < M) *(float4*)(dst_base + (int64_t)m * pitch) = row;
+        }
     }
 }
 
