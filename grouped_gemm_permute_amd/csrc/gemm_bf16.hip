@@ -31,23 +31,28 @@
 //  The backward's dx rows are the down mode run with K = 2F over the
 //  transposed, stacked [W1^T ; W3^T] and A = dgu.
 //
-// Tile engine (up, gate_up, down: 512 threads = 8 wavefronts, two per SIMD;
-// dh: 256 threads = 4 wavefronts, one per SIMD):
+// Tile engine (256 threads = 4 wavefronts, one per SIMD of the CU):
 //  * the MFMA computes the transposed tile C^T = W^T . X^T: its A operand is
 //    a 32-feature block of the weights, its B operand a 32-token block of
 //    rows, so each lane ends with 4 consecutive output features of one token
 //    and stores 8 bytes at a time;
-//  * workgroup tile 256 tokens x 256 MFMA features (up: 128 W1 + 128 W3
+//  * row tiles of 256 tokens x 256 MFMA features (up: 128 W1 + 128 W3
 //    columns of the same 128 outputs); wavefront w owns features
-//    64 (w % 4) .. +63 of tokens 128 (w / 4) .. +127 with eight wavefronts
-//    (2 x 4 v_mfma_f32_32x32x16_bf16 accumulators), of all 256 tokens with
-//    four (2 x 8).  Two wavefronts per SIMD let one issue MFMAs while the
-//    other waits to issue a load into a busy memory pipe (3-4% off the up
-//    GEMM, measured); spreading them over the features rather than 2 x 2
+//    64 w .. 64 w + 63.  Up, gate_up and down: a workgroup takes one
+//    128-token half of a row tile (2 x 4 v_mfma_f32_32x32x16_bf16
+//    accumulators, 250 registers, 72 KiB of LDS), so two workgroups share a
+//    CU and each SIMD runs two wavefronts of different workgroups: one keeps
+//    the MFMA pipe fed while the other is in its prologue, its SiLU
+//    epilogue or held issuing a load into a busy memory pipe (up GEMM 2-9%
+//    faster than one 256-token workgroup of eight wavefronts per CU,
+//    measured; results bitwise identical).  dh: one workgroup per CU on
+//    the whole row tile (2 x 8 accumulators), its epilogue using all the
+//    LDS.  Spreading the wavefronts over the features rather than 2 x 2
 //    halves the slow transposed weight reads per MFMA;
 //  * K step 32; both tiles go global -> LDS with global_load_lds (16 bytes
-//    per lane, no registers) into a ring of 4 stages (4 x 32 KiB): up to
-//    three stages are in flight while one computes;
+//    per lane, no registers) into a ring of stages: three of 24 KiB for
+//    half tiles (one stage in flight while one computes), four of 32 KiB
+//    for dh;
 //  * token rows are K-contiguous in memory and in LDS (read with
 //    ds_read_b128); the weights stay [K][N] (N contiguous) in LDS and the
 //    MFMA's K-consecutive operand is produced by ds_read_b64_tr_b16, which
@@ -73,10 +78,8 @@ constexpr int TT = kBf16TileRows;   // 256 tokens (rows) per tile
 constexpr int TF = 256;             // MFMA features per tile (up: 128 g + 128 u)
 constexpr int BK = 32;
 constexpr int X_ROW = BK * 2;                        // 64 B per token row
-constexpr int X_BYTES = TT * X_ROW;                  // 16 KiB token tile
 constexpr int W_ROW = TF * 2;                        // 512 B per k row
 constexpr int W_BYTES = BK * W_ROW;                  // 16 KiB weight tile
-constexpr int STAGE_BYTES = X_BYTES + W_BYTES;       // 32 KiB
 
 static_assert(TT == 256 && TF == 256 && BK == 32, "index math below assumes these");
 
@@ -92,14 +95,21 @@ enum : int {
     M_DH = 3,      // dy gathered . W2t -> dgu, hw, dwpart
 };
 
-// Wavefronts per workgroup.  Up, gate/up and down run two per SIMD, each
-// owning 64 MFMA features of 128 rows (128 accumulator registers), so that
-// while one stalls issuing its global -> LDS loads the other keeps the SIMD's
-// MFMA pipe fed; dh, whose epilogue is laid out per 64-column wavefront over
-// all 256 rows, runs one per SIMD over 64 features of 256 rows.
-template <int MODE>
+// Workgroup shapes, each chosen by measurement (interleaved A/Bs):
+//  * whole tiles (HALF = false): 8 wavefronts, two per SIMD, on a 256-row
+//    tile, one workgroup per CU (a 4-stage ring of 32 KiB), so one
+//    wavefront's MFMAs cover the other's stalls issuing loads;
+//  * half tiles (HALF = true, up only): 4 wavefronts on one 128-row half of
+//    a tile (a 3-stage ring of 24 KiB), two workgroups per CU, so the SiLU
+//    epilogue and the prologue of one overlap the other's MFMAs and the
+//    last round is finer.  It stages 1.5x the bytes per MFMA: the up GEMM
+//    takes it when its whole-tile grid is short (up_half_tiles), where it
+//    measured 4-9% faster; on long grids it is even to 1% slower, and for
+//    gate/up and down 4-10% slower;
+//  * dh: 4 wavefronts on a whole tile, its epilogue using all the LDS.
+template <int MODE, bool HALF>
 constexpr int waves_of() {
-    return MODE == M_DH ? 4 : 8;
+    return HALF || MODE == M_DH ? 4 : 8;
 }
 
 struct GemmArgs {
@@ -123,21 +133,28 @@ struct GemmArgs {
 // Target of the dh epilogue's stores for rows and columns outside the tile.
 __device__ __attribute__((aligned(16))) u32x4_t dh_trash[1];
 
-template <int MODE>
-__global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_kernel(const GemmArgs a) {
+template <int MODE, bool HALF>
+__global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void grouped_gemm_bf16_kernel(
+    const GemmArgs a) {
     constexpr bool UP = MODE != M_DOWN;         // A gathered by token, K = D, N = F
     constexpr bool PAIR = MODE == M_UP || MODE == M_GU;   // g / u column pairs from W1, W3
-    constexpr int NW = waves_of<MODE>();
+    static_assert(!HALF || MODE == M_UP, "half tiles are built for the up GEMM");
+    constexpr int NW = waves_of<MODE, HALF>();
     constexpr int NT = 64 * NW;
-    constexpr int NJ = 32 / NW;        // 32-row blocks per wavefront
-    constexpr int XJ = 16 / NW;        // DMA instructions per wavefront per operand tile
-    // Four stage buffers as separate LDS objects: every access names its
+    constexpr int ROWS = HALF ? TT / 2 : TT;   // rows of the workgroup's tile
+    constexpr int NJ = ROWS * 4 / (32 * NW);   // 32-row blocks per wavefront
+    constexpr int XJ = ROWS / (16 * NW);       // token-tile DMA instructions per wavefront
+    constexpr int WJ = 16 / NW;                // weight-tile DMA instructions per wavefront
+    constexpr int XBYTES = ROWS * X_ROW;       // token tile
+    constexpr int SBYTES = XBYTES + W_BYTES;   // one stage
+    constexpr int NS = HALF ? 3 : 4;           // ring stages
+    // The stage buffers as separate LDS objects: every access names its
     // buffer statically, so the compiler knows reads of one buffer do not
     // alias the asynchronous global_load_lds writes into the others.
-    __shared__ __attribute__((aligned(1024))) char st0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char st3[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st0[SBYTES];
+    __shared__ __attribute__((aligned(1024))) char st1[SBYTES];
+    __shared__ __attribute__((aligned(1024))) char st2[SBYTES];
+    __shared__ __attribute__((aligned(1024))) char st3[NS == 4 ? SBYTES : 16];
 
     const int K = UP ? a.D : a.F;      // reduction length
     const int N = UP ? a.F : a.D;      // output columns
@@ -145,37 +162,40 @@ __global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_ke
 
     // ---- this workgroup's tile.  The column tiles are split into col_groups
     // groups of ncol; the 8 / col_groups XCDs of group c (XCD x = workgroups
-    // b with b % 8 == x, dispatched round-robin) split its m_tiles x ncol
-    // tiles (row-major) into contiguous, equal ranges.  An XCD thus keeps
-    // one weight slab of ncol column tiles in its L2 while row tiles stream
-    // through; with one group this is xcd_remap_work over all tiles.
-    int mt, nt;
+    // b with b % 8 == x, dispatched round-robin) split its row tiles x ncol
+    // tiles (row-major; with half tiles each row tile counts as its two
+    // halves) into contiguous, equal ranges.  An XCD thus keeps one weight
+    // slab of ncol column tiles in its L2 while row tiles stream through;
+    // with one group this is xcd_remap_work over all tiles.
+    int mt, hf, nt;
     {
         const int m_tiles = a.g.tile_off[a.g.G];
         const int xpg = 8 / a.col_groups, ncol = a.n_tiles / a.col_groups;
         const int xcd = blockIdx.x & 7;
         const int c = xcd / xpg, share = xcd - c * xpg;
-        const int items = m_tiles * ncol;
+        const int items = (HALF ? 2 : 1) * m_tiles * ncol;
         const int per = items / xpg, rem = items - per * xpg;
         const int i = blockIdx.x >> 3;
         if (i >= per + (share < rem ? 1 : 0)) return;
         const int j = share * per + min(share, rem) + i;
-        mt = j / ncol;
-        nt = c * ncol + (j - mt * ncol);
+        const int mh = j / ncol;
+        mt = HALF ? mh >> 1 : mh;
+        hf = HALF ? mh & 1 : 0;
+        nt = c * ncol + (j - mh * ncol);
     }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int fw = wave & 3;           // MFMA features 64 fw .. 64 fw + 63
-    const int rw = wave >> 2;          // rows 32 NJ rw .. 32 NJ rw + 32 NJ - 1 (NW = 8)
+    const int rw = wave >> 2;          // rows 32 NJ rw .. +32 NJ - 1 (eight wavefronts)
 
     // ---- the group owning row tile mt, and the tile's rows.
     if (mt >= a.g.tile_off[a.g.G]) return;
     const TileGroup tg = find_tile_group(a.g, mt, TT, lane);
     const int grp = tg.grp;
     const bool shared = grp >= a.g.E;
-    const int64_t tile_r0 = tg.tile_r0;
-    const int valid_rows = tg.valid_rows;
-    if (valid_rows <= 0) return;       // only if tile_off disagrees with offsets
+    const int64_t tile_r0 = tg.tile_r0 + ROWS * hf;
+    const int valid_rows = min(tg.valid_rows - ROWS * hf, ROWS);
+    if (valid_rows <= 0) return;       // an empty second half, or tile_off disagreeing with offsets
 
     // ---- token tile sources: DMA instruction j (0..XJ-1) of wavefront w fills
     // rows 16 XJ w + 16 j .. +15; lane -> row 16 XJ w + 16 j + lane/4, physical
@@ -204,16 +224,16 @@ __global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_ke
             x_src[j] = (const char*)(a.a + src_row[j] * (int64_t)K + 8 * ((lane & 3) ^ swz_x(row)));
         }
     }
-    // ---- weight tile sources: DMA instruction j (0..XJ-1) of wavefront w fills
-    // k rows 2 XJ w + 2 j, +1; lane -> k row 2 XJ w + 2 j + lane/32, physical chunk
+    // ---- weight tile sources: DMA instruction j (0..WJ-1) of wavefront w fills
+    // k rows 2 WJ w + 2 j, +1; lane -> k row 2 WJ w + 2 j + lane/32, physical chunk
     // lane%32 holding logical chunk cl = phys ^ swz_tr(k) = MFMA features
     // 8 cl .. 8 cl + 7.  Up: wavefront block wb = cl / 8, g when (cl / 4) is
     // even, u when odd, output column 32 wb + 8 (cl % 4) of the tile's 128.
     const int64_t gstride = (int64_t)a.D * a.F;
-    const char* w_src[XJ];
+    const char* w_src[WJ];
 #pragma unroll
-    for (int j = 0; j < XJ; ++j) {
-        const int kr = 2 * XJ * wave + 2 * j + (lane >> 5);
+    for (int j = 0; j < WJ; ++j) {
+        const int kr = 2 * WJ * wave + 2 * j + (lane >> 5);
         const int cl = (lane & 31) ^ swz_tr(kr);
         int col;
         const uint16_t* base;
@@ -235,8 +255,8 @@ __global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_ke
         for (int j = 0; j < XJ; ++j)
             load_lds16(x_src[j] + (int64_t)kt * X_ROW, st + (16 * XJ * wave + 16 * j) * X_ROW);
 #pragma unroll
-        for (int j = 0; j < XJ; ++j)
-            load_lds16(w_src[j] + kt * w_step, st + X_BYTES + (2 * XJ * wave + 2 * j) * W_ROW);
+        for (int j = 0; j < WJ; ++j)
+            load_lds16(w_src[j] + kt * w_step, st + XBYTES + (2 * WJ * wave + 2 * j) * W_ROW);
     };
 
     // ---- MFMA operand read offsets (bytes within a stage).
@@ -251,7 +271,7 @@ __global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_ke
         for (int r = 0; r < 2; ++r) {
             const int k = 8 * (G >> 1) + 4 * r + (sl >> 2);
             const int R = 64 * fw + 32 * mi + 16 * (G & 1) + 4 * (sl & 3);
-            w_off[mi][r] = X_BYTES + k * W_ROW + (((R >> 3) ^ swz_tr(k)) << 4) + 8 * ((R >> 2) & 1);
+            w_off[mi][r] = XBYTES + k * W_ROW + (((R >> 3) ^ swz_tr(k)) << 4) + 8 * ((R >> 2) & 1);
         }
     // Token operand (B): lane reads row 32 nj + lane%32, logical chunk
     // 2 ks + lane/32; rows 32 nj + l and l share swz_x, so one offset serves
@@ -309,9 +329,10 @@ __global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_ke
     // re-read the last stage (into buffers never computed on), so the number
     // of loads per stage stays fixed.
     const int KT = K / BK;
-    constexpr int PER_STAGE = 2 * XJ;  // global_load_lds per wavefront per stage
+    constexpr int PER_STAGE = XJ + WJ; // global_load_lds per wavefront per stage
     auto wait_stage = [] {
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(PER_STAGE, 0));
+        // four stages: one later stage may still be in flight; three: none
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(NS == 4 ? PER_STAGE : 0, 0));
         __builtin_amdgcn_s_barrier();
     };
     auto step = [&](Frags& fc, Frags& fn, const char* nxt, char* dma, int kl) {
@@ -322,12 +343,13 @@ __global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_ke
         mfmas(fc);
         // A wavefront issues in order and stalls on a load or LDS read while
         // that pipe is backed up, so bursts of either would idle its MFMAs.
-        // Eight wavefronts (16 MFMAs, 4 loads, 16 reads each per step): one
-        // load per 4 MFMAs over the whole step, a read after every MFMA (the
+        // Half tiles (16 MFMAs, 6 loads, 16 reads per step): the loads one per
+        // MFMA over the first half of the step, so the only stage in flight
+        // lands before the next step's wait.  Eight wavefronts (16 MFMAs, 4
+        // loads, 16 reads): one load per 4 MFMAs over the whole step (the
         // front-loaded and the compiler's own orders measured 1-4% slower).
-        // Four (dh: 32 MFMAs, 8 loads, 24 reads): the loads one per 2 MFMAs
-        // in the first half of the step, so they land well before the next
-        // step's wait.
+        // dh (32 MFMAs, 8 loads, 24 reads): one load per 2 MFMAs in the
+        // first half of the step.
         if constexpr (NW == 8) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -336,6 +358,28 @@ __global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_ke
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        } else if constexpr (HALF) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -362,24 +406,45 @@ __global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_ke
     Frags fa, fb;
     issue(0, st0);
     issue(min(1, KT - 1), st1);
-    issue(min(2, KT - 1), st2);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * PER_STAGE, 15));   // stage 0 landed
+    if constexpr (NS == 4) issue(min(2, KT - 1), st2);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * PER_STAGE, 15));   // stage 0 landed
     __builtin_amdgcn_s_barrier();
     fence();
     read_frags(st0, fa);
     fence();
     int kt = 0;
-    for (; kt + 4 <= KT; kt += 4) {
-        step(fa, fb, st1, st3, min(kt + 3, KT - 1));
-        step(fb, fa, st2, st0, min(kt + 4, KT - 1));
-        step(fa, fb, st3, st1, min(kt + 5, KT - 1));
-        step(fb, fa, st0, st2, min(kt + 6, KT - 1));
-    }
-    if (kt < KT) {
-        step(fa, fb, st1, st3, KT - 1);
-        if (kt + 1 < KT) {
-            step(fb, fa, st2, st0, KT - 1);
-            if (kt + 2 < KT) step(fa, fb, st3, st1, KT - 1);
+    if constexpr (NS == 4) {
+        // stage s in buffer s % 4; step s issues stage s + 3
+        for (; kt + 4 <= KT; kt += 4) {
+            step(fa, fb, st1, st3, min(kt + 3, KT - 1));
+            step(fb, fa, st2, st0, min(kt + 4, KT - 1));
+            step(fa, fb, st3, st1, min(kt + 5, KT - 1));
+            step(fb, fa, st0, st2, min(kt + 6, KT - 1));
+        }
+        if (kt < KT) {
+            step(fa, fb, st1, st3, KT - 1);
+            if (kt + 1 < KT) {
+                step(fb, fa, st2, st0, KT - 1);
+                if (kt + 2 < KT) step(fa, fb, st3, st1, KT - 1);
+            }
+        }
+    } else {
+        // stage s in buffer s % 3; step s issues stage s + 2.  The operand
+        // registers alternate with period 2 and the buffers with period 3, so
+        // after three steps the next stage's operands are in fb: swap.
+        for (; kt + 3 <= KT; kt += 3) {
+            step(fa, fb, st1, st2, min(kt + 2, KT - 1));
+            step(fb, fa, st2, st0, min(kt + 3, KT - 1));
+            step(fa, fb, st0, st1, min(kt + 4, KT - 1));
+            Frags t = fa;
+            fa = fb;
+            fb = t;
+        }
+        // at most two steps left (stage kt in st0); every stage they need is
+        // already in flight, their own loads re-read the last stage
+        if (kt < KT) {
+            step(fa, fb, st1, st2, KT - 1);
+            if (kt + 1 < KT) step(fb, fa, st2, st0, KT - 1);
         }
     }
     wait_vmem();
@@ -390,10 +455,10 @@ __global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_ke
     // element v of lane l: token 32 NJ rw + 32 nj + l%32, MFMA feature
     // 64 fw + 32 mi + 8 (v/4) + 4 (l/32) + v%4.  Up: h column 32 fw + the
     // feature's offset in its 32-block (g in mi = 0, u in mi = 1); down:
-    // output column = MFMA feature.  Tile rows 64 q .. 64 q + 63 are staged in
-    // stage buffer q, 16-byte chunks XOR-swizzled by the row's low 4 bits.
+    // output column = MFMA feature.  The tile's rows are staged RPS to a
+    // stage buffer, 16-byte chunks XOR-swizzled by the row's low 4 bits.
     if constexpr (MODE == M_DH) {
-        static_assert(NW == 4, "the dh epilogue lays out one wavefront per 64 columns of 256 rows");
+        static_assert(!HALF && NW == 4, "the dh epilogue lays out one wavefront per 64 columns of all 256 rows");
         // Element v of acc[mi][nj] on lane l: token 32 nj + l%32, column
         // nt*256 + 64 w + 32 mi + 8 (v/4) + 4 (l/32) + v%4; each lane handles
         // four consecutive columns at a time.  The wavefront's 64 columns are
@@ -561,10 +626,12 @@ __global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_ke
     constexpr int OCOLS = MODE == M_UP ? TF / 2 : TF;   // output columns of the tile
     constexpr int OROW = OCOLS * 2;             // bytes per staged row
     constexpr int OCH = OROW / 16;              // 16-byte chunks per row
-    static_assert(64 * OROW <= STAGE_BYTES, "a stage buffer holds 64 staged rows");
+    constexpr int RPS = SBYTES / OROW;         // staged rows per stage buffer
+    static_assert(RPS % 16 == 0 && NS * RPS >= ROWS, "the stage buffers hold the staged tile");
     auto orow = [&](int r) -> char* {
-        char* b = r < 64 ? st0 : r < 128 ? st1 : r < 192 ? st2 : st3;
-        return b + (r & 63) * OROW;
+        const int q = r / RPS;
+        char* b = q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3;
+        return b + (r - q * RPS) * OROW;
     };
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // this wavefront's loads and LDS reads done
     __syncthreads();                                // ... and every other wavefront's
@@ -620,7 +687,7 @@ __global__ __launch_bounds__(64 * waves_of<MODE>(), 1) void grouped_gemm_bf16_ke
     const int ldo = MODE == M_GU ? 2 * N : N;
     const bool col_ok = MODE == M_GU ? nt * 128 + 8 * (c & 15) < N : col < N;
 #pragma unroll 4
-    for (int r = tid / OCH; r < TT; r += ROWS_PER_PASS) {
+    for (int r = tid / OCH; r < ROWS; r += ROWS_PER_PASS) {
         if (r >= valid_rows) break;
         const u32x4_t v = *(const u32x4_t*)(orow(r) + ((c ^ (r & 15)) << 4));
         if (col_ok) *(u32x4_t*)((uint16_t*)a.out + (tile_r0 + r) * (int64_t)ldo + col) = v;
@@ -637,6 +704,10 @@ int column_groups(int n_tiles, int K) {
     return 1;
 }
 
+// Whether the up GEMM runs on half tiles: when its grid of whole tiles
+// (an upper bound, known on the host) is under six rounds of 256 CUs.
+bool up_half_tiles(int64_t tiles) { return tiles < 6 * 256; }
+
 int m_tiles_upper(const GroupArgs& g) {
     const int64_t rows = g.S + (g.G > g.E ? g.T : 0);
     return (int)((rows + TT - 1) / TT) + g.G;
@@ -650,8 +721,11 @@ hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* 
     GemmArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, h, D, F, (F + TF / 2 - 1) / (TF / 2)};
     a.col_groups = column_groups(a.n_tiles, D);
-    const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<M_UP><<<grid_for_work(blocks), 64 * waves_of<M_UP>(), 0, s>>>(a);
+    const int64_t tiles = (int64_t)m_tiles_upper(g) * a.n_tiles;
+    if (up_half_tiles(tiles))
+        grouped_gemm_bf16_kernel<M_UP, true><<<grid_for_work(2 * tiles), 64 * waves_of<M_UP, true>(), 0, s>>>(a);
+    else
+        grouped_gemm_bf16_kernel<M_UP, false><<<grid_for_work(tiles), 64 * waves_of<M_UP, false>(), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -661,7 +735,7 @@ hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, c
                Y, D, F, (D + TF - 1) / TF};
     a.col_groups = column_groups(a.n_tiles, F);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<M_DOWN><<<grid_for_work(blocks), 64 * waves_of<M_DOWN>(), 0, s>>>(a);
+    grouped_gemm_bf16_kernel<M_DOWN, false><<<grid_for_work(blocks), 64 * waves_of<M_DOWN, false>(), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -672,7 +746,7 @@ hipError_t launch_bwd_gate_up_bf16(const GroupArgs& g, const void* x, const void
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, gu, D, F, (F + TF / 2 - 1) / (TF / 2)};
     a.col_groups = column_groups(a.n_tiles, D);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<M_GU><<<grid_for_work(blocks), 64 * waves_of<M_GU>(), 0, s>>>(a);
+    grouped_gemm_bf16_kernel<M_GU, false><<<grid_for_work(blocks), 64 * waves_of<M_GU, false>(), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -683,7 +757,7 @@ hipError_t launch_bwd_dh_bf16(const GroupArgs& g, const float* topk_w, const voi
                dgu, D, F, (F + TF - 1) / TF, 1, topk_w, (const uint16_t*)gu, (uint16_t*)hw, dwpart};
     a.col_groups = column_groups(a.n_tiles, D);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<M_DH><<<grid_for_work(blocks), 64 * waves_of<M_DH>(), 0, s>>>(a);
+    grouped_gemm_bf16_kernel<M_DH, false><<<grid_for_work(blocks), 64 * waves_of<M_DH, false>(), 0, s>>>(a);
     return hipGetLastError();
 }
 
