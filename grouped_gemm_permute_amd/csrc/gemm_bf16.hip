@@ -104,7 +104,7 @@ enum : int {
 //    epilogue and the prologue of one overlap the other's MFMAs and the
 //    last round is finer.  It stages 1.5x the bytes per MFMA: the up GEMM
 //    takes it when its whole-tile grid is short (up_half_tiles), where it
-//    measured 4-9% faster; on long grids it is even to 1% slower, and for
+//    measured 3-9% faster; on long grids it is even to 1% slower, and for
 //    gate/up and down 4-10% slower;
 //  * dh: 4 wavefronts on a whole tile, its epilogue using all the LDS.
 template <int MODE, bool HALF>
@@ -705,8 +705,10 @@ int column_groups(int n_tiles, int K) {
 }
 
 // Whether the up GEMM runs on half tiles: when its grid of whole tiles
-// (an upper bound, known on the host) is under six rounds of 256 CUs.
-bool up_half_tiles(int64_t tiles) { return tiles < 6 * 256; }
+// (an upper bound, known on the host) is under twelve rounds of 256 CUs.
+// Measured (D = 768, F = 1536, E = 8): half tiles 3-9% faster at 4096 to
+// 16384 tokens (2.4 to 9.4 rounds), even to 1% slower at 32768 (18 rounds).
+bool up_half_tiles(int64_t tiles) { return tiles < 12 * 256; }
 
 int m_tiles_upper(const GroupArgs& g) {
     const int64_t rows = g.S + (g.G > g.E ? g.T : 0);
