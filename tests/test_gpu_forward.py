@@ -57,6 +57,9 @@ FULL_CASES = [
     # more than 64 groups: the tile -> group lookup spans several 64-group blocks
     (3000, 128, 192, 100, 4, True, "bf16", "zipf"),      # small-chunk kernels, many empty experts
     (20000, 64, 128, 70, 2, True, "bf16", "uniform"),    # 256-row engine
+    # over twelve rounds of up tiles: whole 256-row tiles, two column groups
+    # (12 x 448 x 256 weights per XCD outgrow its L2 share), D tail of 192
+    (24000, 448, 1536, 8, 2, True, "bf16", "zipf"),
     (2000, 64, 128, 1024, 8, True, "bf16", "uniform"),   # the expert limit (1025 groups)
     # wide D and F with a 64-column tail (F = 10 * 256 + 64)
     (96, 2048, 2624, 3, 2, True, "bf16", "uniform"),     # small-chunk kernels
