@@ -145,10 +145,29 @@ def load_traffic(workload_name, key, small=False):
     return rec.get("bytes_per_launch")
 
 
+def host_cpu():
+    """The host's core counts and CPU model, and the oracle's thread count:
+    the cores this process may run on, capped at 16 (one GPU's share of the
+    GPU machine's host)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0))
+    return {"threads": max(1, min(16, affinity)), "nproc": os.cpu_count(), "affinity": affinity,
+            "cpu_model": model}
+
+
 def cpu_baseline(inp, w, target_s):
     import numpy as np
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    host = host_cpu()
+    threads = host["threads"]
     shared = (inp["Ws1"], inp["Ws3"], inp["Ws2"]) if w.shared else None
     W = [np.ascontiguousarray(inp[n], np.float64) for n in ("W1", "W3", "W2")]
     sh = tuple(np.ascontiguousarray(a, np.float64) for a in shared) if shared else None
@@ -165,7 +184,8 @@ def cpu_baseline(inp, w, target_s):
     t = run(n)
     flop = 6 * w.D * w.F * (n * w.k + (n if w.shared else 0))
     return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": round(t, 3),
+            "seconds": round(t, 3), "host_nproc": host["nproc"], "host_affinity_cores": host["affinity"],
+            "cpu_model": host["cpu_model"],
             "sample": f"first {n} of {w.T} tokens of the same workload (same weights and routing), "
                       f"fp64 permuted oracle path, {threads} threads"}
 
@@ -192,7 +212,8 @@ def bwd_stage_work(w, counts):
 def bwd_cpu_baseline(inp, w, target_s):
     import numpy as np
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    host = host_cpu()
+    threads = host["threads"]
     sh = (inp["Ws1"], inp["Ws3"], inp["Ws2"]) if w.shared else None
 
     def run(n):
@@ -207,7 +228,8 @@ def bwd_cpu_baseline(inp, w, target_s):
     t = run(n)
     flop = 16 * w.D * w.F * (n * w.k + (n if w.shared else 0))
     return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": round(t, 3),
+            "seconds": round(t, 3), "host_nproc": host["nproc"], "host_affinity_cores": host["affinity"],
+            "cpu_model": host["cpu_model"],
             "sample": f"first {n} of {w.T} tokens of the same workload (same weights, routing and dy), "
                       f"fp64 oracle backward, {threads} threads"}
 
@@ -373,6 +395,18 @@ def run_sweep(args):
     else:
         D, F = 1024, 4096
         points = [(D, F, t) for t in (64, 128, 256, 512, 1024, 2048)]
+    if args.sweep_point is not None:
+        # one point, one variant (for counter collection under rocprofv3)
+        D, F, t = points[args.sweep_point]
+        T = t * E // k
+        w = moe_inputs.Workload(f"sweep_{args.sweep}_T{T}_D{D}_F{F}_E{E}_top{k}", T, D, F, E, k, False,
+                                "bf16", "uniform")
+        ms = time_forward(w, args.variant, args.steps, args.warmup, args.rotate_bytes)
+        print(json.dumps({"sweep": args.sweep, "point": args.sweep_point, "workload": w.name,
+                          "T": T, "D": D, "F": F, "E": E, "k": k, "t_per_expert": t,
+                          "variant": args.variant, "ms": round(ms, 5),
+                          "tflops": round(6 * D * F * T * k / ms / 1e9, 1)}), flush=True)
+        return
     for D, F, t in points:
         T = t * E // k
         w = moe_inputs.Workload(f"sweep_{args.sweep}_T{T}_D{D}_F{F}_E{E}_top{k}", T, D, F, E, k, False,
@@ -410,6 +444,187 @@ def copy_calibration(nbytes, steps):
                       "gbs_read_plus_write": round(2 * n * 4 / dt / 1e9, 1)}), flush=True)
 
 
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "mean": round(float(a.mean()), 5)}
+
+
+def measure_forward(wid, variant="unfused", steps=50, warmup=10, rotate_bytes=512e6, routed=False):
+    """Time moe_ffn_forward (or the routed forward) on workload wid with its
+    inputs resident in HBM and rotated over enough copies to exceed the
+    on-die caches.
+
+    Region 1: `steps` plain calls between two synchronisations (host clock:
+    ms_per_step), with one event between consecutive calls on the stream the
+    kernels run on (per-call distribution) and an engine-clock sample on
+    each side.  Region 2: the same calls with HIP events recorded between the
+    kernels (moe_ffn_forward_timed) for per-kernel durations; each record
+    costs a few microseconds of GPU time, so whole-call figures come from
+    region 1 only."""
+    import numpy as np
+    import torch
+
+    import grouped_gemm_permute_amd as gg
+    import moe_inputs
+
+    w = moe_inputs.WORKLOADS[wid]
+    log(f"workload {w.name}: drawing inputs")
+    inp = moe_inputs.make_inputs(wid)
+    if routed:
+        moe_inputs.add_router(inp)
+    counts = np.bincount(inp["topk_idx"].reshape(-1), minlength=w.E)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(inp[name]).cuda()
+
+    base = {n: dev(n) for n in ("x", "W1", "W3", "W2")}
+    if w.shared:
+        base.update({n: dev(n) for n in ("Ws1", "Ws3", "Ws2")})
+    base["idx"] = torch.from_numpy(inp["topk_idx"]).cuda()
+    base["w"] = torch.from_numpy(inp["topk_w"]).cuda()
+    if routed:
+        base["gate_w"] = dev("gate_w")
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    R = max(2, math.ceil(rotate_bytes / set_bytes))
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(R - 1)]
+    ws = gg.alloc_workspace(w.T, w.D, w.F, w.E, w.k, w.shared, dt, variant)
+    y = torch.empty((w.T, w.D), dtype=dt, device="cuda")
+    log(f"{R} rotated input sets of {set_bytes / 1e6:.1f} MB; workspace {ws.numel() / 1e6:.1f} MB")
+
+    def step(i, events=None):
+        s = sets[i % R]
+        sh = (s["Ws1"], s["Ws3"], s["Ws2"]) if w.shared else None
+        if routed:
+            gg.forward_routed(s["x"], s["gate_w"], s["W1"], s["W3"], s["W2"], sh, k=w.k, y=y,
+                              variant=variant, workspace=ws, events=events)
+            return
+        gg.forward(s["x"], s["idx"], s["w"], s["W1"], s["W3"], s["W2"], sh, y=y, variant=variant,
+                   workspace=ws, events=events)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {warmup} steps done")
+
+    # Region 1
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    clk0 = gg.device_clock_sample()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        marks[i].record()
+        step(i)
+    marks[steps].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    clk1 = gg.device_clock_sample()
+    torch.cuda.synchronize()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    per_call = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
+    clocks = gg.engine_clock_ghz(clk0.cpu(), clk1.cpu())
+
+    # Region 2
+    hip = HipEvents()
+    evs = [hip.create(5) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    stage_samples = {st: [hip.elapsed_ms(e[j], e[j + 1]) for e in evs] for j, st in enumerate(STAGES)}
+    for e in evs:
+        hip.destroy(e)
+    if routed:
+        sidx, _ = gg.router_topk(sets[0]["x"], sets[0]["gate_w"], w.k)
+        counts = np.bincount(sidx.cpu().numpy().reshape(-1), minlength=w.E)
+    small = bool(gg.workspace_layout(w.T, w.D, w.F, w.E, w.k, w.shared, dt, variant)["small_tiles"])
+    log(f"timed {steps} steps of {w.name}: {ms_per_step:.4f} ms/step (host clock), per-call "
+        f"median {np.median(per_call):.4f} ms; stage means "
+        f"{ {k: round(float(np.mean(v)), 4) for k, v in stage_samples.items()} }")
+    del sets, ws, y
+    torch.cuda.empty_cache()
+    return {"w": w, "inp": inp, "counts": counts, "R": R, "ms_per_step": ms_per_step,
+            "per_call": per_call, "stage_samples": stage_samples, "clocks": clocks, "small": small}
+
+
+def dominant_roofline(m, variant):
+    """The dominant kernel's algorithmic work over its mean event-timed launch
+    duration, against the MFMA or HBM peak by its arithmetic intensity."""
+    import numpy as np
+    w, counts = m["w"], m["counts"]
+    stage_ms = {st: float(np.mean(v)) for st, v in m["stage_samples"].items()}
+    work = stage_work(w, counts)
+    if variant == "fused":             # one kernel does up, SwiGLU and down
+        b = 2 if w.dtype == "bf16" else 4
+        groups = int(sum(1 for c in counts if c > 0)) + (1 if w.shared else 0)
+        work["up_swiglu"]["flop"] += work["down"]["flop"]
+        work["up_swiglu"]["bytes"] = (w.T * w.D * b + 3 * w.D * w.F * b * groups
+                                      + (w.T * w.k + (w.T if w.shared else 0)) * w.D * b)
+        kernels = ("up_swiglu",)
+    else:
+        kernels = ("up_swiglu", "down")
+    dom = max(kernels, key=lambda s: stage_ms[s])
+    sec = stage_ms[dom] * 1e-3
+    mfma_bound = work[dom]["flop"] / work[dom]["bytes"] > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3
+    if mfma_bound:
+        ach = work[dom]["flop"] / sec / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    else:
+        ach = work[dom]["bytes"] / sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = load_traffic(w.name, f"{variant}:{dom}", m["small"])
+    roof["kernel"] = "fused_up_act_down" if variant == "fused" else dom
+    roof["launch_ms"] = round(stage_ms[dom], 5)
+    roof["launch_ms_median"] = round(float(np.median(m["stage_samples"][dom])), 5)
+    roof["algorithmic"] = work[dom]["flop"] if mfma_bound else work[dom]["bytes"]
+    return roof, stage_ms
+
+
+def clock_record(m, value_tflops):
+    """Mean engine clock over the timed region (per XCD) and the bf16 MFMA
+    peak at that clock: compute units x clock x 4096 dense bf16 FLOPs per CU
+    per cycle (2.5 PFLOP/s at 256 CUs and 2.4 GHz)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    c = m["clocks"]
+    if not c:
+        return {"compute_units": cus, "sclk_ghz_mean": None}
+    mean = sum(c.values()) / len(c)
+    peak = cus * mean * 1e9 * 4096 / 1e12
+    return {"compute_units": cus, "sclk_ghz_mean": round(mean, 4),
+            "sclk_ghz_per_xcd": {str(k): round(v, 4) for k, v in sorted(c.items())},
+            "peak_bf16_tflops_at_measured_clock": round(peak, 1),
+            "frac_of_peak_at_measured_clock": round(value_tflops / peak, 4),
+            "peak_bf16_tflops_at_2p4ghz": round(cus * 2.4 * 4096, 1)}
+
+
+def small_chunk_record(args):
+    """The small-chunk workload (512 tokens, 8 experts of ~128 rows) in the
+    same run: it is bound by streaming the experts' weights, so it is priced
+    in HBM bytes (x, y, routing and the weights of every active expert) per
+    forward, against 8 TB/s."""
+    import numpy as np
+    m = measure_forward(3, "unfused", steps=max(args.steps, 200), warmup=max(args.warmup, 20),
+                        rotate_bytes=args.rotate_bytes)
+    w, counts = m["w"], m["counts"]
+    nbytes = path_bytes(w, counts)
+    pc = percentiles(m["per_call"])
+    roof, stage_ms = dominant_roofline(m, "unfused")
+    gbs = nbytes / (pc["median"] * 1e-3) / 1e9
+    return {"workload": w.name, "T": w.T, "D": w.D, "F": w.F, "E": w.E, "k": w.k,
+            "steps": max(args.steps, 200), "rotated_sets": m["R"],
+            "ms_per_call": pc, "ms_per_step_host_clock": round(m["ms_per_step"], 5),
+            "bytes_alg": nbytes, "gbs": round(gbs, 1), "frac_of_8tbs": round(gbs / PEAK_HBM_GBS, 4),
+            "stage_ms_mean_with_events": {k: round(v, 5) for k, v in stage_ms.items()},
+            "dominant": roof}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,6 +636,8 @@ def main():
                     help="target length of the CPU-oracle baseline sample; 0 skips it")
     ap.add_argument("--rotate-bytes", type=float, default=512e6,
                     help="rotate input copies until their total exceeds this many bytes")
+    ap.add_argument("--no-small-chunk", action="store_true",
+                    help="skip the same-run small-chunk (512-token) record")
     ap.add_argument("--backward", action="store_true",
                     help="time moe_ffn_backward (dx, weight gradients, dtopk_w) instead of the forward")
     ap.add_argument("--routed", action="store_true",
@@ -429,6 +646,9 @@ def main():
     ap.add_argument("--sweep", choices=("fd", "t"), default=None,
                     help="fused vs unfused forward over F/D at fixed tokens per expert (fd) or over "
                          "tokens per expert at fixed F/D (t); one JSON line per point")
+    ap.add_argument("--sweep-point", type=int, default=None,
+                    help="with --sweep: run only this point (index) and variant --variant, for "
+                         "counter collection under rocprofv3")
     ap.add_argument("--copy-bytes", type=float, default=0,
                     help="only run a plain device-to-device copy of this many bytes --steps times "
                          "(the reference kernel for scaling HBM byte counters); prints its timing")
@@ -447,115 +667,23 @@ def main():
         run_sweep(args)
         return
 
-    import numpy as np
     import torch
 
-    import grouped_gemm_permute_amd as gg
     import moe_inputs
-
-    w = moe_inputs.WORKLOADS[args.workload]
-    log(f"workload {w.name}: drawing inputs")
-    inp = moe_inputs.make_inputs(args.workload)
-    if args.routed:
-        moe_inputs.add_router(inp)
-    counts = np.bincount(inp["topk_idx"].reshape(-1), minlength=w.E)
     torch.cuda.set_device(0)
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-
-    def dev(name):
-        if w.dtype == "bf16":
-            return torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(inp[name]).cuda()
-
-    base = {n: dev(n) for n in ("x", "W1", "W3", "W2")}
-    if w.shared:
-        base.update({n: dev(n) for n in ("Ws1", "Ws3", "Ws2")})
-    base["idx"] = torch.from_numpy(inp["topk_idx"]).cuda()
-    base["w"] = torch.from_numpy(inp["topk_w"]).cuda()
-    if args.routed:
-        base["gate_w"] = dev("gate_w")
-    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
-    R = max(2, math.ceil(args.rotate_bytes / set_bytes))
-    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(R - 1)]
-    ws = gg.alloc_workspace(w.T, w.D, w.F, w.E, w.k, w.shared, dt, args.variant)
-    y = torch.empty((w.T, w.D), dtype=dt, device="cuda")
-    log(f"{R} rotated input sets of {set_bytes / 1e6:.1f} MB; workspace {ws.numel() / 1e6:.1f} MB")
-
-    def step(i, events=None):
-        s = sets[i % R]
-        sh = (s["Ws1"], s["Ws3"], s["Ws2"]) if w.shared else None
-        if args.routed:
-            _, ridx, _ = gg.forward_routed(s["x"], s["gate_w"], s["W1"], s["W3"], s["W2"], sh, k=w.k,
-                                           y=y, variant=args.variant, workspace=ws, events=events)
-            return
-        gg.forward(s["x"], s["idx"], s["w"], s["W1"], s["W3"], s["W2"], sh, y=y,
-                   variant=args.variant, workspace=ws, events=events)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
-
-    # Timed region 1: K plain forward calls, synchronized on both sides.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # Timed region 2: the same K calls with HIP events recorded on the stream
-    # between the kernels (moe_ffn_forward_timed); each record costs a few
-    # microseconds of GPU time, so only per-kernel durations come from here.
-    hip = HipEvents()
-    evs = [hip.create(5) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    stage_ms = {st: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs]))
-                for j, st in enumerate(STAGES)}
-    fwd_ms = float(np.mean([hip.elapsed_ms(e[0], e[4]) for e in evs]))
-    for e in evs:
-        hip.destroy(e)
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (host clock, no events), "
-        f"{fwd_ms:.4f} ms/step with per-kernel events; stages {stage_ms}")
-
-    if args.routed:
-        # the routing comes from the router; count what it chose
-        sidx, _ = gg.router_topk(sets[0]["x"], sets[0]["gate_w"], w.k)
-        counts = np.bincount(sidx.cpu().numpy().reshape(-1), minlength=w.E)
-    flop = w.flops()
-    value = flop / (ms_per_step * 1e-3) / 1e12
-    work = stage_work(w, counts)
-    if args.variant == "fused":       # one kernel does up, SwiGLU and down
+    m = measure_forward(args.workload, args.variant, args.steps, args.warmup, args.rotate_bytes,
+                        args.routed)
+    w, inp, counts = m["w"], m["inp"], m["counts"]
+    value = w.flops() / (m["ms_per_step"] * 1e-3) / 1e12
+    roof, stage_ms = dominant_roofline(m, args.variant)
+    if args.variant == "fused":
         stage_ms.pop("down")           # an empty interval between two back-to-back events
-        work["up_swiglu"]["flop"] += work["down"]["flop"]
-        work["up_swiglu"]["bytes"] = (w.T * w.D * (2 if w.dtype == "bf16" else 4)
-                                      + 3 * w.D * w.F * (2 if w.dtype == "bf16" else 4)
-                                      * (int(sum(1 for c in counts if c > 0)) + (1 if w.shared else 0))
-                                      + (w.T * w.k + (w.T if w.shared else 0)) * w.D * 2)
-        stage_ms["down"] = 0.0
-        kernels = ("up_swiglu",)
-    else:
-        kernels = ("up_swiglu", "down")
-    dom = max(kernels, key=lambda s: stage_ms[s])
-    sec = stage_ms[dom] * 1e-3
-    mfma_bound = work[dom]["flop"] / work[dom]["bytes"] > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3
-    if mfma_bound:
-        ach = work[dom]["flop"] / sec / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-    else:
-        ach = work[dom]["bytes"] / sec / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4)}
-    small = bool(gg.workspace_layout(w.T, w.D, w.F, w.E, w.k, w.shared, dt,
-                                     args.variant)["small_tiles"])
-    roof["traffic"] = load_traffic(w.name, f"{args.variant}:{dom}", small)
-    roof["kernel"] = "fused_up_act_down" if args.variant == "fused" else dom
-    roof["launch_ms"] = round(stage_ms[dom], 5)
-    roof["algorithmic"] = work[dom]["flop"] if mfma_bound else work[dom]["bytes"]
+    pc = percentiles(m["per_call"])
+
+    small = None
+    if args.workload == 2 and args.variant == "unfused" and not args.routed and not args.no_small_chunk:
+        log("same-run small-chunk record")
+        small = small_chunk_record(args)
 
     cpu = None
     if args.cpu_seconds > 0 and not args.routed:
@@ -567,18 +695,24 @@ def main():
     out = {
         "metric": METRIC + (" (routed: router feeding the permute)" if args.routed else ""),
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(m["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "D": w.D, "F": w.F, "E": w.E, "k": w.k,
                    "shared_expert": w.shared, "routing": "router" if args.routed else w.routing,
-                   "variant": args.variant, "rotated_sets": R},
+                   "variant": args.variant, "rotated_sets": m["R"]},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "hbm_gbs_path": round(path_bytes(w, counts) / (ms_per_step * 1e-3) / 1e9, 1),
+        "ms_per_call": pc,
+        "tflops_at_median_call": round(w.flops() / (pc["median"] * 1e-3) / 1e12, 3),
+        "clock": clock_record(m, value),
+        "hbm_gbs_path": round(path_bytes(w, counts) / (m["ms_per_step"] * 1e-3) / 1e9, 1),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "stage_ms_median": {k: round(float(percentiles(v)["median"]), 5)
+                            for k, v in m["stage_samples"].items() if k in stage_ms},
         "expert_rows": counts.tolist(),
         "input_sha256": moe_inputs.input_digest(inp),
         "roofline": roof,
+        "small_chunk": small,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -26,7 +26,7 @@ EXPORTS = (
     "moe_ffn_forward", "moe_ffn_forward_timed", "moe_expert_permute", "moe_expert_permute_scratch_size",
     "moe_ffn_get_device_error", "moe_ffn_backward_workspace_layout", "moe_ffn_backward_workspace_size",
     "moe_ffn_backward", "moe_ffn_backward_timed", "moe_router_topk", "moe_ffn_forward_routed",
-    "moe_ffn_forward_routed_timed",
+    "moe_ffn_forward_routed_timed", "moe_device_clock_sample",
 )
 
 
@@ -102,6 +102,8 @@ def lib():
         L.moe_ffn_forward_routed.argtypes = routed
         L.moe_ffn_forward_routed_timed.restype = ci
         L.moe_ffn_forward_routed_timed.argtypes = routed + [P]
+        L.moe_device_clock_sample.restype = ci
+        L.moe_device_clock_sample.argtypes = [P, ci, P]
         L.moe_ffn_get_device_error.restype = ci
         L.moe_ffn_get_device_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32)]
         _lib = L
@@ -131,6 +133,71 @@ def _variant_enum(v: str) -> int:
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
+
+
+def _same_device(ref, named):
+    """Every tensor must live on ref's device, which must be a GPU: the C ABI
+    takes raw device pointers and cannot tell a host pointer from one."""
+    if ref.device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {ref.device}")
+    for name, t in named.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _expect(name, t, shape, dtype):
+    if t.shape != shape:
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_layer(x, W1, W3, W2, shared, y):
+    """Shapes, dtypes, contiguity and device of the layer's tensors; returns
+    (T, D, F, E).  Weights and y take x's dtype, so the library's element
+    size matches every buffer it touches."""
+    _dtype_enum(x.dtype)
+    if x.dim() != 2 or W1.dim() != 3:
+        raise ValueError("x must be [T,D] and W1 [E,D,F]")
+    T, D = x.shape
+    E, _, F = W1.shape
+    _expect("x", x, (T, D), x.dtype)
+    _expect("W1", W1, (E, D, F), x.dtype)
+    _expect("W3", W3, (E, D, F), x.dtype)
+    _expect("W2", W2, (E, F, D), x.dtype)
+    if shared is not None:
+        if len(shared) != 3:
+            raise ValueError("shared must be (Ws1, Ws3, Ws2)")
+        _expect("Ws1", shared[0], (D, F), x.dtype)
+        _expect("Ws3", shared[1], (D, F), x.dtype)
+        _expect("Ws2", shared[2], (F, D), x.dtype)
+    if y is not None:
+        _expect("y", y, (T, D), x.dtype)
+    return T, D, F, E
+
+
+def _layer_tensors(W1, W3, W2, shared, y):
+    sh = dict(zip(("Ws1", "Ws3", "Ws2"), shared)) if shared is not None else {}
+    return dict(W1=W1, W3=W3, W2=W2, y=y, **sh)
+
+
+def _check_routing(x, topk_idx, topk_w, T):
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T,k]")
+    k = topk_idx.shape[1]
+    _expect("topk_idx", topk_idx, (T, k), torch.int32)
+    _expect("topk_w", topk_w, (T, k), torch.float32)
+    return k
+
+
+def _check_workspace(x, workspace, need):
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor")
+    _same_device(x, dict(workspace=workspace))
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
 
 
 def _stream(stream):
@@ -167,28 +234,16 @@ def forward(x, topk_idx, topk_w, W1, W3, W2, shared=None, y=None, variant="unfus
     Tensors must be contiguous and on the current device.  ``events``: a
     ctypes array of five hipEvent_t handles to route the call through
     moe_ffn_forward_timed."""
-    if topk_idx.dtype != torch.int32:
-        raise TypeError("topk_idx must be int32")
-    if topk_w.dtype != torch.float32:
-        raise TypeError("topk_w must be float32")
-    for t in (x, topk_idx, topk_w, W1, W3, W2, *(shared or ())):
-        if not t.is_contiguous():
-            raise ValueError("all tensors must be contiguous")
-    T, D = x.shape
-    E, _, F = W1.shape
-    k = topk_idx.shape[1]
-    if W1.shape != (E, D, F) or W3.shape != (E, D, F) or W2.shape != (E, F, D):
-        raise ValueError("weight shapes must be W1/W3 [E,D,F], W2 [E,F,D]")
-    if topk_idx.shape != (T, k) or topk_w.shape != (T, k):
-        raise ValueError("topk_idx / topk_w must be [T,k]")
+    T, D, F, E = _check_layer(x, W1, W3, W2, shared, y)
+    k = _check_routing(x, topk_idx, topk_w, T)
+    _same_device(x, dict(topk_idx=topk_idx, topk_w=topk_w, **_layer_tensors(W1, W3, W2, shared, y)))
     Ws1, Ws3, Ws2 = shared if shared is not None else (None, None, None)
-    if shared is not None and (Ws1.shape != (D, F) or Ws3.shape != (D, F) or Ws2.shape != (F, D)):
-        raise ValueError("shared weights must be [D,F], [D,F], [F,D]")
     dt = _dtype_enum(x.dtype)
     if y is None:
         y = torch.empty((T, D), dtype=x.dtype, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(T, D, F, E, k, shared is not None, x.dtype, variant, x.device)
+    _check_workspace(x, workspace, workspace_size(T, D, F, E, k, shared is not None, x.dtype, variant))
     args = (_ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1),
             _ptr(Ws3), _ptr(Ws2), _ptr(y), T, D, F, E, k, dt, _variant_enum(variant),
             _ptr(workspace), workspace.numel(), _stream(stream))
@@ -202,9 +257,11 @@ def forward(x, topk_idx, topk_w, W1, W3, W2, shared=None, y=None, variant="unfus
 def expert_permute(topk_idx, E, tile_rows_=1, shared_rows=0, stream=None) -> dict:
     """Stable counting sort of the slots on the device; returns device int32
     tensors counts [E], offsets [E+1], tile_off [E+2], perm, inv [T*k], err [1]."""
-    if topk_idx.dtype != torch.int32 or not topk_idx.is_contiguous():
-        raise TypeError("topk_idx must be contiguous int32")
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T,k]")
     T, k = topk_idx.shape
+    _expect("topk_idx", topk_idx, (T, k), torch.int32)
+    _same_device(topk_idx, {})
     dev = topk_idx.device
     out = {n: torch.empty(sz, dtype=torch.int32, device=dev) for n, sz in
            (("counts", E), ("offsets", E + 1), ("tile_off", E + 2), ("perm", max(T * k, 1)),
@@ -228,6 +285,27 @@ def device_error(workspace, stream=None) -> int:
     return int(v.value)
 
 
+def device_clock_sample(blocks=64, stream=None):
+    """Issue a clock sample on the stream; returns the device int64 [blocks, 3]
+    tensor (XCD id, shader-clock cycles, 100 MHz counter) it will hold."""
+    out = torch.empty((blocks, 3), dtype=torch.int64, device="cuda")
+    _check(lib().moe_device_clock_sample(_ptr(out), blocks, _stream(stream)), "moe_device_clock_sample")
+    return out
+
+
+def engine_clock_ghz(before, after):
+    """Mean engine clock (GHz) of each XCD between two device_clock_sample
+    results (host copies), pairing the samples by XCD id."""
+    first = {}
+    for xcc, cyc, rt in before.tolist():
+        first.setdefault(xcc, (cyc, rt))
+    out = {}
+    for xcc, cyc, rt in after.tolist():
+        if xcc in first and xcc not in out and rt > first[xcc][1]:
+            out[xcc] = (cyc - first[xcc][0]) / (rt - first[xcc][1]) * 0.1
+    return out
+
+
 def backward_workspace_layout(T, D, F, E, k, has_shared, dtype) -> dict:
     L = BwdWsLayout()
     _check(lib().moe_ffn_backward_workspace_layout(T, D, F, E, k, int(has_shared), _dtype_enum(dtype),
@@ -243,18 +321,9 @@ def backward(x, topk_idx, topk_w, W1, W3, W2, shared, dy, out=None, workspace=No
     [D,F], dWs2 [F,D] (None without a shared expert) and dtopk_w [T,k], all
     fp32 except dx.  ``out`` may supply any of these tensors.  ``events``: a
     ctypes array of nine hipEvent_t handles (moe_ffn_backward_timed)."""
-    if topk_idx.dtype != torch.int32 or topk_w.dtype != torch.float32:
-        raise TypeError("topk_idx must be int32 and topk_w float32")
-    for t in (x, topk_idx, topk_w, W1, W3, W2, dy, *(shared or ())):
-        if not t.is_contiguous():
-            raise ValueError("all tensors must be contiguous")
-    T, D = x.shape
-    E, _, F = W1.shape
-    k = topk_idx.shape[1]
-    if dy.shape != (T, D) or dy.dtype != x.dtype:
-        raise ValueError("dy must be [T,D] with x's dtype")
-    if W1.shape != (E, D, F) or W3.shape != (E, D, F) or W2.shape != (E, F, D):
-        raise ValueError("weight shapes must be W1/W3 [E,D,F], W2 [E,F,D]")
+    T, D, F, E = _check_layer(x, W1, W3, W2, shared, None)
+    k = _check_routing(x, topk_idx, topk_w, T)
+    _expect("dy", dy, (T, D), x.dtype)
     dev = x.device
     f32 = dict(dtype=torch.float32, device=dev)
     o = dict(out or {})
@@ -269,10 +338,21 @@ def backward(x, topk_idx, topk_w, W1, W3, W2, shared, dy, out=None, workspace=No
         o.setdefault("dWs2", torch.empty((F, D), **f32))
     else:
         o["dWs1"] = o["dWs3"] = o["dWs2"] = None
+    shapes = dict(dx=((T, D), x.dtype), dW1=((E, D, F), torch.float32), dW3=((E, D, F), torch.float32),
+                  dW2=((E, F, D), torch.float32), dtopk_w=((T, k), torch.float32),
+                  dWs1=((D, F), torch.float32), dWs3=((D, F), torch.float32),
+                  dWs2=((F, D), torch.float32))
+    for name, (shape, dtype) in shapes.items():
+        if o.get(name) is not None:
+            _expect(name, o[name], shape, dtype)
+    _same_device(x, dict(topk_idx=topk_idx, topk_w=topk_w, dy=dy,
+                         **_layer_tensors(W1, W3, W2, shared, None),
+                         **{n: t for n, t in o.items() if n in shapes}))
     Ws1, Ws3, Ws2 = shared if shared is not None else (None, None, None)
+    n = backward_workspace_layout(T, D, F, E, k, shared is not None, x.dtype)["total"]
     if workspace is None:
-        n = backward_workspace_layout(T, D, F, E, k, shared is not None, x.dtype)["total"]
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    _check_workspace(x, workspace, n)
     args = (_ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1),
             _ptr(Ws3), _ptr(Ws2), _ptr(dy), _ptr(o["dx"]), _ptr(o["dW1"]), _ptr(o["dW3"]),
             _ptr(o["dW2"]), _ptr(o["dWs1"]), _ptr(o["dWs3"]), _ptr(o["dWs2"]), _ptr(o["dtopk_w"]),
@@ -287,10 +367,16 @@ def backward(x, topk_idx, topk_w, W1, W3, W2, shared, dy, out=None, workspace=No
 def router_topk(x, gate_w, k, stream=None):
     """moe_router_topk: (topk_idx int32 [T,k], topk_w fp32 [T,k]) for x [T,D]
     and gate_w [D,E] of x's dtype."""
-    if not (x.is_contiguous() and gate_w.is_contiguous()) or gate_w.dtype != x.dtype:
-        raise ValueError("x and gate_w must be contiguous and of one dtype")
+    _dtype_enum(x.dtype)
+    if x.dim() != 2 or gate_w.dim() != 2:
+        raise ValueError("x must be [T,D] and gate_w [D,E]")
     T, D = x.shape
     E = gate_w.shape[1]
+    _expect("x", x, (T, D), x.dtype)
+    _expect("gate_w", gate_w, (D, E), x.dtype)
+    _same_device(x, dict(gate_w=gate_w))
+    if not 1 <= k <= E:
+        raise ValueError(f"k must be in [1, E={E}], got {k}")
     idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     _check(lib().moe_router_topk(_ptr(x), _ptr(gate_w), T, D, E, k, _dtype_enum(x.dtype), _ptr(idx),
@@ -301,11 +387,11 @@ def router_topk(x, gate_w, k, stream=None):
 def forward_routed(x, gate_w, W1, W3, W2, shared=None, k=2, y=None, variant="unfused",
                    workspace=None, stream=None, events=None):
     """moe_ffn_forward_routed: returns (y, topk_idx, topk_w)."""
-    for t in (x, gate_w, W1, W3, W2, *(shared or ())):
-        if not t.is_contiguous():
-            raise ValueError("all tensors must be contiguous")
-    T, D = x.shape
-    E, _, F = W1.shape
+    T, D, F, E = _check_layer(x, W1, W3, W2, shared, y)
+    _expect("gate_w", gate_w, (D, E), x.dtype)
+    if not 1 <= k <= E:
+        raise ValueError(f"k must be in [1, E={E}], got {k}")
+    _same_device(x, dict(gate_w=gate_w, **_layer_tensors(W1, W3, W2, shared, y)))
     Ws1, Ws3, Ws2 = shared if shared is not None else (None, None, None)
     if y is None:
         y = torch.empty((T, D), dtype=x.dtype, device=x.device)
@@ -313,6 +399,7 @@ def forward_routed(x, gate_w, W1, W3, W2, shared=None, k=2, y=None, variant="unf
     w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(T, D, F, E, k, shared is not None, x.dtype, variant, x.device)
+    _check_workspace(x, workspace, workspace_size(T, D, F, E, k, shared is not None, x.dtype, variant))
     args = (_ptr(x), _ptr(gate_w), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1), _ptr(Ws3), _ptr(Ws2),
             _ptr(y), _ptr(idx), _ptr(w), T, D, F, E, k, _dtype_enum(x.dtype), _variant_enum(variant),
             _ptr(workspace), workspace.numel(), _stream(stream))

@@ -31,28 +31,33 @@
 //  The backward's dx rows are the down mode run with K = 2F over the
 //  transposed, stacked [W1^T ; W3^T] and A = dgu.
 //
-// Tile engine (256 threads = 4 wavefronts, one per SIMD of the CU):
+// Tile engine:
 //  * the MFMA computes the transposed tile C^T = W^T . X^T: its A operand is
 //    a 32-feature block of the weights, its B operand a 32-token block of
 //    rows, so each lane ends with 4 consecutive output features of one token
 //    and stores 8 bytes at a time;
 //  * row tiles of 256 tokens x 256 MFMA features (up: 128 W1 + 128 W3
-//    columns of the same 128 outputs); wavefront w owns features
-//    64 w .. 64 w + 63.  Up, gate_up and down: a workgroup takes one
-//    128-token half of a row tile (2 x 4 v_mfma_f32_32x32x16_bf16
-//    accumulators, 250 registers, 72 KiB of LDS), so two workgroups share a
-//    CU and each SIMD runs two wavefronts of different workgroups: one keeps
-//    the MFMA pipe fed while the other is in its prologue, its SiLU
-//    epilogue or held issuing a load into a busy memory pipe (up GEMM 2-9%
-//    faster than one 256-token workgroup of eight wavefronts per CU,
-//    measured; results bitwise identical).  dh: one workgroup per CU on
-//    the whole row tile (2 x 8 accumulators), its epilogue using all the
-//    LDS.  Spreading the wavefronts over the features rather than 2 x 2
-//    halves the slow transposed weight reads per MFMA;
+//    columns of the same 128 outputs), in one of three workgroup shapes
+//    (waves_of below), each chosen by interleaved A/Bs with bitwise-equal
+//    results:
+//      - whole tiles, 8 wavefronts (up on long grids, gate_up, down): two
+//        wavefronts per SIMD, wavefront w owning features 64 (w % 4) .. +63
+//        of rows 128 (w / 4) .. +127 (2 x 4 v_mfma_f32_32x32x16_bf16
+//        accumulators), one workgroup per CU and a ring of four 32 KiB
+//        stages; one wavefront's MFMAs run while its partner is held issuing
+//        a load into a busy memory pipe;
+//      - half tiles, 4 wavefronts (up when its whole-tile grid is under
+//        twelve rounds of the CUs): a workgroup takes one 128-token half of
+//        a row tile (2 x 4 accumulators, a ring of three 24 KiB stages,
+//        72 KiB), so two workgroups share a CU and one's prologue and SiLU
+//        epilogue run under the other's MFMAs;
+//      - dh: 4 wavefronts on a whole tile, wavefront w owning features
+//        64 w .. +63 of all 256 rows (2 x 8 accumulators), its epilogue using
+//        all four stage buffers;
+//    spreading the wavefronts over the features rather than 2 x 2 halves the
+//    slow transposed weight reads per MFMA;
 //  * K step 32; both tiles go global -> LDS with global_load_lds (16 bytes
-//    per lane, no registers) into a ring of stages: three of 24 KiB for
-//    half tiles (one stage in flight while one computes), four of 32 KiB
-//    for dh;
+//    per lane, no registers) into the ring of stages;
 //  * token rows are K-contiguous in memory and in LDS (read with
 //    ds_read_b128); the weights stay [K][N] (N contiguous) in LDS and the
 //    MFMA's K-consecutive operand is produced by ds_read_b64_tr_b16, which

@@ -204,6 +204,23 @@ size_t moe_expert_permute_scratch_size(int64_t T, int k, int E);
  */
 moe_status moe_ffn_get_device_error(const void *workspace, hipStream_t stream, int32_t *out);
 
+/*
+ * Measurement helper, not part of the layer: launches `blocks` one-wavefront
+ * workgroups on `stream`; workgroup b writes out[3b] = the id of the XCD it
+ * ran on, out[3b+1] = that XCD's shader-clock cycle counter and out[3b+2] =
+ * its constant 100 MHz counter.  Two samples taken around a timed region,
+ * paired by XCD, give the mean engine clock over the region:
+ * (difference of cycle counters) / (difference of 100 MHz counters) * 100 MHz.
+ *
+ *   out     device int64 [3 * blocks], 8-byte aligned, caller-owned
+ *   blocks  1 .. 1024 (workgroups are dealt round-robin over the XCDs, so 64
+ *           reach every XCD)
+ *
+ * Returns MOE_OK, MOE_ERR_INVALID_ARG (null or misaligned out, blocks out of
+ * range) or MOE_ERR_HIP.
+ */
+moe_status moe_device_clock_sample(int64_t *out, int blocks, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Router in front of the layer.
  *

@@ -4,6 +4,7 @@ apply the output tolerances.
 Tolerances (float outputs): bf16 max|y - y_ref| <= 1e-2 * max|y_ref| + 1e-3,
 fp32 max|y - y_ref| <= 1e-5 * max|y_ref|; y_ref is the fp64 oracle.
 """
+import os
 import sys
 
 import numpy as np
@@ -13,6 +14,12 @@ import moe_inputs
 
 BF16_RTOL, BF16_ATOL = 1e-2, 1e-3
 F32_RTOL = 1e-5
+
+
+def oracle_threads():
+    """Threads for the CPU oracle: the host cores this process may use,
+    capped at 16 (a one-GPU machine's share of its host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def say(msg):

@@ -14,11 +14,11 @@ import torch
 
 import moe_inputs
 import oracle
-from gpu_util import check_close, dev, device_inputs, host_shared, make_case, say, to_f64
+from gpu_util import check_close, dev, device_inputs, host_shared, make_case, oracle_threads, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
-NTHREADS = 16
+
 
 
 def gpu_backward(inp, workspace=None):
@@ -33,7 +33,7 @@ def gpu_backward(inp, workspace=None):
 
 def oracle_grads(inp):
     return oracle.backward(inp["x"], inp["topk_idx"], inp["topk_w"], inp["W1"], inp["W3"],
-                           inp["W2"], host_shared(inp), inp["dy"], nthreads=NTHREADS)
+                           inp["W2"], host_shared(inp), inp["dy"], nthreads=oracle_threads())
 
 
 def compare_all(g, ref, dtype, label):
@@ -130,12 +130,12 @@ def test_backward_workload_sampled(cfg):
                                        rng.choice(w.T, 16, replace=False)]))
     sub = {n: inp[n][tokens] for n in ("x", "topk_idx", "topk_w", "dy")}
     ref = oracle.backward(sub["x"], sub["topk_idx"], sub["topk_w"], inp["W1"], inp["W3"], inp["W2"],
-                          host_shared(inp), sub["dy"], nthreads=NTHREADS)
+                          host_shared(inp), sub["dy"], nthreads=oracle_threads())
     check_close(to_f64(g["dx"])[tokens], ref["dx"], w.dtype, f"{w.name} dx")
     check_close(to_f64(g["dtopk_w"])[tokens], ref["dw"], w.dtype, f"{w.name} dtopk_w")
     counts = np.bincount(inp["topk_idx"].reshape(-1), minlength=w.E)
     e = int(np.argmin(counts))
     wg = oracle.backward_weight_grads(inp["x"], inp["topk_idx"], inp["topk_w"], inp["W1"], inp["W3"],
-                                      inp["W2"], host_shared(inp), inp["dy"], [e], nthreads=NTHREADS)[e]
+                                      inp["W2"], host_shared(inp), inp["dy"], [e], nthreads=oracle_threads())[e]
     for name, ref_e in zip(("dW1", "dW3", "dW2"), wg):
         check_close(to_f64(g[name][e]), ref_e, w.dtype, f"{w.name} {name}[{e}] ({counts[e]} rows)")

@@ -3,8 +3,9 @@
 * full element-by-element parity at sizes the oracle finishes in seconds,
   spanning several 256-row tiles, ragged tails, column tails, the
   multi-block permute, Zipf skew and empty experts;
-* the five workload shapes at full size in the launch configuration the
-  benchmark times, on sampled tokens the oracle computes one by one;
+* (the five workload shapes at full size, every token, are in
+  test_gpu_fullsize.py)
+* 2^20 tokens on sampled tokens the oracle computes one by one;
 * the sorted-row intermediates h and Y on sampled rows;
 * run-to-run bitwise determinism with garbage-filled workspaces;
 * edge cases: T = 1, all tokens on one expert, zero routing weights,
@@ -17,11 +18,9 @@ import torch
 import moe_inputs
 import oracle
 from oracle import brute
-from gpu_util import check_close, device_inputs, host_shared, make_case, say, to_f64
+from gpu_util import check_close, device_inputs, host_shared, make_case, oracle_threads, say, to_f64
 
 pytestmark = pytest.mark.gpu
-
-NTHREADS = 16
 
 
 def gpu_forward(inp, variant="unfused", workspace=None):
@@ -35,7 +34,7 @@ def gpu_forward(inp, variant="unfused", workspace=None):
 
 def oracle_y(inp, tokens=None):
     return oracle.forward_dense(inp["x"], inp["topk_idx"], inp["topk_w"], inp["W1"], inp["W3"],
-                                inp["W2"], host_shared(inp), tokens=tokens, nthreads=NTHREADS)
+                                inp["W2"], host_shared(inp), tokens=tokens, nthreads=oracle_threads())
 
 
 FULL_CASES = [
@@ -93,33 +92,6 @@ def test_fused_full_parity(case):
     say(f"fused full parity {case}")
     y, _ = gpu_forward(inp, variant="fused")
     check_close(to_f64(y), oracle_y(inp), "bf16", "fused " + str(case))
-
-
-@pytest.mark.parametrize("cfg", [1, 2, 4])
-def test_fused_workload_sampled(cfg):
-    w = moe_inputs.WORKLOADS[cfg]
-    inp = moe_inputs.make_inputs(cfg)
-    say(f"fused workload {w.name}")
-    y, _ = gpu_forward(inp, variant="fused")
-    rng = np.random.default_rng(100 + cfg)
-    tokens = np.unique(np.concatenate([np.arange(8), np.arange(w.T - 8, w.T),
-                                       rng.choice(w.T, 32, replace=False)]))
-    check_close(to_f64(y)[tokens], oracle_y(inp, tokens), w.dtype, "fused " + w.name)
-
-
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
-def test_forward_workload_sampled(cfg):
-    w = moe_inputs.WORKLOADS[cfg]
-    inp = moe_inputs.make_inputs(cfg)
-    say(f"forward workload {w.name}")
-    y, _ = gpu_forward(inp)
-    rng = np.random.default_rng(cfg)
-    n = min(w.T, 48)
-    tokens = np.unique(np.concatenate([np.arange(8), np.arange(w.T - 8, w.T),
-                                       rng.choice(w.T, n - 16, replace=False)]))
-    tokens = tokens[tokens < w.T]
-    ref = oracle_y(inp, tokens)
-    check_close(to_f64(y)[tokens], ref, w.dtype, w.name)
 
 
 def test_forward_million_tokens_sampled():
