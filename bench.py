@@ -590,18 +590,26 @@ def clock_record(m, value_tflops):
     """Mean engine clock over the timed region (per XCD) and the bf16 MFMA
     peak at that clock: compute units x clock x 4096 dense bf16 FLOPs per CU
     per cycle (2.5 PFLOP/s at 256 CUs and 2.4 GHz)."""
+    import numpy as np
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     c = m["clocks"]
     if not c:
-        return {"compute_units": cus, "sclk_ghz_mean": None}
-    mean = sum(c.values()) / len(c)
-    peak = cus * mean * 1e9 * 4096 / 1e12
-    return {"compute_units": cus, "sclk_ghz_mean": round(mean, 4),
-            "sclk_ghz_per_xcd": {str(k): round(v, 4) for k, v in sorted(c.items())},
+        return {"compute_units": cus, "sclk_ghz_median": None}
+    v = np.array(list(c.values()))
+    med = float(np.median(v))
+    per_xcd = {}
+    for (x, _), g in c.items():
+        per_xcd.setdefault(x, []).append(g)
+    peak = cus * med * 1e9 * 4096 / 1e12
+    return {"compute_units": cus, "units_sampled": len(c), "sclk_ghz_median": round(med, 4),
+            "sclk_ghz_p10_p90": [round(float(np.percentile(v, 10)), 4),
+                                 round(float(np.percentile(v, 90)), 4)],
+            "sclk_ghz_median_per_xcd": {str(x): round(float(np.median(g)), 4)
+                                        for x, g in sorted(per_xcd.items())},
             "peak_bf16_tflops_at_measured_clock": round(peak, 1),
             "frac_of_peak_at_measured_clock": round(value_tflops / peak, 4),
-            "peak_bf16_tflops_at_2p4ghz": round(cus * 2.4 * 4096, 1)}
+            "peak_bf16_tflops_at_2p4ghz": round(cus * 2.4e9 * 4096 / 1e12, 1)}
 
 
 def small_chunk_record(args):

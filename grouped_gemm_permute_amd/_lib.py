@@ -285,24 +285,24 @@ def device_error(workspace, stream=None) -> int:
     return int(v.value)
 
 
-def device_clock_sample(blocks=64, stream=None):
+def device_clock_sample(blocks=1024, stream=None):
     """Issue a clock sample on the stream; returns the device int64 [blocks, 3]
-    tensor (XCD id, shader-clock cycles, 100 MHz counter) it will hold."""
+    tensor (compute unit, shader-clock cycles, 100 MHz counter) it will hold."""
     out = torch.empty((blocks, 3), dtype=torch.int64, device="cuda")
     _check(lib().moe_device_clock_sample(_ptr(out), blocks, _stream(stream)), "moe_device_clock_sample")
     return out
 
 
 def engine_clock_ghz(before, after):
-    """Mean engine clock (GHz) of each XCD between two device_clock_sample
-    results (host copies), pairing the samples by XCD id."""
+    """Mean engine clock (GHz) between two device_clock_sample results (host
+    copies) of every compute unit sampled in both, keyed by (XCD, unit)."""
     first = {}
-    for xcc, cyc, rt in before.tolist():
-        first.setdefault(xcc, (cyc, rt))
+    for loc, cyc, rt in before.tolist():
+        first.setdefault(loc, (cyc, rt))
     out = {}
-    for xcc, cyc, rt in after.tolist():
-        if xcc in first and xcc not in out and rt > first[xcc][1]:
-            out[xcc] = (cyc - first[xcc][0]) / (rt - first[xcc][1]) * 0.1
+    for loc, cyc, rt in after.tolist():
+        if loc in first and loc not in out and rt > first[loc][1]:
+            out[(loc >> 16, loc & 0xffff)] = (cyc - first[loc][0]) / (rt - first[loc][1]) * 0.1
     return out
 
 

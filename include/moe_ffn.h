@@ -206,15 +206,15 @@ moe_status moe_ffn_get_device_error(const void *workspace, hipStream_t stream, i
 
 /*
  * Measurement helper, not part of the layer: launches `blocks` one-wavefront
- * workgroups on `stream`; workgroup b writes out[3b] = the id of the XCD it
- * ran on, out[3b+1] = that XCD's shader-clock cycle counter and out[3b+2] =
- * its constant 100 MHz counter.  Two samples taken around a timed region,
- * paired by XCD, give the mean engine clock over the region:
+ * workgroups on `stream`; workgroup b writes out[3b] = the compute unit it
+ * ran on (XCD id * 65536 + the shader engine, array and CU bits of the
+ * hardware id), out[3b+1] = the shader-clock cycle counter and out[3b+2] =
+ * the constant 100 MHz counter.  Two samples taken around a timed region,
+ * paired by compute unit, give the mean engine clock over the region:
  * (difference of cycle counters) / (difference of 100 MHz counters) * 100 MHz.
  *
  *   out     device int64 [3 * blocks], 8-byte aligned, caller-owned
- *   blocks  1 .. 1024 (workgroups are dealt round-robin over the XCDs, so 64
- *           reach every XCD)
+ *   blocks  1 .. 1024 (1024 one-wavefront workgroups reach every CU)
  *
  * Returns MOE_OK, MOE_ERR_INVALID_ARG (null or misaligned out, blocks out of
  * range) or MOE_ERR_HIP.
