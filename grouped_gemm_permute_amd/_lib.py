@@ -26,8 +26,11 @@ EXPORTS = (
     "moe_ffn_forward", "moe_ffn_forward_timed", "moe_expert_permute", "moe_expert_permute_scratch_size",
     "moe_ffn_get_device_error", "moe_ffn_backward_workspace_layout", "moe_ffn_backward_workspace_size",
     "moe_ffn_backward", "moe_ffn_backward_timed", "moe_router_topk", "moe_ffn_forward_routed",
-    "moe_ffn_forward_routed_timed", "moe_device_clock_sample",
+    "moe_ffn_forward_routed_timed", "moe_device_clock_sample", "moe_ffn_forward_noalloc",
 )
+
+# Bytes of the per-device workspace array behind moe_ffn_forward_noalloc.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -102,6 +105,8 @@ def lib():
         L.moe_ffn_forward_routed.argtypes = routed
         L.moe_ffn_forward_routed_timed.restype = ci
         L.moe_ffn_forward_routed_timed.argtypes = routed + [P]
+        L.moe_ffn_forward_noalloc.restype = ci
+        L.moe_ffn_forward_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, i64, ci, ci, ci, ci, ci, ci, P]
         L.moe_device_clock_sample.restype = ci
         L.moe_device_clock_sample.argtypes = [P, ci, P]
         L.moe_ffn_get_device_error.restype = ci
@@ -251,6 +256,26 @@ def forward(x, topk_idx, topk_w, W1, W3, W2, shared=None, y=None, variant="unfus
         _check(lib().moe_ffn_forward(*args), "moe_ffn_forward")
     else:
         _check(lib().moe_ffn_forward_timed(*args, events), "moe_ffn_forward_timed")
+    return y
+
+
+def forward_noalloc(x, topk_idx, topk_w, W1, W3, W2, shared=None, y=None, variant="unfused",
+                    stream=None):
+    """y = moe_ffn_forward_noalloc(...): the forward on the library's own
+    per-device workspace array (no allocation by the library; ``y`` is
+    allocated here only when not given).  Calls overlapping on one GPU race
+    on that array."""
+    T, D, F, E = _check_layer(x, W1, W3, W2, shared, y)
+    k = _check_routing(x, topk_idx, topk_w, T)
+    _same_device(x, dict(topk_idx=topk_idx, topk_w=topk_w, **_layer_tensors(W1, W3, W2, shared, y)))
+    Ws1, Ws3, Ws2 = shared if shared is not None else (None, None, None)
+    if y is None:
+        y = torch.empty((T, D), dtype=x.dtype, device=x.device)
+    _check(lib().moe_ffn_forward_noalloc(_ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W1), _ptr(W3),
+                                         _ptr(W2), _ptr(Ws1), _ptr(Ws3), _ptr(Ws2), _ptr(y), T, D, F,
+                                         E, k, _dtype_enum(x.dtype), _variant_enum(variant),
+                                         _stream(stream)),
+           "moe_ffn_forward_noalloc")
     return y
 
 

@@ -13,6 +13,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 namespace {
 
 using namespace moe;
@@ -296,6 +298,53 @@ moe_status moe_ffn_forward(const void* x, const int32_t* topk_idx, const float* 
                            size_t ws_bytes, hipStream_t stream) {
     return moe_ffn_forward_timed(x, topk_idx, topk_w, W1, W3, W2, Ws1, Ws3, Ws2, y, T, D, F, E, k,
                                  dtype, variant, workspace, ws_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of moe_ffn_forward_noalloc: one array per device, resolved to a
+// device address once per device with hipGetSymbolAddress (the array's name
+// in host code is only a host-side stand-in and must never reach a kernel).
+__device__ __attribute__((aligned(256))) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, or null.
+void* scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_ffn_forward_noalloc(const void* x, const int32_t* topk_idx, const float* topk_w,
+                                   const void* W1, const void* W3, const void* W2, const void* Ws1,
+                                   const void* Ws3, const void* Ws2, void* y, int64_t T, int D,
+                                   int F, int E, int k, moe_dtype dtype, moe_variant variant,
+                                   hipStream_t stream) {
+    const int nsh = (Ws1 != nullptr) + (Ws3 != nullptr) + (Ws2 != nullptr);
+    if (nsh != 0 && nsh != 3) return MOE_ERR_INVALID_ARG;
+    moe_ws_layout L;
+    const moe_status st = make_layout(T, D, F, E, k, nsh == 3, dtype, variant, &L);
+    if (st != MOE_OK) return st;
+    if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    void* ws = scratch_ptr();
+    if (!ws) return MOE_ERR_HIP;
+    return forward_impl(x, nullptr, topk_idx, topk_w, W1, W3, W2, Ws1, Ws3, Ws2, y, T, D, F, E, k,
+                        dtype, variant, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 moe_status moe_ffn_get_device_error(const void* workspace, hipStream_t stream, int32_t* out) {

@@ -170,6 +170,37 @@ moe_status moe_ffn_forward_timed(const void *x, const int32_t *topk_idx, const f
                                  hipEvent_t events[5]);
 
 /*
+ * moe_ffn_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The library keeps one workspace of
+ * MOE_NOALLOC_SCRATCH_BYTES per device in a file-scope device array, which
+ * each GPU the library runs on holds until the process ends; the first call
+ * on a device resolves its address (hipGetSymbolAddress), no call allocates
+ * or frees memory.  The caller still passes the inputs and y.
+ *
+ * Arguments, results, variants and errors are those of moe_ffn_forward,
+ * except that MOE_ERR_WORKSPACE means the call would need more than
+ * MOE_NOALLOC_SCRATCH_BYTES of workspace (moe_ffn_workspace_size() of the
+ * same sizes; for example the 4096-token layer at D 768, F 1536, E 8, top-2
+ * with a shared expert needs 54 MiB, 32768 tokens need 433 MiB and are
+ * refused).  The forward reads nothing from its workspace that the same call
+ * has not written, so the array needs no clearing between calls.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents: two calls that overlap in time on the same GPU (different
+ * streams not ordered by events, or different host threads) race on it and
+ * give undefined results.  moe_ffn_get_device_error cannot read this
+ * workspace's invalid-slot count.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+moe_status moe_ffn_forward_noalloc(const void *x, const int32_t *topk_idx, const float *topk_w,
+                                   const void *W1, const void *W3, const void *W2,
+                                   const void *Ws1, const void *Ws3, const void *Ws2,
+                                   void *y, int64_t T, int D, int F, int E, int k,
+                                   moe_dtype dtype, moe_variant variant, hipStream_t stream);
+
+/*
  * Expert permute alone: the stable counting sort of the T*k slots
  * s = t*k + j by expert id ("Triton MoE Kernels & Memory Checkpointing",
  * Part A section 10.3 steps 1-2: flatten, stable argsort, bincount and
