@@ -9,26 +9,45 @@
 // traffic model).  Here the activation is SwiGLU, as everywhere in this
 // library:
 //
-//   for each chunk of CH = 128 h columns f:
+//   for each chunk of CH = 256 h columns f (the last one may hold 128):
 //     g, u = x_tile . W1[:, f], x_tile . W3[:, f]        (fp32 accumulate, K = D)
 //     h    = bf16(silu(g) * u)                           (into LDS)
 //     acc += h . W2[f, :]                                (fp32 accumulate, K = CH)
 //   Y[row] = bf16(acc[row])                              (the combine applies the routing weight)
 //
-// Shapes and placement on gfx950 (256 threads = 4 wavefronts, one per SIMD):
+// Shapes and placement on gfx950 (512 threads = 8 wavefronts, two per SIMD,
+// one workgroup per CU):
 //  * token tile TT = 64 rows of one group; the fp32 accumulator acc is
-//    64 x D, each wavefront owning D/4 output columns (D <= 1024 -> at most
-//    256 accumulator registers per lane);
-//  * up phase per chunk: MFMA tile 256 features (128 g + 128 u) x 64 tokens,
-//    K step 64; wavefront w holds g and u of h columns 32 w .. 32 w + 31;
-//  * down phase per chunk: 8 K steps of 16 rows of W2 [16, D];
-//  * all operand tiles stream global -> LDS with global_load_lds (double
-//    buffered, 40 KiB per stage); weights stay [K][N] and reach the MFMA
-//    through ds_read_b64_tr_b16; token rows and h are K-contiguous;
+//    64 x D (D <= 1024 -> at most 128 accumulator registers per lane, which
+//    two wavefronts per SIMD can hold).  With D / 128 even, wavefront w owns
+//    output columns w D / 8 .. +D/8 - 1 of all 64 rows; otherwise columns
+//    (w % 4) D / 4 .. +D/4 - 1 of rows 32 (w / 4) .. +31;
+//  * up phase: MFMA tile 512 features x 64 tokens per chunk; wavefront w
+//    owns two 32-feature blocks, each 16 W1 columns followed by the same 16
+//    W3 columns (h columns 32 w .. 32 w + 31), for both 32-row blocks, so
+//    accumulator elements v (g) and v + 8 (u) of a lane belong to the same h
+//    element and every operand fragment read from LDS feeds two MFMAs (the
+//    LDS read rate, not the MFMA rate, bounds a tile this short);
+//  * the up phase (K step 16: token rows [64][16], weights [16][512]) and
+//    the down phase (16 rows of W2 [16][D] per step) share one stream of
+//    stages through a ring of four 32 KiB LDS buffers, two stages in flight
+//    while one is computed, all filled with global_load_lds; weights stay
+//    [K][N] and reach the MFMA through ds_read_b64_tr_b16, token rows and h
+//    are K-contiguous; h of the current chunk sits in its own 32 KiB buffer
+//    (160 KiB of LDS in all);
+//  * token rows are loaded with the non-temporal policy: each tile re-reads
+//    its own 128 KiB of x once per chunk, and 32 tiles' worth would fill an
+//    XCD's L2 and evict the weight chunks its workgroups share;
 //  * tiles are numbered group-major and each XCD takes a contiguous range,
 //    so the workgroups of one XCD work on the same expert at the same time
-//    and share each weight chunk through that XCD's L2 instead of streaming
-//    it from HBM once per token tile.
+//    and share each weight chunk through that XCD's L2, each starting the
+//    chunk's steps at a different point.
+//
+// Measured on the 16384-token F > D workload (D 1024, F 4096, 16 experts):
+// the kernel stages ~27 MB per 64-row tile (each tile re-streams its
+// expert's weights), ~50 MB per CU per launch, and sustains ~40 GB/s of
+// weight staging per CU; with no loads at all its loop alone takes half the
+// launch.  The unfused pair stages 4x fewer bytes per FLOP and is faster.
 #include "mfma_common.h"
 
 namespace moe {
@@ -37,19 +56,47 @@ namespace {
 using namespace mfma;
 
 constexpr int TT = kFusedTileRows;   // 64 tokens per tile
-constexpr int CH = 128;              // h columns per F chunk
-constexpr int NT = 256;
-constexpr int UP_BK = 64;
-constexpr int X_ROW = UP_BK * 2;                 // 128 B token row (K-contiguous)
-constexpr int X_BYTES = TT * X_ROW;              // 8 KiB
-constexpr int WGU_ROW = 2 * CH * 2;              // 512 B: 256 features of one k row
-constexpr int WGU_BYTES = UP_BK * WGU_ROW;       // 32 KiB
-constexpr int STAGE_BYTES = X_BYTES + WGU_BYTES; // 40 KiB (a down stage [16][D] needs <= 32 KiB)
-constexpr int H_ROW = CH * 2;                    // 256 B
-constexpr int H_BYTES = TT * H_ROW;              // 16 KiB
-constexpr int DN_STEPS = CH / 16;                // 8 down steps per chunk
+constexpr int CH = 256;              // h columns per F chunk
+constexpr int NW = 8;                // wavefronts
+constexpr int NT = 64 * NW;
+constexpr int UP_BK = 16;                        // up K step
+constexpr int X_ROW = UP_BK * 2;                 // 32 B token row (K-contiguous)
+constexpr int X_BYTES = TT * X_ROW;              // 2 KiB
+constexpr int WGU_ROW = 2 * CH * 2;              // 1 KiB: 512 features of one k row
+constexpr int WGU_BYTES = UP_BK * WGU_ROW;       // 16 KiB
+constexpr int UP_LOADS = (X_BYTES + WGU_BYTES) / 1024;   // 1 KiB DMA instructions per up stage
+constexpr int DN_K = 16;                         // W2 rows per down stage
+constexpr int DN_STEPS = CH / DN_K;              // 16 down stages per whole chunk
+constexpr int STAGE_BYTES = 32 * 1024;           // >= max(18 KiB up, 16 * 2 D down)
+constexpr int H_ROW = CH * 2;                    // 512 B
+constexpr int H_BYTES = TT * H_ROW;              // 32 KiB
 
-static_assert(TT == 64 && CH == 128 && NT == 256, "index math below assumes these");
+static_assert(TT == 64 && CH == 256 && NW == 8 && UP_BK == 16, "index math below assumes these");
+static_assert(X_BYTES + WGU_BYTES <= STAGE_BYTES && 4 * STAGE_BYTES + H_BYTES <= 160 * 1024,
+              "four stages and h fit in LDS");
+
+// 32-byte token rows (2 chunks): the 16 rows one ds_read_b128 phase reads
+// at one logical chunk fill distinct bank groups.
+__device__ __forceinline__ int swz_x(int row) { return (row >> 3) & 1; }
+
+// DMA instructions j = w, w + 8, ... (< n) of a stage belong to wavefront w.
+__host__ __device__ constexpr int per_wave(int n, int w) { return n > w ? (n - w + NW - 1) / NW : 0; }
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in 0..8 (the immediate must be a
+// compile-time constant).
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(waitcnt_imm(1, 0)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(waitcnt_imm(2, 0)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(waitcnt_imm(3, 0)); break;
+        case 4: __builtin_amdgcn_s_waitcnt(waitcnt_imm(4, 0)); break;
+        case 5: __builtin_amdgcn_s_waitcnt(waitcnt_imm(5, 0)); break;
+        case 6: __builtin_amdgcn_s_waitcnt(waitcnt_imm(6, 0)); break;
+        case 7: __builtin_amdgcn_s_waitcnt(waitcnt_imm(7, 0)); break;
+        default: __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0)); break;
+    }
+}
 
 struct FusedArgs {
     GroupArgs g;
@@ -63,18 +110,29 @@ struct FusedArgs {
 // D = 128 * NFB.
 template <int NFB>
 __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArgs a) {
-    // Separate LDS objects per stage buffer: the compiler then knows reads of
-    // one never alias the asynchronous global_load_lds writes into the other.
-    __shared__ __attribute__((aligned(1024))) char lds0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char lds1[STAGE_BYTES];
+    // Separate LDS objects per stage buffer, each named statically by the
+    // unrolled loops below: the compiler then knows reads of one never alias
+    // the asynchronous global_load_lds writes into another.
+    __shared__ __attribute__((aligned(1024))) char st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st3[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char hbuf[H_BYTES];
 
     constexpr int D = 128 * NFB;
-    constexpr int DN_ROW = 2 * D;          // bytes of one W2 row in LDS
-    constexpr int WCOLS = 32 * NFB;        // output columns per wavefront
-    constexpr int KU = D / UP_BK;          // up K steps per chunk (even)
+    constexpr int DN_ROW = 2 * D;              // bytes of one W2 row in LDS
+    constexpr int DN_LOADS = DN_K * DN_ROW / 1024;   // 4 NFB DMA instructions per down stage
+    constexpr int KU = D / UP_BK;              // up stages per chunk (8 NFB)
+    constexpr int SPC = KU + DN_STEPS;         // stages per whole chunk (a multiple of 4)
+    // output layout: NCG column groups of CBW 32-column blocks, RBW row blocks per wavefront
+    constexpr int NCG = NFB % 2 == 0 ? 8 : 4;
+    constexpr int CBW = 4 * NFB / NCG;
+    constexpr int RBW = NCG == 8 ? 2 : 1;
+    static_assert(DN_K * DN_ROW <= STAGE_BYTES && SPC % 4 == 0 && KU % 4 == 0, "stage shapes");
     const int F = a.F;
-    const int NC = F / CH;
+    const int NCH = (F + CH - 1) / CH;         // chunks; the last holds 128 columns when F % 256 != 0
+    const bool half = F % CH != 0;
+    const int NSTEP = NCH * SPC - (half ? DN_STEPS / 2 : 0);
 
     const int mt = xcd_remap_work(blockIdx.x, a.g.tile_off[a.g.G]);
     if (mt < 0) return;
@@ -92,232 +150,238 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
     const uint16_t* W3g = shared ? a.Ws3 : a.W3 + grp * gstride;
     const uint16_t* W2g = shared ? a.Ws2 : a.W2 + grp * gstride;
 
-    // ---- token rows: DMA instruction j (0, 1) of wavefront w fills rows
-    // 16 w + 8 j .. +7; lane -> row 16 w + 8 j + lane/8, physical chunk lane%8.
-    const char* x_src[2];
+    // DMA loads of this wavefront per stage (fixed per stage kind).
+    const int up_n = per_wave(UP_LOADS, wave);
+    const int dn_n = per_wave(DN_LOADS, wave);
+
+    // ---- up stage: instruction j (0..17) fills LDS bytes 1024 j .. +1023.
+    // j < 2: token rows 32 j .. 32 j + 31 (lane -> row 32 j + lane/2,
+    // physical chunk lane%2 holding logical chunk (lane%2) ^ swz_x(row));
+    // j >= 2: weight k row j - 2 (lane = physical chunk, holding logical chunk
+    // cl = lane ^ swz_tr(k): MFMA features 8 cl .. 8 cl + 7 = wavefront block
+    // cl / 8, its 32-feature block (cl / 4) % 2, W3 when (cl / 2) is odd, h
+    // column 32 (cl / 8) + 16 ((cl / 4) % 2) + 8 (cl % 2)).  Wavefront w
+    // issues j = w, w + 8, w + 16 (< 18): waves 0 and 1 own token block w and
+    // weight rows w + 6, w + 14; waves 2-7 weight rows w - 2, w + 6.  A
+    // wavefront's weight rows share k % 4, hence one per-lane source.
+    const char* x_src = nullptr;
+    if (wave < 2) {
+        const int row = 32 * wave + (lane >> 1);
+        const int64_t p = tile_r0 + min(row, valid_rows - 1);
+        const int64_t tok = shared ? p - a.g.S : (int64_t)(a.g.perm[p] / a.g.k);
+        x_src = (const char*)(a.x + tok * D + 8 * ((lane & 1) ^ swz_x(row)));
+    }
+    const int kw0 = wave < 2 ? wave + 6 : wave - 2;   // first weight k row of this wavefront
+    int col_hi;                                       // 128 when this lane's column is in the chunk's upper half
+    const uint16_t* w_src;
     {
-        int64_t src_row[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t p = tile_r0 + min(16 * wave + 8 * j + (lane >> 3), valid_rows - 1);
-            src_row[j] = p;
-        }
-        if (!shared) {
-            const int32_t s0 = a.g.perm[src_row[0]], s1 = a.g.perm[src_row[1]];
-            src_row[0] = s0 / a.g.k;
-            src_row[1] = s1 / a.g.k;
-        } else {
-            src_row[0] -= a.g.S;
-            src_row[1] -= a.g.S;
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = 16 * wave + 8 * j + (lane >> 3);
-            const int c = (lane & 7) ^ swz8(row);
-            x_src[j] = (const char*)(a.x + src_row[j] * (int64_t)D + 8 * c);
-        }
+        const int cl = lane ^ swz_tr(kw0);
+        const int col = 32 * (cl >> 3) + 16 * ((cl >> 2) & 1) + 8 * (cl & 1);
+        col_hi = col >= 128 ? 128 : 0;
+        w_src = (((cl >> 1) & 1) ? W3g : W1g) + col;
     }
-
-    // ---- up weights: DMA instruction j (0..7) of wavefront w fills k rows
-    // 16 w + 2 j, +1; lane -> k row 16 w + 2 j + lane/32, physical chunk
-    // lane%32 holding logical chunk cl = phys ^ swz_tr(k).  Logical chunk cl
-    // (8 features): wavefront block wb = cl / 8, g when (cl / 4) is even, u
-    // when odd, h column 32 wb + 8 (cl % 4) within the chunk.
-    // (The per-lane source is rebuilt at every issue: a few integer ops are
-    // cheaper than keeping eight 64-bit pointers live next to the accumulators.)
-    auto wgu_src = [&](int j) {
-        const int kr = 16 * wave + 2 * j + (lane >> 5);
-        const int cl = (lane & 31) ^ swz_tr(kr);
-        const int col = 32 * (cl >> 3) + 8 * (cl & 3);
-        return (((cl >> 2) & 1) ? W3g : W1g) + (int64_t)kr * F + col;
+    auto issue_up = [&](int c, int ks, char* st) {
+        if (wave < 2) load_lds16_nt(x_src + ks * X_ROW, st + 1024 * wave);
+        // a last chunk of 128 columns re-reads the lower half for the upper
+        // (valid addresses; those features are never used)
+        const uint16_t* base = w_src + c * CH - (half && c == NCH - 1 ? col_hi : 0);
+        const int64_t k0 = (int64_t)ks * UP_BK + kw0;
+        load_lds16(base + k0 * F, st + X_BYTES + 1024 * kw0);
+        load_lds16(base + (k0 + 8) * F, st + X_BYTES + 1024 * (kw0 + 8));
     };
-    // ---- down weights: a stage is W2 rows [16][D] = 256 NFB chunks; DMA
-    // instruction j (0..NFB-1) of wavefront w covers linear chunks
-    // 64 (w NFB + j) + lane: row L / (16 NFB), physical chunk L % (16 NFB).
-
-    auto issue_up = [&](int c, int s, char* st) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            load_lds16(x_src[j] + (int64_t)s * X_ROW, st + (16 * wave + 8 * j) * X_ROW);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            load_lds16(wgu_src(j) + (int64_t)s * UP_BK * F + c * CH,
-                       st + X_BYTES + (16 * wave + 2 * j) * WGU_ROW);
-    };
+    // ---- down stage: W2 rows [16][D] = 256 NFB chunks; instruction j
+    // covers linear chunks 64 j + lane: row L / (16 NFB), physical chunk
+    // L % (16 NFB) holding logical chunk phys ^ swz_tr(row).
     auto issue_down = [&](int c, int q, char* st) {
-        const uint16_t* base = W2g + (int64_t)(c * CH + 16 * q) * D;
+        const uint16_t* base = W2g + (int64_t)(c * CH + DN_K * q) * D;
 #pragma unroll
-        for (int j = 0; j < NFB; ++j) {
-            const int L = 64 * (wave * NFB + j) + lane;
-            const int row = L / (16 * NFB), pc = L - row * (16 * NFB);
-            load_lds16(base + row * D + 8 * (pc ^ swz_tr(row)), st + 1024 * (wave * NFB + j));
+        for (int i = 0; i < (DN_LOADS + NW - 1) / NW; ++i) {
+            const int j = wave + NW * i;
+            if (j < DN_LOADS) {
+                const int L = 64 * j + lane;
+                const int row = L / (16 * NFB), pc = L - row * (16 * NFB);
+                load_lds16(base + row * D + 8 * (pc ^ swz_tr(row)), st + 1024 * j);
+            }
         }
     };
+    // stage s of the stream: chunk c = s / SPC, up step (s % SPC) < KU, else
+    // down step (s % SPC) - KU.  Stages past the last re-load the last one
+    // (a down stage, into a buffer never computed on), so every stage issues
+    // its kind's fixed number of loads.
+    // Neighbouring tiles (which run at the same time on one XCD) walk a
+    // chunk's up and down steps from 8 different starting points, so they
+    // request different weight rows of the shared chunk at any moment
+    // instead of all the same lines (3.5% faster than all starting at 0,
+    // measured; the order is fixed per tile, so results stay reproducible).
+    const int rot = mt % 8;
+    auto issue = [&](int s, char* st) {
+        s = min(s, NSTEP - 1);
+        const int c = s / SPC, r = s - c * SPC;
+        if (r < KU) issue_up(c, (r + rot * (KU / 8)) % KU, st);
+        else {
+            const int dsn = half && c == NCH - 1 ? DN_STEPS / 2 : DN_STEPS;
+            issue_down(c, (r - KU + rot * (dsn / 8)) % dsn, st);
+        }
+    };
+    auto loads_of = [&](int s) {
+        s = min(s, NSTEP - 1);
+        return s - (s / SPC) * SPC < KU ? up_n : dn_n;
+    };
 
-    // ---- operand read offsets.  Transposed reads: lane = 16 G + s reads
-    // k = 8 (G>>1) + 4 r + s/4 (+16 ks), feature R = ... + 16 (G&1) + 4 (s&3).
+    // ---- operand read offsets.  Transposed weight reads: lane = 16 G + s
+    // reads k = 8 (G>>1) + 4 r + s/4, feature R = ... + 16 (G&1) + 4 (s&3);
+    // the r = 1 read is the r = 0 one plus four rows.
     const int G = lane >> 4, sl = lane & 15;
-    int gu_off[2][2];
+    const int tk = 8 * (G >> 1) + (sl >> 2);
+    int gu_off[2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int k = 8 * (G >> 1) + 4 * r + (sl >> 2);
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-            const int R = 64 * wave + 32 * mi + 16 * (G & 1) + 4 * (sl & 3);
-            gu_off[mi][r] = X_BYTES + k * WGU_ROW + (((R >> 3) ^ swz_tr(k)) << 4) + 8 * (sl & 1);
-        }
+    for (int fb = 0; fb < 2; ++fb) {
+        const int R = 64 * wave + 32 * fb + 16 * (G & 1) + 4 * (sl & 3);
+        gu_off[fb] = X_BYTES + tk * WGU_ROW + (((R >> 3) ^ swz_tr(tk)) << 4) + 8 * ((R >> 2) & 1);
     }
-    // Down weight operand: k = 8 (G>>1) + 4 r + s/4 within the 16-row stage,
-    // column R = WCOLS w + 32 fb + 16 (G&1) + 4 (s&3); the chunk index is
-    // recomputed per block (cheaper than keeping 2 NFB offsets live).
-    const int dn_k0 = 8 * (G >> 1) + (sl >> 2);
-    const int dn_c0 = (WCOLS * wave + 16 * (G & 1) + 4 * (sl & 3)) >> 3;
-    const int dn_b = 8 * (sl & 1);
-    auto dn_off = [&](int fb, int r) {
-        const int k = dn_k0 + 4 * r;
-        return k * DN_ROW + (((dn_c0 + 4 * fb) ^ swz_tr(k)) << 4) + dn_b;
-    };
-    int tok_off[2], tok_swz8[2], tok_swz16[2];
+    const int cb0 = NCG == 8 ? wave * CBW : (wave & 3) * CBW;   // first 32-column block
+    const int rb0 = NCG == 8 ? 0 : (wave >> 2);                  // first 32-row block
+    int dn_off[CBW];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const int t = 32 * tb + (lane & 31);
-        tok_off[tb] = t;
-        tok_swz8[tb] = swz8(t);
-        tok_swz16[tb] = swz16(t);
+    for (int i = 0; i < CBW; ++i) {
+        const int R = 32 * (cb0 + i) + 16 * (G & 1) + 4 * (sl & 3);
+        dn_off[i] = tk * DN_ROW + (((R >> 3) ^ swz_tr(tk)) << 4) + 8 * ((R >> 2) & 1);
     }
+    const int xr = lane & 31;                      // token / h row within a 32-row block
+    const int x_off = xr * X_ROW + (((lane >> 5) ^ swz_x(xr)) << 4);   // + 32 nj rows
 
-    f32x16_t acc_y[NFB][2];
+    f32x16_t acc_y[CBW][RBW];
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) acc_y[fb][0] = acc_y[fb][1] = f32x16_t{};
+    for (int i = 0; i < CBW; ++i)
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) acc_y[i][j] = f32x16_t{};
     f32x16_t acc_up[2][2];
 
-    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-    // One up K step (64) on stage st: 4 slices x (2 weight frags, 2 token frags, 4 MFMAs).
+    // One up K step (16) on stage st: 2 weight frags x 2 token frags = 4 MFMAs.
     auto compute_up = [&](const char* st) {
+        bf16x8_t wf[2], xf[2];
 #pragma unroll
-        for (int ks = 0; ks < UP_BK / 16; ++ks) {
-            bf16x8_t wf[2], xf[2];
+        for (int fb = 0; fb < 2; ++fb)
+            wf[fb] = cat_bf16(read_tr(st + gu_off[fb]), read_tr(st + gu_off[fb] + 4 * WGU_ROW));
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                wf[mi] = cat_bf16(read_tr(st + gu_off[mi][0] + ks * 16 * WGU_ROW),
-                                  read_tr(st + gu_off[mi][1] + ks * 16 * WGU_ROW));
+        for (int nj = 0; nj < 2; ++nj)
+            xf[nj] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + x_off + 32 * nj * X_ROW));
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                const int c = (2 * ks + (lane >> 5)) ^ tok_swz8[tb];
-                xf[tb] = __builtin_bit_cast(bf16x8_t,
-                                            *(const u32x4_t*)(st + tok_off[tb] * X_ROW + (c << 4)));
-            }
+        for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-                    acc_up[mi][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[mi], xf[tb],
-                                                                             acc_up[mi][tb], 0, 0, 0);
-        }
+            for (int nj = 0; nj < 2; ++nj)
+                acc_up[fb][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[fb], xf[nj], acc_up[fb][nj], 0, 0, 0);
     };
     // One down K step (16 rows of W2) on stage st, h slice q of the chunk.
-    // Weight fragments are read in groups of up to 4 column blocks to bound
-    // the live registers next to the 32 NFB accumulator registers.
     auto compute_down = [&](const char* st, int q) {
-        bf16x8_t hf[2];
+        bf16x8_t hf[RBW];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const int c = (2 * q + (lane >> 5)) ^ tok_swz16[tb];
-            hf[tb] = __builtin_bit_cast(bf16x8_t,
-                                        *(const u32x4_t*)(hbuf + tok_off[tb] * H_ROW + (c << 4)));
+        for (int j = 0; j < RBW; ++j) {
+            const int row = 32 * (rb0 + j) + xr;
+            const int c = (2 * q + (lane >> 5)) ^ swz16(row);
+            hf[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(hbuf + row * H_ROW + (c << 4)));
         }
-        constexpr int GRP = NFB < 4 ? NFB : 4;
 #pragma unroll
-        for (int f0 = 0; f0 < NFB; f0 += GRP) {
-            bf16x8_t wf[GRP];
+        for (int i = 0; i < CBW; ++i) {
+            const bf16x8_t wf = cat_bf16(read_tr(st + dn_off[i]), read_tr(st + dn_off[i] + 4 * DN_ROW));
 #pragma unroll
-            for (int i = 0; i < GRP && f0 + i < NFB; ++i)
-                wf[i] = cat_bf16(read_tr(st + dn_off(f0 + i, 0)), read_tr(st + dn_off(f0 + i, 1)));
-#pragma unroll
-            for (int i = 0; i < GRP && f0 + i < NFB; ++i)
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-                    acc_y[f0 + i][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        wf[i], hf[tb], acc_y[f0 + i][tb], 0, 0, 0);
+            for (int j = 0; j < RBW; ++j)
+                acc_y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, hf[j], acc_y[i][j], 0, 0, 0);
         }
     };
     // h = silu(g) * u for the chunk, bf16, into hbuf (token rows, K-contiguous).
-    // acc_up[mi][tb] element v of lane l: token 32 tb + l%32, h column
-    // 32 w + 8 (v/4) + 4 (l/32) + v%4 (g for mi = 0, u for mi = 1).
+    // acc_up[fb][nj] element v of lane l: token 32 nj + l%32, h column
+    // 32 w + 16 fb + 8 (v/4) + 4 (l/32) + v%4 for v < 8 (g), its u at v + 8.
     auto write_h = [&]() {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+        for (int nj = 0; nj < 2; ++nj) {
+            const int t = 32 * nj + xr;
 #pragma unroll
-            for (int vg = 0; vg < 4; ++vg) {
-                const f32x16_t& g = acc_up[0][tb];
-                const f32x16_t& u = acc_up[1][tb];
-                const int v = 4 * vg;
-                const int c = (4 * wave + vg) ^ tok_swz16[tb];
-                *(uint2*)(hbuf + tok_off[tb] * H_ROW + (c << 4) + 8 * (lane >> 5)) =
-                    make_uint2(pack_bf16(silu_mul(g[v], u[v]), silu_mul(g[v + 1], u[v + 1])),
-                               pack_bf16(silu_mul(g[v + 2], u[v + 2]), silu_mul(g[v + 3], u[v + 3])));
+            for (int fb = 0; fb < 2; ++fb) {
+                const f32x16_t& c = acc_up[fb][nj];
+#pragma unroll
+                for (int vg = 0; vg < 2; ++vg) {
+                    const int v = 4 * vg;
+                    const int ch = (4 * wave + 2 * fb + vg) ^ swz16(t);
+                    *(uint2*)(hbuf + t * H_ROW + (ch << 4) + 8 * (lane >> 5)) =
+                        make_uint2(pack_bf16(silu_mul(c[v], c[v + 8]), silu_mul(c[v + 1], c[v + 9])),
+                                   pack_bf16(silu_mul(c[v + 2], c[v + 10]), silu_mul(c[v + 3], c[v + 11])));
+                }
             }
+        }
     };
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
-    // ---- stage stream: per chunk KU up steps then DN_STEPS down steps (an
-    // even count, so chunk step i always uses buffer i % 2); the loads of
-    // step i+1 are in flight while step i computes.  After the very last step
-    // the last down stage is reloaded into the idle buffer instead of
-    // branching around the loads.
-    issue_up(0, 0, lds0);
-    wait_vmem();
-    __syncthreads();
-    for (int c = 0; c < NC; ++c) {
+    // ---- step s (buffer s % 4): wait until stage s has landed (stages s+1
+    // and s+2 of this wavefront may still be in flight) and every LDS access
+    // of the previous step is done; barrier; issue stage s + 3 into the
+    // buffer of stage s - 1 (free: its last readers finished before this
+    // barrier); compute stage s.  Each chunk runs its KU up steps, writes h,
+    // then its down steps (16, or 8 for a last chunk of 128 columns); every
+    // count is a multiple of 4, so every phase starts in buffer 0 and the
+    // buffers are named statically.  The barrier of the first down step
+    // orders the h writes before the down steps' reads, and the barriers of
+    // the next chunk's up phase order those reads before the next write.
+    auto begin_step = [&](int s, char* dma) {
+        wait_vm(loads_of(s + 1) + loads_of(s + 2));
+        __builtin_amdgcn_s_barrier();
+        fence();
+        issue(s + 3, dma);
+    };
+    issue(0, st0);
+    issue(1, st1);
+    issue(2, st2);
+    for (int c = 0; c < NCH; ++c) {
+        const int s0 = c * SPC;
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) acc_up[mi][0] = acc_up[mi][1] = f32x16_t{};
-        for (int s = 0; s < KU; s += 2) {
-            issue_up(c, s + 1, lds1);
+        for (int fb = 0; fb < 2; ++fb) acc_up[fb][0] = acc_up[fb][1] = f32x16_t{};
+        for (int u = 0; u < KU; u += 4) {
+            begin_step(s0 + u, st3);
+            compute_up(st0);
             fence();
-            compute_up(lds0);
+            begin_step(s0 + u + 1, st0);
+            compute_up(st1);
             fence();
-            wait_vmem();
-            __syncthreads();
-            if (s + 2 < KU) issue_up(c, s + 2, lds0);
-            else issue_down(c, 0, lds0);
+            begin_step(s0 + u + 2, st1);
+            compute_up(st2);
             fence();
-            compute_up(lds1);
+            begin_step(s0 + u + 3, st2);
+            compute_up(st3);
             fence();
-            wait_vmem();
-            __syncthreads();
         }
         write_h();
-        __syncthreads();
-        for (int q = 0; q < DN_STEPS; q += 2) {
-            issue_down(c, q + 1, lds1);
+        const int ds = half && c == NCH - 1 ? DN_STEPS / 2 : DN_STEPS;
+        const int qr = rot * (ds / 8);
+        for (int q = 0; q < ds; q += 4) {
+            begin_step(s0 + KU + q, st3);
+            compute_down(st0, (q + qr) % ds);
             fence();
-            compute_down(lds0, q);
+            begin_step(s0 + KU + q + 1, st0);
+            compute_down(st1, (q + 1 + qr) % ds);
             fence();
-            wait_vmem();
-            __syncthreads();
-            if (q + 2 < DN_STEPS) issue_down(c, q + 2, lds0);
-            else if (c + 1 < NC) issue_up(c + 1, 0, lds0);
-            else issue_down(c, DN_STEPS - 1, lds0);
+            begin_step(s0 + KU + q + 2, st1);
+            compute_down(st2, (q + 2 + qr) % ds);
             fence();
-            compute_down(lds1, q + 1);
+            begin_step(s0 + KU + q + 3, st2);
+            compute_down(st3, (q + 3 + qr) % ds);
             fence();
-            wait_vmem();
-            __syncthreads();
         }
     }
+    wait_vm(0);
 
-    // ---- epilogue: acc_y[fb][tb] element v of lane l: token 32 tb + l%32,
-    // output column WCOLS w + 32 fb + 8 (v/4) + 4 (l/32) + v%4.
+    // ---- epilogue: acc_y[i][j] element v of lane l: token 32 (rb0 + j) + l%32,
+    // output column 32 (cb0 + i) + 8 (v/4) + 4 (l/32) + v%4.
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const int t = 32 * tb + (lane & 31);
+    for (int j = 0; j < RBW; ++j) {
+        const int t = 32 * (rb0 + j) + xr;
         if (t >= valid_rows) continue;
         uint16_t* out = a.Y + (tile_r0 + t) * (int64_t)D;
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb)
+        for (int i = 0; i < CBW; ++i)
 #pragma unroll
             for (int vg = 0; vg < 4; ++vg) {
-                const int col = WCOLS * wave + 32 * fb + 8 * vg + 4 * (lane >> 5);
-                const f32x16_t& y = acc_y[fb][tb];
+                const int col = 32 * (cb0 + i) + 8 * vg + 4 * (lane >> 5);
+                const f32x16_t& y = acc_y[i][j];
                 const int v = 4 * vg;
                 *(uint2*)(out + col) = make_uint2(pack_bf16(y[v], y[v + 1]),
                                                   pack_bf16(y[v + 2], y[v + 3]));

@@ -65,6 +65,12 @@ __device__ __forceinline__ void load_lds16(const void* g, char* lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
 }
 
+// The same with the non-temporal cache policy: for data read once per use
+// that should not displace reused lines from the L2.
+__device__ __forceinline__ void load_lds16_nt(const void* g, char* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 2);
+}
+
 // s_waitcnt immediate (gfx9 encoding): at most vm vector-memory and lgkm
 // LDS/scalar operations of this wavefront outstanding (vm up to 63, lgkm up
 // to 15; 15 leaves the LDS counter unchecked).
