@@ -28,7 +28,21 @@
 //  * tiles run m-major (all column slabs of one row tile back to back), so
 //    the workgroups of one XCD stream whole weight rows of one group in step
 //    and share that group's token rows through the XCD's L2.
+//
+// Routed form (ROUTE, up to kPermuteSingleMax slots): the counting sort of
+// the permute runs inside this kernel, so the forward needs no permute
+// launch.  Workgroup (g, nt) is fixed by its block index alone: it issues
+// its weight slab's first stages at entry, before it knows anything about
+// the routing, then reads the slots' expert ids, counts the slots of lower
+// experts (its group's first sorted row) and ranks its own group's slots in
+// slot order -- the same stable order as the permute -- into an LDS row
+// table, from which the token rows are gathered.  A group with more rows
+// than a tile walks its row tiles in turn.  One more workgroup, beside the
+// GEMM workgroups, runs the permute's one-workgroup counting sort and writes
+// counts, offsets, both row-tile prefixes, perm, inv and the invalid-slot
+// count, which only the later launches read.
 #include "mfma_common.h"
+#include "permute_device.h"
 
 namespace moe {
 namespace {
@@ -47,7 +61,7 @@ constexpr int W_BYTES = BK * W_ROW;    // 16 KiB
 static_assert(NT == 256 && FB == 4 && BK == 64 && W_BYTES == 16384, "index math below assumes these");
 
 struct SlabArgs {
-    GroupArgs g;
+    GroupArgs g;              // ROUTE: only S, T, E, k, G are read
     const uint16_t* x;        // [T, D]
     const uint16_t* w1;       // [E, D, F]
     const uint16_t* w3;
@@ -56,65 +70,83 @@ struct SlabArgs {
     uint16_t* h;              // [R, F]
     int D, F;
     int n_tiles;
+    // ROUTE only: the routing in, the permute's outputs out
+    const int32_t* idx;       // [S] expert id of each slot
+    int32_t *counts, *offsets, *tile_off, *tile_off64, *perm, *inv, *err;
+    int tile_rows;            // row-tile height of tile_off (32 RB)
+    int sh_tiles;             // row tiles of the shared group (one workgroup per column slab each)
 };
 
-template <int RB>
+constexpr int kRouteSlotsPerThread = kPermuteSingleMax / 256;
+
+template <int RB, bool ROUTE>
 __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a) {
     constexpr int TT = 32 * RB;
     constexpr int X_BYTES = TT * X_ROW;
     constexpr int STAGE_BYTES = X_BYTES + W_BYTES;
     constexpr int PER_STAGE = RB + W_BYTES / 1024 / 4;     // global_load_lds per wavefront per stage
+    // LDS of the in-kernel routing: the row table and reduction slots
+    constexpr int ROUTE_LDS = ROUTE ? 4 * (TT + 16) : 0;
     // Four stage buffers when they fit in LDS, else three; separate LDS
     // objects so the compiler sees that reads of one do not alias the
     // asynchronous loads into another.
-    constexpr int NS = 4 * STAGE_BYTES <= 160 * 1024 ? 4 : 3;
-    constexpr bool HALF = RB >= 7;             // operands read half a stage at a time
+    constexpr int NS = 4 * STAGE_BYTES + ROUTE_LDS <= 160 * 1024 ? 4 : 3;
+    // operands read half a stage at a time: tall tiles, and three-stage rings
+    // (the routed form at RB 6, whose LDS holds only three)
+    constexpr bool HALF = RB >= 7 || NS == 3;
     __shared__ __attribute__((aligned(1024))) char st0[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st3[NS == 4 ? STAGE_BYTES : 16];
+    __shared__ int32_t rtab[ROUTE ? TT : 1];                 // slot of each row of the tile
+    __shared__ int32_t rred[ROUTE ? 16 : 1];
 
+    // ROUTE: the last workgroup of the grid does the counting sort's
+    // bookkeeping for the later launches (counts, offsets, both row-tile
+    // prefixes, perm, inv, the invalid-slot count), in parallel with the
+    // GEMM workgroups, with the stage buffers as its scratch.
+    if (ROUTE && blockIdx.x == gridDim.x - 1) {
+        static_assert(4 * (6 * kRouteMaxExperts + 1) <= STAGE_BYTES, "the sort's scratch fits a stage");
+        int32_t* scratch = (int32_t*)st0;
+        permute_dev::permute_one_workgroup<NT>(
+            a.idx, a.g.S, a.g.E, permute_dev::TileSpec{a.tile_rows, a.tile_off},
+            permute_dev::TileSpec{64, a.tile_off64}, a.g.G > a.g.E ? a.g.T : 0, a.counts, a.offsets,
+            a.perm, a.inv, a.err, scratch, scratch + kMaxExperts + 1, scratch + 2 * kMaxExperts + 1);
+        return;
+    }
     const int K = a.D, N = a.F;
-    // the group lookup's loads go out with the tile count's (one round trip)
-    const GroupBlock gblock = load_group_block(a.g, 0, threadIdx.x & 63);
-    const int total = a.g.tile_off[a.g.G];
-    const int id = xcd_remap_work(blockIdx.x, total * a.n_tiles);
-    if (id < 0) return;
-    const int mt = id / a.n_tiles, nt = id - mt * a.n_tiles;     // m-major
+    const int KT = K / BK;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const TileGroup tg = find_tile_group(a.g, mt, TT, lane, gblock);
-    const int grp = tg.grp;
-    const bool shared = grp >= a.g.E;
-    const int64_t tile_r0 = tg.tile_r0;
-    const int valid_rows = tg.valid_rows;
-    if (valid_rows <= 0) return;
-
-    // ---- token rows: DMA instruction j (0 .. RB-1) of wavefront w fills rows
-    // 8 q .. 8 q + 7 with q = w + 4 j; lane -> row 8 q + lane/8, physical
-    // chunk lane%8 holding logical chunk (lane%8) ^ swz8(row).
-    const char* x_src[RB];
-    {
-        int64_t src_row[RB];
-#pragma unroll
-        for (int j = 0; j < RB; ++j)
-            src_row[j] = tile_r0 + min(8 * (wave + 4 * j) + (lane >> 3), valid_rows - 1);
-        if (!shared) {
-            int32_t slot[RB];
-#pragma unroll
-            for (int j = 0; j < RB; ++j) slot[j] = a.g.perm[src_row[j]];
-#pragma unroll
-            for (int j = 0; j < RB; ++j) src_row[j] = slot[j] / a.g.k;
-        } else {
-#pragma unroll
-            for (int j = 0; j < RB; ++j) src_row[j] -= a.g.S;
-        }
-#pragma unroll
-        for (int j = 0; j < RB; ++j) {
-            const int row = 8 * (wave + 4 * j) + (lane >> 3);
-            x_src[j] = (const char*)(a.x + src_row[j] * (int64_t)K + 8 * ((lane & 7) ^ swz8(row)));
-        }
+    int grp, nt;
+    bool shared;
+    int64_t tile_r0 = 0;
+    int valid_rows = 0;
+    int sh_rt = 0;                    // ROUTE: row tile of a shared-group workgroup
+    if constexpr (ROUTE) {
+        // (group, column slab) from the block index alone, m-major
+        const int id = xcd_remap(blockIdx.x, (a.g.E + a.sh_tiles) * a.n_tiles);
+        const int m = id / a.n_tiles;
+        nt = id - m * a.n_tiles;
+        shared = m >= a.g.E;
+        grp = shared ? a.g.E : m;
+        sh_rt = m - a.g.E;
+    } else {
+        // the group lookup's loads go out with the tile count's (one round trip)
+        const GroupBlock gblock = load_group_block(a.g, 0, lane);
+        const int total = a.g.tile_off[a.g.G];
+        const int id = xcd_remap_work(blockIdx.x, total * a.n_tiles);
+        if (id < 0) return;
+        const int mt = id / a.n_tiles;
+        nt = id - mt * a.n_tiles;     // m-major
+        const TileGroup tg = find_tile_group(a.g, mt, TT, lane, gblock);
+        grp = tg.grp;
+        shared = grp >= a.g.E;
+        tile_r0 = tg.tile_r0;
+        valid_rows = tg.valid_rows;
+        if (valid_rows <= 0) return;
     }
+
     // ---- weight slab [64 k][128 features]: DMA instruction j (0..3) of
     // wavefront w fills k rows 4 q .. 4 q + 3 with q = w + 4 j; lane -> k row
     // 4 q + lane/16, physical chunk lane%16 holding logical chunk
@@ -133,15 +165,164 @@ __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a)
         w_src[j] = (const char*)(base + (int64_t)kr * N + col);
     }
     const int64_t w_step = (int64_t)BK * N * 2;
-
-    auto issue = [&](int kt, char* st) {
-#pragma unroll
-        for (int j = 0; j < RB; ++j)
-            load_lds16(x_src[j] + (int64_t)kt * X_ROW, st + 8 * (wave + 4 * j) * X_ROW);
+    auto issue_w = [&](int kt, char* st) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             load_lds16(w_src[j] + kt * w_step, st + X_BYTES + 4 * (wave + 4 * j) * W_ROW);
     };
+
+    // ---- ROUTE: the weight slab's first stages go out now, before the routing.
+    int n_rows = 0, row0 = 0, eq_base = 0, s0 = 0;
+    uint32_t eq_mask = 0;
+    // A barrier that waits for this wavefront's LDS accesses only (a plain
+    // __syncthreads would also drain the weight stages in flight).
+    auto lds_barrier = [] {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+        __builtin_amdgcn_s_barrier();
+    };
+    if constexpr (ROUTE) {
+        auto issue_w_first = [&] {
+#pragma unroll
+            for (int i = 0; i < NS - 1; ++i) issue_w(min(i, KT - 1), i == 0 ? st0 : i == 1 ? st1 : st2);
+        };
+        if (shared) issue_w_first();
+        if (!shared) {
+            // The slots' expert ids come into the last stage buffer (not used
+            // before the first K step) by LDS DMA ahead of the weight stages:
+            // DMA loads retire in order, so once at most the weight stages'
+            // loads are outstanding the ids are in, and the routing below
+            // runs while the weights are still in flight.  Instruction i
+            // (i = w, w + 4, ...) covers slots 64 i .. 64 i + 63, 4 bytes a lane
+            // (addresses clamped to the last slot).
+            const int S = (int)a.g.S, E = a.g.E;
+            char* ids_lds = NS == 4 ? st3 : st2;
+            for (int i = wave; i < (S + 63) / 64; i += 4)
+                __builtin_amdgcn_global_load_lds(a.idx + min(64 * i + lane, S - 1),
+                                                 (lds_void_t*)(ids_lds + 256 * i), 4, 0, 0);
+            issue_w_first();
+            // (Pulling further weight stages into L2 here, while the routing
+            // waits on memory, measured slower: every DMA instruction must be
+            // issued into the busy memory pipe before the ids can be used.)
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 1) * 4, 15));   // the ids are in
+            __builtin_amdgcn_s_barrier();
+            // Slots 16 tid .. 16 tid + 15 of this thread, in slot order across
+            // the workgroup.  Keys: the expert id when valid, E when out of
+            // range, E + 1 past the last slot.
+            s0 = kRouteSlotsPerThread * tid;
+            int key[kRouteSlotsPerThread];
+#pragma unroll
+            for (int q = 0; q < kRouteSlotsPerThread / 4; ++q) {
+                const u32x4_t v = *(const u32x4_t*)(ids_lds + 4 * (s0 + 4 * q));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = (int)v[i];
+                    key[4 * q + i] = s0 + 4 * q + i >= S ? E + 1 : (e >= 0 && e < E ? e : E);
+                }
+            }
+            int lt = 0;
+#pragma unroll
+            for (int j = 0; j < kRouteSlotsPerThread; ++j) {
+                lt += key[j] < grp ? 1 : 0;
+                eq_mask |= (key[j] == grp ? 1u : 0u) << j;
+            }
+            // the group's first sorted row (slots of lower experts), its row
+            // count (slots of this expert) and this thread's first rank
+            const int eqc = __popc(eq_mask);
+            int inc = eqc;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int t = __shfl_up(inc, d);
+                if (lane >= d) inc += t;
+            }
+            int ltw = lt;
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) ltw += __shfl_xor(ltw, d);
+            if (lane == 63) rred[wave] = inc;
+            if (lane == 0) rred[4 + wave] = ltw;
+            lds_barrier();
+            int before = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                before += w < wave ? rred[w] : 0;
+                n_rows += rred[w];
+                row0 += rred[4 + w];
+            }
+            eq_base = before + inc - eqc;
+        }
+    }
+    const int ntile = !ROUTE ? 1 : shared ? 1 : (n_rows + TT - 1) / TT;
+    if (ntile == 0) {
+        wait_vmem();                  // no rows: drain the weight stages before leaving
+        return;
+    }
+    for (int rt = 0; rt < ntile; ++rt) {
+    if constexpr (ROUTE) {
+        if (rt > 0) __syncthreads();  // every wavefront is done with the previous tile's LDS
+        if (shared) {
+            tile_r0 = a.g.S + (int64_t)sh_rt * TT;
+            valid_rows = min(TT, (int)(a.g.T - (int64_t)sh_rt * TT));
+        } else {
+            tile_r0 = row0 + rt * TT;
+            valid_rows = min(TT, n_rows - rt * TT);
+            int r = eq_base;
+#pragma unroll
+            for (int j = 0; j < kRouteSlotsPerThread; ++j)
+                if ((eq_mask >> j) & 1u) {
+                    if (r >= rt * TT && r < rt * TT + TT) rtab[r - rt * TT] = s0 + j;
+                    ++r;
+                }
+            lds_barrier();
+        }
+    }
+
+    // ---- token rows: DMA instruction j (0 .. RB-1) of wavefront w fills rows
+    // 8 q .. 8 q + 7 with q = w + 4 j; lane -> row 8 q + lane/8, physical
+    // chunk lane%8 holding logical chunk (lane%8) ^ swz8(row).  Routed rows
+    // gather token slot / k, the slot from perm (or, routed in this kernel,
+    // from the row table); shared rows read token row - S.
+    const char* x_src[RB];
+    {
+        int64_t src_row[RB];
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            const int row = min(8 * (wave + 4 * j) + (lane >> 3), valid_rows - 1);
+            src_row[j] = ROUTE && !shared ? row : tile_r0 + row;
+        }
+        if (!shared) {
+            int32_t slot[RB];
+#pragma unroll
+            for (int j = 0; j < RB; ++j) slot[j] = ROUTE ? rtab[src_row[j]] : a.g.perm[src_row[j]];
+#pragma unroll
+            for (int j = 0; j < RB; ++j) src_row[j] = slot[j] / a.g.k;
+        } else {
+#pragma unroll
+            for (int j = 0; j < RB; ++j) src_row[j] -= a.g.S;
+        }
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            const int row = 8 * (wave + 4 * j) + (lane >> 3);
+            x_src[j] = (const char*)(a.x + src_row[j] * (int64_t)K + 8 * ((lane & 7) ^ swz8(row)));
+        }
+    }
+    auto issue_x = [&](int kt, char* st) {
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+            load_lds16(x_src[j] + (int64_t)kt * X_ROW, st + 8 * (wave + 4 * j) * X_ROW);
+    };
+    auto issue = [&](int kt, char* st) {
+        issue_x(kt, st);
+        issue_w(kt, st);
+    };
+    // The prologue's stages: only the token rows when the weights went out at
+    // entry.  Then stage 0 has landed once at most the later stages' token
+    // loads are outstanding (loads complete in order); that stricter count
+    // is also right for the usual order.
+    const bool w_early = ROUTE && rt == 0;
+    auto issue_first = [&](int kt, char* st) {
+        if (w_early) issue_x(kt, st);
+        else issue(kt, st);
+    };
+    constexpr int FIRST_WAIT = ROUTE ? (NS - 2) * RB : (NS - 2) * PER_STAGE;
 
     // ---- operand reads.  Weights (A), transposed: lane = 16 G + s reads
     // k = 16 ks + 8 (G>>1) + 4 r + s/4, feature 32 w + 16 (G&1) + 4 (s&3).
@@ -199,7 +380,6 @@ __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a)
     // re-read the last stage (into buffers never computed on), so the number
     // of loads per stage stays fixed; operands read past the last stage are
     // never used.
-    const int KT = K / BK;
     constexpr int WAIT_N = (NS - 3) * PER_STAGE;
     auto wait_stage = [] {
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(WAIT_N, 0));
@@ -227,12 +407,15 @@ __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a)
         Frags fa, fb;
 #pragma unroll
         for (int i = 0; i < NS - 1; ++i)
-            issue(min(i, KT - 1), i == 0 ? st0 : i == 1 ? st1 : st2);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * PER_STAGE, 15));   // stage 0 landed
+            issue_first(min(i, KT - 1), i == 0 ? st0 : i == 1 ? st1 : st2);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(FIRST_WAIT, 15));   // stage 0 landed
         __builtin_amdgcn_s_barrier();
         fence();
         read_frags(st0, fa);
         fence();
+        // weights issued first: stage 1 has landed once at most stage 2's
+        // token loads are outstanding (the steps' own waits allow a whole stage)
+        if (ROUTE && NS == 4) __builtin_amdgcn_s_waitcnt(waitcnt_imm(RB, 15));
         int kt = 0;
         if constexpr (NS == 4) {
             // buffers rotate with period 4, operand sets with period 2
@@ -329,8 +512,8 @@ __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a)
         static_assert(!HALF || NS == 3, "tall tiles use three stages");
         Half h0, h1;
 #pragma unroll
-        for (int i = 0; i < NS - 1; ++i) issue(min(i, KT - 1), i == 0 ? st0 : st1);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * PER_STAGE, 15));   // stage 0 landed
+        for (int i = 0; i < NS - 1; ++i) issue_first(min(i, KT - 1), i == 0 ? st0 : st1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(FIRST_WAIT, 15));   // stage 0 landed
         __builtin_amdgcn_s_barrier();
         fence();
         read_half(st0, 0, h0);
@@ -368,6 +551,9 @@ __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a)
                            pack_bf16(silu_mul(c[v + 2], c[v + 10]), silu_mul(c[v + 3], c[v + 11])));
         }
     }
+#pragma unroll
+    for (int j = 0; j < RB; ++j) acc[j] = f32x16_t{};
+    }   // row tiles
 }
 
 template <int RB>
@@ -375,7 +561,12 @@ hipError_t launch_rb(const SlabArgs& a, hipStream_t s) {
     const int64_t rows = a.g.S + (a.g.G > a.g.E ? a.g.T : 0);
     const int64_t m_upper = (rows + 32 * RB - 1) / (32 * RB) + a.g.G;
     const int64_t blocks = m_upper * a.n_tiles;
-    up_swiglu_slab_kernel<RB><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    if (a.idx) {
+        // one more workgroup than tiles: the sort's bookkeeping
+        up_swiglu_slab_kernel<RB, true><<<(unsigned)((a.g.E + a.sh_tiles) * a.n_tiles + 1), NT, 0, s>>>(a);
+    } else {
+        up_swiglu_slab_kernel<RB, false><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
@@ -399,12 +590,35 @@ int slab_row_blocks(int64_t S, int64_t shared_rows, int E, int F) {
     return rb0;
 }
 
+namespace {
+hipError_t launch_slab(const SlabArgs& a, int rb, hipStream_t s);
+}  // namespace
+
 hipError_t launch_up_swiglu_bf16_slab(const GroupArgs& g, int rb, const void* x, const void* W1,
                                       const void* W3, const void* Ws1, const void* Ws3, void* h,
                                       int D, int F, hipStream_t s) {
     SlabArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, (uint16_t*)h, D, F,
                (F + TCOL - 1) / TCOL};
+    return launch_slab(a, rb, s);
+}
+
+hipError_t launch_up_swiglu_bf16_slab_routed(const GroupArgs& g, int rb, const int32_t* idx,
+                                             int32_t* counts, int32_t* offsets, int32_t* tile_off,
+                                             int32_t* tile_off64, int32_t* perm, int32_t* inv,
+                                             int32_t* err, const void* x, const void* W1,
+                                             const void* W3, const void* Ws1, const void* Ws3,
+                                             void* h, int D, int F, hipStream_t s) {
+    if (g.S > kPermuteSingleMax || g.S < 1 || g.E > kRouteMaxExperts) return hipErrorInvalidValue;
+    SlabArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
+               (const uint16_t*)Ws1, (const uint16_t*)Ws3, (uint16_t*)h, D, F,
+               (F + TCOL - 1) / TCOL, idx, counts, offsets, tile_off, tile_off64, perm, inv, err,
+               32 * rb, g.G > g.E ? (int)((g.T + 32 * rb - 1) / (32 * rb)) : 0};
+    return launch_slab(a, rb, s);
+}
+
+namespace {
+hipError_t launch_slab(const SlabArgs& a, int rb, hipStream_t s) {
     switch (rb) {
         case 1: return launch_rb<1>(a, s);
         case 2: return launch_rb<2>(a, s);
@@ -417,5 +631,6 @@ hipError_t launch_up_swiglu_bf16_slab(const GroupArgs& g, int rb, const void* x,
     }
     return hipErrorInvalidValue;
 }
+}  // namespace
 
 }  // namespace moe

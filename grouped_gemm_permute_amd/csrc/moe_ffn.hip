@@ -176,12 +176,17 @@ moe_status forward_impl(const void* x, const void* gate_w, const int32_t* topk_i
         return events ? hipEventRecord(events[i], stream) : hipSuccess;
     };
     if (mark(0) != hipSuccess) return MOE_ERR_HIP;
+    // Small chunks with at most kPermuteSingleMax slots: the up GEMM does the
+    // counting sort itself (no permute launch); it writes the same outputs.
+    const bool sort_in_up = dtype == MOE_BF16 && variant == MOE_VARIANT_UNFUSED && L.small_tiles &&
+                            S <= kPermuteSingleMax && E <= kRouteMaxExperts;
     if (gate_w) {
-        const bool fine = permute_fine_ok(S, E, kRouterSub);
+        const bool fine = !sort_in_up && permute_fine_ok(S, E, kRouterSub);
         if (launch_router(x, gate_w, T, D, E, k, dtype == MOE_BF16, (int32_t*)topk_idx,
                           (float*)topk_w, fine ? hist : nullptr, stream) != hipSuccess)
             return MOE_ERR_HIP;
-        if (fine) {
+        if (sort_in_up) {
+        } else if (fine) {
             if (launch_permute_from_hist(topk_idx, S, E, L.tile_rows, has_shared ? T : 0, counts,
                                          offsets, tile_off, perm, inv, err, hist, kRouterSub, stream,
                                          64, tile_off64) != hipSuccess)
@@ -191,7 +196,8 @@ moe_status forward_impl(const void* x, const void* gate_w, const int32_t* topk_i
                                   tile_off64) != hipSuccess) {
             return MOE_ERR_HIP;
         }
-    } else if (launch_permute(topk_idx, S, E, L.tile_rows, has_shared ? T : 0, counts, offsets,
+    } else if (!sort_in_up &&
+               launch_permute(topk_idx, S, E, L.tile_rows, has_shared ? T : 0, counts, offsets,
                               tile_off, perm, inv, err, hist, L.hist_blocks, stream, 64,
                               tile_off64) != hipSuccess) {
         return MOE_ERR_HIP;
@@ -203,6 +209,11 @@ moe_status forward_impl(const void* x, const void* gate_w, const int32_t* topk_i
     if (variant == MOE_VARIANT_FUSED) {
         // one launch does up, SwiGLU and down; both timing marks follow it
         e = launch_fused_bf16(g, x, W1, W3, W2, Ws1, Ws3, Ws2, Y, D, F, stream);
+        if (e == hipSuccess) e = mark(2);
+    } else if (sort_in_up) {
+        e = launch_up_swiglu_bf16_slab_routed(g, L.tile_rows / 32, topk_idx, counts, offsets, tile_off,
+                                              tile_off64, perm, inv, err, x, W1, W3, Ws1, Ws3, h, D,
+                                              F, stream);
         if (e == hipSuccess) e = mark(2);
     } else if (dtype == MOE_BF16 && L.small_tiles) {
         e = launch_up_swiglu_bf16_slab(g, L.tile_rows / 32, x, W1, W3, Ws1, Ws3, h, D, F, stream);

@@ -59,12 +59,25 @@ constexpr int kSmallTileRows = 64;
 constexpr int kSlabMaxRowBlocks = 8;
 // Workgroups of one round of the slab kernel (one per compute unit).
 constexpr int kSlabRoundTiles = 256;
+// Largest expert count whose counting sort the small-chunk up GEMM runs itself.
+constexpr int kRouteMaxExperts = 512;
 // rb for S routed rows over E experts, shared_rows shared-expert rows (0:
 // none) and F output columns.
 int slab_row_blocks(int64_t S, int64_t shared_rows, int E, int F);
 hipError_t launch_up_swiglu_bf16_slab(const GroupArgs& g, int rb, const void* x, const void* W1,
                                       const void* W3, const void* Ws1, const void* Ws3, void* h,
                                       int D, int F, hipStream_t s);
+// The same with the counting sort of the permute done inside the kernel
+// (S = T*k <= kPermuteSingleMax, E <= kRouteMaxExperts): reads the expert id of
+// every slot and writes counts, offsets, tile_off (tile rows 32 rb),
+// tile_off64, perm, inv and err exactly as launch_permute would; g's
+// offsets, tile_off and perm are not read.
+hipError_t launch_up_swiglu_bf16_slab_routed(const GroupArgs& g, int rb, const int32_t* idx,
+                                             int32_t* counts, int32_t* offsets, int32_t* tile_off,
+                                             int32_t* tile_off64, int32_t* perm, int32_t* inv,
+                                             int32_t* err, const void* x, const void* W1,
+                                             const void* W3, const void* Ws1, const void* Ws3,
+                                             void* h, int D, int F, hipStream_t s);
 hipError_t launch_up_swiglu_bf16_small(const GroupArgs& g, const void* x, const void* W1,
                                        const void* W3, const void* Ws1, const void* Ws3, void* h,
                                        int D, int F, hipStream_t s);

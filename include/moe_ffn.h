@@ -153,7 +153,9 @@ moe_status moe_ffn_forward(const void *x, const int32_t *topk_idx, const float *
 
 /*
  * moe_ffn_forward plus per-stage timing: the same call, which also records
- * events[0] before the permute, events[1] after it, events[2] after the
+ * events[0] before the permute, events[1] after it (back to back when the
+ * small-chunk up GEMM does the counting sort itself: bf16, unfused, groups
+ * averaging under 256 rows, T*k <= 4096, E <= 512), events[2] after the
  * up+SwiGLU GEMM (the fused variant: after its single up-act-down kernel),
  * events[3] after the down GEMM (fused: immediately after events[2]) and
  * events[4] after the combine, all on `stream` (five caller-created
