@@ -41,7 +41,14 @@
 //  * tiles are numbered group-major and each XCD takes a contiguous range,
 //    so the workgroups of one XCD work on the same expert at the same time
 //    and share each weight chunk through that XCD's L2, each starting the
-//    chunk's steps at a different point.
+//    chunk's steps at a different point;
+//  * when the tiles are few (fused_splits), the chunks of each tile are
+//    shared out over `splits` workgroups: workgroup (tile, sp) runs chunks
+//    sp NCH / splits .. (sp + 1) NCH / splits - 1 and stores its fp32
+//    accumulator as plane sp of P; fused_reduce_kernel then adds the planes
+//    in plane order and rounds once to bf16 Y.  On the 16-expert layer with
+//    64 tokens per expert this takes the kernel from 16 workgroups and
+//    0.88 ms to 128 workgroups and 0.16 ms (measured).
 //
 // Measured on the 16384-token F > D workload (D 1024, F 4096, 16 experts):
 // the kernel stages ~27 MB per 64-row tile (each tile re-streams its
@@ -103,7 +110,10 @@ struct FusedArgs {
     const uint16_t* x;                     // [T, D]
     const uint16_t *W1, *W3, *W2;          // [E, D, F], [E, D, F], [E, F, D]
     const uint16_t *Ws1, *Ws3, *Ws2;       // shared expert or null
-    uint16_t* Y;                           // [R, D] bf16 expert outputs
+    uint16_t* Y;                           // [R, D] bf16 expert outputs (splits == 1)
+    float* P;                              // [splits][R][D] fp32 partial outputs (splits > 1)
+    int64_t R;
+    int splits;
     int D, F;
 };
 
@@ -132,10 +142,13 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
     const int F = a.F;
     const int NCH = (F + CH - 1) / CH;         // chunks; the last holds 128 columns when F % 256 != 0
     const bool half = F % CH != 0;
-    const int NSTEP = NCH * SPC - (half ? DN_STEPS / 2 : 0);
 
-    const int mt = xcd_remap_work(blockIdx.x, a.g.tile_off[a.g.G]);
-    if (mt < 0) return;
+    // work item = (tile mt, split sp): chunks c0 .. c1-1 of tile mt
+    const int work = xcd_remap_work(blockIdx.x, a.g.tile_off[a.g.G] * a.splits);
+    if (work < 0) return;
+    const int mt = work / a.splits, sp = work - mt * a.splits;
+    const int c0 = sp * NCH / a.splits, c1 = (sp + 1) * NCH / a.splits;
+    const int NSTEP = (c1 - c0) * SPC - (half && c1 == NCH ? DN_STEPS / 2 : 0);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const TileGroup tg = find_tile_group(a.g, mt, TT, lane);
@@ -204,8 +217,8 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
             }
         }
     };
-    // stage s of the stream: chunk c = s / SPC, up step (s % SPC) < KU, else
-    // down step (s % SPC) - KU.  Stages past the last re-load the last one
+    // stage s of the stream: chunk c = c0 + s / SPC, up step (s % SPC) < KU,
+    // else down step (s % SPC) - KU.  Stages past the last re-load the last one
     // (a down stage, into a buffer never computed on), so every stage issues
     // its kind's fixed number of loads.
     // Neighbouring tiles (which run at the same time on one XCD) walk a
@@ -216,7 +229,7 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
     const int rot = mt % 8;
     auto issue = [&](int s, char* st) {
         s = min(s, NSTEP - 1);
-        const int c = s / SPC, r = s - c * SPC;
+        const int r = s - (s / SPC) * SPC, c = c0 + s / SPC;
         if (r < KU) issue_up(c, (r + rot * (KU / 8)) % KU, st);
         else {
             const int dsn = half && c == NCH - 1 ? DN_STEPS / 2 : DN_STEPS;
@@ -331,8 +344,8 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
     issue(0, st0);
     issue(1, st1);
     issue(2, st2);
-    for (int c = 0; c < NCH; ++c) {
-        const int s0 = c * SPC;
+    for (int c = c0; c < c1; ++c) {
+        const int s0 = (c - c0) * SPC;
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) acc_up[fb][0] = acc_up[fb][1] = f32x16_t{};
         for (int u = 0; u < KU; u += 4) {
@@ -371,6 +384,24 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
 
     // ---- epilogue: acc_y[i][j] element v of lane l: token 32 (rb0 + j) + l%32,
     // output column 32 (cb0 + i) + 8 (v/4) + 4 (l/32) + v%4.
+    if (a.splits > 1) {
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+            const int t = 32 * (rb0 + j) + xr;
+            if (t >= valid_rows) continue;
+            float* out = a.P + ((int64_t)sp * a.R + tile_r0 + t) * D;
+#pragma unroll
+            for (int i = 0; i < CBW; ++i)
+#pragma unroll
+                for (int vg = 0; vg < 4; ++vg) {
+                    const int col = 32 * (cb0 + i) + 8 * vg + 4 * (lane >> 5);
+                    const f32x16_t& y = acc_y[i][j];
+                    const int v = 4 * vg;
+                    *(float4*)(out + col) = make_float4(y[v], y[v + 1], y[v + 2], y[v + 3]);
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < RBW; ++j) {
         const int t = 32 * (rb0 + j) + xr;
@@ -389,16 +420,57 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
     }
 }
 
+// Y[r] = bf16(P[0][r] + P[1][r] + ... + P[splits-1][r]), fp32 sums in
+// plane order (reproducible); one thread per 8 columns of a row, D % 8 == 0.
+// Rows no tile covers (slots with invalid expert ids) hold unused values.
+__global__ __launch_bounds__(256) void fused_reduce_kernel(const float* __restrict__ P, int splits,
+                                                          int64_t R, int D, uint16_t* __restrict__ Y) {
+    const int cg = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= R * cg) return;
+    const int64_t r = gid / cg;
+    const int c = (int)(gid - r * cg) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < splits; ++p) {
+        typedef __attribute__((ext_vector_type(4))) float f4;
+        const f4* src = (const f4*)(P + ((int64_t)p * R + r) * D + c);
+        const f4 lo = __builtin_nontemporal_load(src), hi = __builtin_nontemporal_load(src + 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[i] += lo[i];
+            acc[4 + i] += hi[i];
+        }
+    }
+    *(uint4*)(Y + r * D + c) = make_uint4(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
+                                          pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7]));
+}
+
 }  // namespace
+
+int fused_splits(int64_t R, int F) {
+    const int chunks = (F + CH - 1) / CH;
+    const int64_t tiles = (R + TT - 1) / TT;
+    int s = 1;
+    while (2 * s <= chunks && tiles * 2 * s <= kFusedSplitTarget) s *= 2;
+    return s;
+}
+
+hipError_t launch_fused_reduce(const float* P, int splits, int64_t R, int D, void* Y, hipStream_t s) {
+    const int64_t threads = R * (D / 8);
+    if (threads == 0) return hipSuccess;
+    fused_reduce_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(P, splits, R, D, (uint16_t*)Y);
+    return hipGetLastError();
+}
 
 hipError_t launch_fused_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
                              const void* W2, const void* Ws1, const void* Ws3, const void* Ws2,
-                             void* Y, int D, int F, hipStream_t s) {
+                             void* Y, float* P, int splits, int64_t R, int D, int F, hipStream_t s) {
+    if (splits < 1 || splits > (F + CH - 1) / CH || (splits > 1 && !P)) return hipErrorInvalidValue;
     FusedArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
                 (const uint16_t*)W2, (const uint16_t*)Ws1, (const uint16_t*)Ws3,
-                (const uint16_t*)Ws2, (uint16_t*)Y, D, F};
+                (const uint16_t*)Ws2, (uint16_t*)Y, P, R, splits, D, F};
     const int64_t rows = g.S + (g.G > g.E ? g.T : 0);
-    const unsigned blocks = (unsigned)((rows + TT - 1) / TT + g.G);
+    const unsigned blocks = (unsigned)(((rows + TT - 1) / TT + g.G) * splits);
     switch (D / 128) {
         case 1: fused_up_act_down_kernel<1><<<grid_for_work(blocks), NT, 0, s>>>(a); break;
         case 2: fused_up_act_down_kernel<2><<<grid_for_work(blocks), NT, 0, s>>>(a); break;

@@ -57,7 +57,11 @@ moe_status make_layout(int64_t T, int D, int F, int E, int k, int has_shared, mo
     // multi-block permute histogram; kRouterSub columns per block when the
     // router writes it
     L->hist = take(sizeof(int32_t) * (size_t)(E + 1) * (size_t)nb * kRouterSub);
-    L->h = take(fused ? 0 : esize * (size_t)R * (size_t)F);   // the fused variant keeps h on chip
+    // The fused variant keeps h on chip; when it splits the tiles' F chunks
+    // over several workgroups this slot holds their fp32 partial outputs.
+    const int splits = fused ? fused_splits(R, F) : 1;
+    L->h = take(fused ? (splits > 1 ? sizeof(float) * (size_t)splits * (size_t)R * (size_t)D : 0)
+                      : esize * (size_t)R * (size_t)F);
     L->Y = take(esize * (size_t)R * (size_t)D);
     L->total = off;
     // bf16 unfused: groups averaging under one 256-row tile are bound by
@@ -207,9 +211,13 @@ moe_status forward_impl(const void* x, const void* gate_w, const int32_t* topk_i
     GroupArgs g{offsets, tile_off, perm, S, T, E, k, E + (has_shared ? 1 : 0)};
     hipError_t e;
     if (variant == MOE_VARIANT_FUSED) {
-        // one launch does up, SwiGLU and down; both timing marks follow it
-        e = launch_fused_bf16(g, x, W1, W3, W2, Ws1, Ws3, Ws2, Y, D, F, stream);
+        // one launch does up, SwiGLU and down (mark 2); with split chunks the
+        // reduction of the partial outputs follows (mark 3)
+        const int64_t R = S + (has_shared ? T : 0);
+        const int splits = fused_splits(R, F);
+        e = launch_fused_bf16(g, x, W1, W3, W2, Ws1, Ws3, Ws2, Y, (float*)h, splits, R, D, F, stream);
         if (e == hipSuccess) e = mark(2);
+        if (e == hipSuccess && splits > 1) e = launch_fused_reduce((const float*)h, splits, R, D, Y, stream);
     } else if (sort_in_up) {
         e = launch_up_swiglu_bf16_slab_routed(g, L.tile_rows / 32, topk_idx, counts, offsets, tile_off,
                                               tile_off64, perm, inv, err, x, W1, W3, Ws1, Ws3, h, D,

@@ -88,9 +88,23 @@ hipError_t launch_down_bf16_small(const GroupArgs& g, const void* h, const void*
 // chip; writes the same Y as the down GEMM.  Needs D % 128 == 0,
 // D <= 1024, F % 128 == 0.
 constexpr int kFusedTileRows = 64;
+// Workgroups the fused grid aims for when it splits each tile's F chunks.
+// Half the compute units: on the 16-expert D 1024 F 4096 layer, grids of
+// 128 workgroups ran faster than grids of 256 (one per CU) at 16, 32 and 128
+// tiles, and within 5% of the best split count at 64 (measured).
+constexpr int kFusedSplitTarget = 128;
+// Number of workgroups that share one token tile's F chunks: 1 when the
+// tile grid alone (at least ceil(R / 64) tiles for R rows) fills
+// kFusedSplitTarget workgroups, else the largest power of two that keeps
+// tiles x splits within it, at most the number of 256-column chunks.
+int fused_splits(int64_t R, int F);
+// splits == 1: Y directly.  splits > 1: each workgroup writes its fp32
+// partial output to plane `split` of P [splits][R][D] and
+// launch_fused_reduce sums the planes in plane order into Y.
 hipError_t launch_fused_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
                              const void* W2, const void* Ws1, const void* Ws3, const void* Ws2,
-                             void* Y, int D, int F, hipStream_t s);
+                             void* Y, float* P, int splits, int64_t R, int D, int F, hipStream_t s);
+hipError_t launch_fused_reduce(const float* P, int splits, int64_t R, int D, void* Y, hipStream_t s);
 
 // fp32 grouped GEMMs (plain fp32 FMA; correctness-first path).
 constexpr int kF32TileRows = 64;

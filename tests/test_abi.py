@@ -106,6 +106,26 @@ def test_fused_layout_has_no_h_and_64_row_tiles():
     assert L.lib().moe_ffn_tile_rows(L.MOE_BF16, L.MOE_VARIANT_FUSED) == 64
 
 
+def test_fused_layout_holds_split_partials_when_tiles_are_few():
+    """16 tiles of 64 rows (512 tokens, top-2): each tile's 16 chunks of 256
+    columns go to 8 workgroups (128 in all), whose fp32 partial outputs
+    [8][R][D] take the h slot."""
+    import torch
+    T, D, F, E, k = 512, 1024, 4096, 16, 2
+    lay = L.workspace_layout(T, D, F, E, k, False, torch.bfloat16, "fused")
+    R = T * k
+    assert lay["Y"] - lay["h"] == 8 * R * D * 4
+    # with a shared expert R = 1536 rows: 24 tiles -> 4 splits
+    lay = L.workspace_layout(T, D, F, E, k, True, torch.bfloat16, "fused")
+    assert lay["Y"] - lay["h"] == 4 * (R + T) * D * 4
+    # F = 384: two chunks at most -> 2 splits
+    lay = L.workspace_layout(T, D, 384, E, k, False, torch.bfloat16, "fused")
+    assert lay["Y"] - lay["h"] == 2 * R * D * 4
+    # 4096 tokens: 128 tiles -> no split, no partials
+    lay = L.workspace_layout(4096, D, F, E, k, False, torch.bfloat16, "fused")
+    assert lay["Y"] == lay["h"]
+
+
 def test_permute_rejects_bad_arguments_on_host():
     lib = L.lib()
     args = [FAKE, 10, 2, 4, 256, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None]

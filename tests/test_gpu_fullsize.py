@@ -4,9 +4,10 @@ The five workload shapes (the 4096-token GPT-OSS-Lite layer, the
 32768-token Zipf step, the 512-token small-chunk case and the F > D case)
 run in the launch configuration the benchmark times (a caller-owned
 workspace, one call on the current stream), and every token of y is
-compared with the fp64 oracle's dense path, with the benchmark spec's tolerance of
+compared with the fp64 oracle's dense path, with the tolerance of
 ``gpu_util.check_close``.  The fused variant is checked the same way on the
-step and F > D workloads.
+step, small-chunk (its tiles' F chunks split over workgroups) and F > D
+workloads.
 
 The permute the forward runs inside its own workspace (counts, offsets,
 tile_off for the call's tile height, tile_off64 for 64-row tiles, perm, inv
@@ -28,7 +29,7 @@ pytestmark = pytest.mark.gpu
 # (workload, variant), ordered so that each workload's oracle result is
 # computed once and reused by both variants
 CASES = [(0, "unfused"), (1, "unfused"), (2, "unfused"), (2, "fused"), (3, "unfused"),
-         (4, "unfused"), (4, "fused")]
+         (3, "fused"), (4, "unfused"), (4, "fused")]
 
 
 def case_id(v):
