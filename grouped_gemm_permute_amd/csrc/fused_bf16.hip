@@ -42,19 +42,22 @@
 //    so the workgroups of one XCD work on the same expert at the same time
 //    and share each weight chunk through that XCD's L2, each starting the
 //    chunk's steps at a different point;
-//  * when the tiles are few (fused_splits), the chunks of each tile are
-//    shared out over `splits` workgroups: workgroup (tile, sp) runs chunks
-//    sp NCH / splits .. (sp + 1) NCH / splits - 1 and stores its fp32
-//    accumulator as plane sp of P; fused_reduce_kernel then adds the planes
-//    in plane order and rounds once to bf16 Y.  On the 16-expert layer with
-//    64 tokens per expert this takes the kernel from 16 workgroups and
-//    0.88 ms to 128 workgroups and 0.16 ms (measured).
+//  * the tiles of the last, partial round of 256 workgroups (all tiles when
+//    there are fewer than 256) are shared out over s workgroups each
+//    (fused_plan): workgroup (tile, sp) runs chunks sp NCH / s ..
+//    (sp + 1) NCH / s - 1 and stores its fp32 accumulator as a partial
+//    output; fused_reduce_kernel adds a tile's partials in split order and
+//    rounds once to bf16 Y.  Ragged group ends make the tile count a little
+//    over a multiple of 256 (16384 tokens on 16 experts: 528 tiles), and
+//    the few tiles past it would otherwise cost a whole extra round.
 //
 // Measured on the 16384-token F > D workload (D 1024, F 4096, 16 experts):
 // the kernel stages ~27 MB per 64-row tile (each tile re-streams its
 // expert's weights), ~50 MB per CU per launch, and sustains ~40 GB/s of
 // weight staging per CU; with no loads at all its loop alone takes half the
 // launch.  The unfused pair stages 4x fewer bytes per FLOP and is faster.
+#include <algorithm>
+
 #include "mfma_common.h"
 
 namespace moe {
@@ -110,12 +113,31 @@ struct FusedArgs {
     const uint16_t* x;                     // [T, D]
     const uint16_t *W1, *W3, *W2;          // [E, D, F], [E, D, F], [E, F, D]
     const uint16_t *Ws1, *Ws3, *Ws2;       // shared expert or null
-    uint16_t* Y;                           // [R, D] bf16 expert outputs (splits == 1)
-    float* P;                              // [splits][R][D] fp32 partial outputs (splits > 1)
-    int64_t R;
-    int splits;
+    uint16_t* Y;                           // [R, D] bf16 expert outputs (whole tiles)
+    float* P;                              // [r s][64][D] fp32 partial outputs (split tiles)
     int D, F;
 };
+
+// Workgroup bid -> (tile mt, split sp) under plan p.  XCD x = bid % 8 runs,
+// in its first whole / 8 slots, whole tiles x whole / 8 .. (x + 1) whole / 8 - 1
+// (whole rounds, contiguous tiles sharing their weights in the XCD's L2),
+// then the split units x rs / 8 .. (x + 1) rs / 8 - 1 of the last round
+// (unit u: tile whole + u / s, split u % s).  False: nothing to do.
+__device__ __forceinline__ bool fused_unit(int bid, const FusedPlan& p, int& mt, int& sp) {
+    const int x = bid & 7, i = bid >> 3;
+    const int nw = p.whole >> 3;
+    if (i < nw) {
+        mt = x * nw + i;
+        sp = 0;
+        return true;
+    }
+    const int units = p.r * p.s;
+    const int u = x * units / 8 + (i - nw);
+    if (u >= (x + 1) * units / 8) return false;
+    mt = p.whole + u / p.s;
+    sp = u - (u / p.s) * p.s;
+    return true;
+}
 
 // D = 128 * NFB.
 template <int NFB>
@@ -143,11 +165,12 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
     const int NCH = (F + CH - 1) / CH;         // chunks; the last holds 128 columns when F % 256 != 0
     const bool half = F % CH != 0;
 
-    // work item = (tile mt, split sp): chunks c0 .. c1-1 of tile mt
-    const int work = xcd_remap_work(blockIdx.x, a.g.tile_off[a.g.G] * a.splits);
-    if (work < 0) return;
-    const int mt = work / a.splits, sp = work - mt * a.splits;
-    const int c0 = sp * NCH / a.splits, c1 = (sp + 1) * NCH / a.splits;
+    // work item = (tile mt, split sp of ns): chunks c0 .. c1-1 of tile mt
+    const FusedPlan plan = fused_plan(a.g.tile_off[a.g.G], NCH);
+    int mt, sp;
+    if (!fused_unit(blockIdx.x, plan, mt, sp)) return;
+    const int ns = mt >= plan.whole ? plan.s : 1;
+    const int c0 = sp * NCH / ns, c1 = (sp + 1) * NCH / ns;
     const int NSTEP = (c1 - c0) * SPC - (half && c1 == NCH ? DN_STEPS / 2 : 0);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -384,12 +407,13 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
 
     // ---- epilogue: acc_y[i][j] element v of lane l: token 32 (rb0 + j) + l%32,
     // output column 32 (cb0 + i) + 8 (v/4) + 4 (l/32) + v%4.
-    if (a.splits > 1) {
+    if (ns > 1) {
+        const int unit = (mt - plan.whole) * ns + sp;
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
             const int t = 32 * (rb0 + j) + xr;
             if (t >= valid_rows) continue;
-            float* out = a.P + ((int64_t)sp * a.R + tile_r0 + t) * D;
+            float* out = a.P + ((int64_t)unit * TT + t) * D;
 #pragma unroll
             for (int i = 0; i < CBW; ++i)
 #pragma unroll
@@ -420,57 +444,66 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
     }
 }
 
-// Y[r] = bf16(P[0][r] + P[1][r] + ... + P[splits-1][r]), fp32 sums in
-// plane order (reproducible); one thread per 8 columns of a row, D % 8 == 0.
-// Rows no tile covers (slots with invalid expert ids) hold unused values.
-__global__ __launch_bounds__(256) void fused_reduce_kernel(const float* __restrict__ P, int splits,
-                                                          int64_t R, int D, uint16_t* __restrict__ Y) {
+// Split tile whole + j (j < r) of the plan: Y[row] = bf16(sum over sp of
+// its partial outputs), fp32 adds in split order (reproducible).  Workgroup
+// b takes rows RED_ROWS (b % (TT / RED_ROWS)) .. + RED_ROWS - 1 of split
+// tile b / (TT / RED_ROWS); one thread per 8 columns of a row.
+constexpr int RED_ROWS = 8;
+__global__ __launch_bounds__(256) void fused_reduce_kernel(const GroupArgs g, const float* __restrict__ P,
+                                                          uint16_t* __restrict__ Y, int D, int chunks) {
+    const FusedPlan plan = fused_plan(g.tile_off[g.G], chunks);
+    const int j = blockIdx.x / (TT / RED_ROWS), rb = blockIdx.x % (TT / RED_ROWS);
+    if (plan.s == 1 || j >= plan.r) return;
+    const TileGroup tg = find_tile_group(g, plan.whole + j, TT, threadIdx.x & 63);
     const int cg = D / 8;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= R * cg) return;
-    const int64_t r = gid / cg;
-    const int c = (int)(gid - r * cg) * 8;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < splits; ++p) {
-        typedef __attribute__((ext_vector_type(4))) float f4;
-        const f4* src = (const f4*)(P + ((int64_t)p * R + r) * D + c);
-        const f4 lo = __builtin_nontemporal_load(src), hi = __builtin_nontemporal_load(src + 1);
+    const int rows = min(RED_ROWS, tg.valid_rows - RED_ROWS * rb);
+    for (int it = threadIdx.x; it < rows * cg; it += 256) {
+        const int t = RED_ROWS * rb + it / cg, c = (it % cg) * 8;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < plan.s; ++sp) {
+            typedef __attribute__((ext_vector_type(4))) float f4;
+            const f4* src = (const f4*)(P + ((int64_t)(j * plan.s + sp) * TT + t) * D + c);
+            const f4 lo = __builtin_nontemporal_load(src), hi = __builtin_nontemporal_load(src + 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[i] += lo[i];
-            acc[4 + i] += hi[i];
+            for (int i = 0; i < 4; ++i) {
+                acc[i] += lo[i];
+                acc[4 + i] += hi[i];
+            }
         }
+        *(uint4*)(Y + (tg.tile_r0 + t) * D + c) =
+            make_uint4(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
+                       pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7]));
     }
-    *(uint4*)(Y + r * D + c) = make_uint4(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
-                                          pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7]));
 }
+
+// Upper bound of the tile count of a call with R rows in G groups.
+int64_t fused_tiles_upper(int64_t R, int G) { return (R + TT - 1) / TT + G; }
 
 }  // namespace
 
-int fused_splits(int64_t R, int F) {
-    const int chunks = (F + CH - 1) / CH;
-    const int64_t tiles = (R + TT - 1) / TT;
-    int s = 1;
-    while (2 * s <= chunks && tiles * 2 * s <= kFusedSplitTarget) s *= 2;
-    return s;
+size_t fused_partial_bytes(int64_t R, int G, int D, int F) {
+    const int64_t chunks = (F + CH - 1) / CH;
+    const int64_t units = std::min<int64_t>(kFusedUnits, fused_tiles_upper(R, G) * chunks);
+    return sizeof(float) * (size_t)units * TT * (size_t)D;
 }
 
-hipError_t launch_fused_reduce(const float* P, int splits, int64_t R, int D, void* Y, hipStream_t s) {
-    const int64_t threads = R * (D / 8);
-    if (threads == 0) return hipSuccess;
-    fused_reduce_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(P, splits, R, D, (uint16_t*)Y);
+hipError_t launch_fused_reduce(const GroupArgs& g, const float* P, void* Y, int D, int F, hipStream_t s) {
+    const int64_t rows = g.S + (g.G > g.E ? g.T : 0);
+    const int blocks = (int)std::min<int64_t>(kFusedUnits, fused_tiles_upper(rows, g.G)) * (TT / RED_ROWS);
+    fused_reduce_kernel<<<blocks, 256, 0, s>>>(g, P, (uint16_t*)Y, D, (F + CH - 1) / CH);
     return hipGetLastError();
 }
 
 hipError_t launch_fused_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
                              const void* W2, const void* Ws1, const void* Ws3, const void* Ws2,
-                             void* Y, float* P, int splits, int64_t R, int D, int F, hipStream_t s) {
-    if (splits < 1 || splits > (F + CH - 1) / CH || (splits > 1 && !P)) return hipErrorInvalidValue;
+                             void* Y, float* P, int D, int F, hipStream_t s) {
     FusedArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
                 (const uint16_t*)W2, (const uint16_t*)Ws1, (const uint16_t*)Ws3,
-                (const uint16_t*)Ws2, (uint16_t*)Y, P, R, splits, D, F};
+                (const uint16_t*)Ws2, (uint16_t*)Y, P, D, F};
     const int64_t rows = g.S + (g.G > g.E ? g.T : 0);
-    const unsigned blocks = (unsigned)(((rows + TT - 1) / TT + g.G) * splits);
+    // whole tiles (at most the upper bound, whole / 8 slots per XCD) plus at
+    // most kFusedUnits / 8 split units per XCD
+    const unsigned blocks = grid_for_work(fused_tiles_upper(rows, g.G)) + kFusedUnits + 8;
     switch (D / 128) {
         case 1: fused_up_act_down_kernel<1><<<grid_for_work(blocks), NT, 0, s>>>(a); break;
         case 2: fused_up_act_down_kernel<2><<<grid_for_work(blocks), NT, 0, s>>>(a); break;

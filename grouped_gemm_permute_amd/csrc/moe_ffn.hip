@@ -57,16 +57,14 @@ moe_status make_layout(int64_t T, int D, int F, int E, int k, int has_shared, mo
     // multi-block permute histogram; kRouterSub columns per block when the
     // router writes it
     L->hist = take(sizeof(int32_t) * (size_t)(E + 1) * (size_t)nb * kRouterSub);
-    // The fused variant keeps h on chip; when it splits the tiles' F chunks
-    // over several workgroups this slot holds their fp32 partial outputs.
-    const int splits = fused ? fused_splits(R, F) : 1;
-    L->h = take(fused ? (splits > 1 ? sizeof(float) * (size_t)splits * (size_t)R * (size_t)D : 0)
-                      : esize * (size_t)R * (size_t)F);
+    // The fused variant keeps h on chip; this slot then holds the fp32
+    // partial outputs of the tiles it shares out over several workgroups.
+    const int G = E + (has_shared ? 1 : 0);
+    L->h = take(fused ? fused_partial_bytes(R, G, D, F) : esize * (size_t)R * (size_t)F);
     L->Y = take(esize * (size_t)R * (size_t)D);
     L->total = off;
     // bf16 unfused: groups averaging under one 256-row tile are bound by
     // streaming their weights; they run on the small-tile kernels.
-    const int G = E + (has_shared ? 1 : 0);
     // Their up GEMM tiles hold a whole typical group (tile_off); the down
     // GEMM runs on 64-row tiles (tile_off64).
     L->small_tiles = (!fused && dt == MOE_BF16 && R < (int64_t)kBf16TileRows * G) ? 1 : 0;
@@ -211,13 +209,11 @@ moe_status forward_impl(const void* x, const void* gate_w, const int32_t* topk_i
     GroupArgs g{offsets, tile_off, perm, S, T, E, k, E + (has_shared ? 1 : 0)};
     hipError_t e;
     if (variant == MOE_VARIANT_FUSED) {
-        // one launch does up, SwiGLU and down (mark 2); with split chunks the
-        // reduction of the partial outputs follows (mark 3)
-        const int64_t R = S + (has_shared ? T : 0);
-        const int splits = fused_splits(R, F);
-        e = launch_fused_bf16(g, x, W1, W3, W2, Ws1, Ws3, Ws2, Y, (float*)h, splits, R, D, F, stream);
+        // one launch does up, SwiGLU and down (mark 2); the sum of the split
+        // tiles' partial outputs follows (mark 3)
+        e = launch_fused_bf16(g, x, W1, W3, W2, Ws1, Ws3, Ws2, Y, (float*)h, D, F, stream);
         if (e == hipSuccess) e = mark(2);
-        if (e == hipSuccess && splits > 1) e = launch_fused_reduce((const float*)h, splits, R, D, Y, stream);
+        if (e == hipSuccess) e = launch_fused_reduce(g, (const float*)h, Y, D, F, stream);
     } else if (sort_in_up) {
         e = launch_up_swiglu_bf16_slab_routed(g, L.tile_rows / 32, topk_idx, counts, offsets, tile_off,
                                               tile_off64, perm, inv, err, x, W1, W3, Ws1, Ws3, h, D,

@@ -88,23 +88,39 @@ hipError_t launch_down_bf16_small(const GroupArgs& g, const void* h, const void*
 // chip; writes the same Y as the down GEMM.  Needs D % 128 == 0,
 // D <= 1024, F % 128 == 0.
 constexpr int kFusedTileRows = 64;
-// Workgroups the fused grid aims for when it splits each tile's F chunks.
-// Half the compute units: on the 16-expert D 1024 F 4096 layer, grids of
-// 128 workgroups ran faster than grids of 256 (one per CU) at 16, 32 and 128
-// tiles, and within 5% of the best split count at 64 (measured).
-constexpr int kFusedSplitTarget = 128;
-// Number of workgroups that share one token tile's F chunks: 1 when the
-// tile grid alone (at least ceil(R / 64) tiles for R rows) fills
-// kFusedSplitTarget workgroups, else the largest power of two that keeps
-// tiles x splits within it, at most the number of 256-column chunks.
-int fused_splits(int64_t R, int F);
-// splits == 1: Y directly.  splits > 1: each workgroup writes its fp32
-// partial output to plane `split` of P [splits][R][D] and
-// launch_fused_reduce sums the planes in plane order into Y.
+// Work plan of one fused launch, from the actual number of 64-row tiles W
+// (tile_off[G], known on the device only).  Tiles run whole in full rounds
+// of kFusedUnits workgroups (one per compute unit); each of the
+// r = W mod kFusedUnits tiles of the last, partial round is shared out over
+// s workgroups, s the largest power of two with r s <= kFusedUnits and
+// s <= the number of 256-column F chunks, so the last round fills the GPU
+// as far as the chunk count allows.  Split tiles write fp32 partial outputs
+// that launch_fused_reduce sums in split order.
+constexpr int kFusedUnits = 256;
+struct FusedPlan {
+    int whole;   // tiles 0 .. whole-1 run whole (a multiple of kFusedUnits)
+    int r;       // tiles whole .. W-1 form the last round
+    int s;       // workgroups per tile of the last round
+};
+__host__ __device__ inline FusedPlan fused_plan(int W, int chunks) {
+    FusedPlan p;
+    p.r = W % kFusedUnits;
+    p.whole = W - p.r;
+    p.s = 1;
+    if (p.r > 0)
+        while (2 * p.s <= chunks && p.r * 2 * p.s <= kFusedUnits) p.s *= 2;
+    return p;
+}
+// Bytes of the fp32 partial outputs of a call with R rows and G groups: at
+// most kFusedUnits split workgroups, 64 x D floats each.
+size_t fused_partial_bytes(int64_t R, int G, int D, int F);
+// Y [R, D] bf16 for whole tiles; split tiles write P and need
+// launch_fused_reduce afterwards (on the same stream; it returns at once
+// when the call splits nothing).
 hipError_t launch_fused_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
                              const void* W2, const void* Ws1, const void* Ws3, const void* Ws2,
-                             void* Y, float* P, int splits, int64_t R, int D, int F, hipStream_t s);
-hipError_t launch_fused_reduce(const float* P, int splits, int64_t R, int D, void* Y, hipStream_t s);
+                             void* Y, float* P, int D, int F, hipStream_t s);
+hipError_t launch_fused_reduce(const GroupArgs& g, const float* P, void* Y, int D, int F, hipStream_t s);
 
 // fp32 grouped GEMMs (plain fp32 FMA; correctness-first path).
 constexpr int kF32TileRows = 64;

@@ -77,10 +77,9 @@ typedef struct moe_ws_layout {
     size_t perm;        /* int32 [T*k] sorted position -> slot t*k+j (-1 past the valid rows) */
     size_t inv;         /* int32 [T*k] slot -> sorted position (-1 for an invalid slot) */
     size_t hist;        /* int32 scratch of the multi-block permute */
-    size_t h;           /* unfused: [R, F] silu(g)*u, dtype of the call.  fused: empty, or, when
-                           the 64-row tiles number at most 64 (R <= 4096 rows),
-                           [splits][R][D] fp32 partial outputs of the workgroups that
-                           share a tile's F chunks */
+    size_t h;           /* unfused: [R, F] silu(g)*u, dtype of the call.  fused: fp32
+                           partial outputs [units][64][D] of the workgroups that share
+                           out the tiles of the last, partial round of 256 (units <= 256) */
     size_t Y;           /* [R, D] per-row expert outputs (unweighted), dtype of the call */
     int32_t tile_rows;  /* row-tile height of the grouped GEMMs (tile_off's divisor) */
     int32_t hist_blocks;/* number of slot blocks of the multi-block permute (0: single block) */
@@ -142,11 +141,12 @@ size_t moe_ffn_workspace_size(int64_t T, int D, int F, int E, int k, int has_sha
  * Variants: MOE_VARIANT_UNFUSED writes h [R, F] to the workspace between
  * the up and down grouped GEMMs; MOE_VARIANT_FUSED ("Chinchilla scaling,
  * MoE, and fused Triton kernels", fused kernel sections) computes up,
- * SwiGLU and down per 64-token tile in one kernel and never stores h; when
- * the tiles are too few to occupy the GPU, each tile's F chunks are shared
- * out over several workgroups (a power of two, at most one per 256-column
- * chunk) whose fp32 partial outputs a second kernel sums in a fixed order
- * before rounding Y to bf16.  Both
+ * SwiGLU and down per 64-token tile in one kernel and never stores h.
+ * Tiles run whole in full rounds of 256 workgroups; each tile of the last,
+ * partial round (all tiles when there are fewer than 256) has its F chunks
+ * shared out over several workgroups (a power of two, at most one per
+ * 256-column chunk, at most 256 in all) whose fp32 partial outputs a second
+ * kernel sums in a fixed order before rounding Y to bf16.  Both
  * give results within the same tolerance of the exact layer; they are not
  * bitwise equal to each other (different accumulation blocking).
  * T == 0 returns MOE_OK and launches nothing.
@@ -164,8 +164,8 @@ moe_status moe_ffn_forward(const void *x, const int32_t *topk_idx, const float *
  * small-chunk up GEMM does the counting sort itself: bf16, unfused, groups
  * averaging under 256 rows, T*k <= 4096, E <= 512), events[2] after the
  * up+SwiGLU GEMM (the fused variant: after its single up-act-down kernel),
- * events[3] after the down GEMM (fused: after the sum of the split partial
- * outputs, immediately after events[2] when the tiles are not split) and
+ * events[3] after the down GEMM (fused: after the sum of the split tiles'
+ * partial outputs) and
  * events[4] after the combine, all on `stream` (five caller-created
  * hipEvent_t).  For measuring
  * each kernel's duration inside a timed loop; results are identical to

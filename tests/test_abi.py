@@ -99,31 +99,22 @@ def test_forward_rejects_bad_arguments_on_host(over, status):
     assert _fwd(**over) == status
 
 
-def test_fused_layout_has_no_h_and_64_row_tiles():
+def test_fused_layout_64_row_tiles_and_partial_outputs():
+    """The fused variant keeps h on chip; its h slot holds the fp32 partial
+    outputs of the tiles it shares out over several workgroups: at most 256
+    workgroups of 64 x D floats, fewer when the tiles times the 256-column
+    chunks are fewer."""
     import torch
-    lay = L.workspace_layout(16384, 1024, 4096, 16, 2, False, torch.bfloat16, "fused")
-    assert lay["tile_rows"] == 64 and lay["Y"] == lay["h"]
+    D, F, E, k = 1024, 4096, 16, 2
+    lay = L.workspace_layout(16384, D, F, E, k, False, torch.bfloat16, "fused")
+    assert lay["tile_rows"] == 64 and lay["Y"] - lay["h"] == 256 * 64 * D * 4
     assert L.lib().moe_ffn_tile_rows(L.MOE_BF16, L.MOE_VARIANT_FUSED) == 64
-
-
-def test_fused_layout_holds_split_partials_when_tiles_are_few():
-    """16 tiles of 64 rows (512 tokens, top-2): each tile's 16 chunks of 256
-    columns go to 8 workgroups (128 in all), whose fp32 partial outputs
-    [8][R][D] take the h slot."""
-    import torch
-    T, D, F, E, k = 512, 1024, 4096, 16, 2
-    lay = L.workspace_layout(T, D, F, E, k, False, torch.bfloat16, "fused")
-    R = T * k
-    assert lay["Y"] - lay["h"] == 8 * R * D * 4
-    # with a shared expert R = 1536 rows: 24 tiles -> 4 splits
-    lay = L.workspace_layout(T, D, F, E, k, True, torch.bfloat16, "fused")
-    assert lay["Y"] - lay["h"] == 4 * (R + T) * D * 4
-    # F = 384: two chunks at most -> 2 splits
-    lay = L.workspace_layout(T, D, 384, E, k, False, torch.bfloat16, "fused")
-    assert lay["Y"] - lay["h"] == 2 * R * D * 4
-    # 4096 tokens: 128 tiles -> no split, no partials
-    lay = L.workspace_layout(4096, D, F, E, k, False, torch.bfloat16, "fused")
-    assert lay["Y"] == lay["h"]
+    # 32 rows in 2 groups: at most 3 tiles x 1 chunk of 256 columns
+    lay = L.workspace_layout(32, 256, 256, 2, 1, False, torch.bfloat16, "fused")
+    assert lay["Y"] - lay["h"] == 3 * 64 * 256 * 4
+    # 1024 rows in 16 groups, F = 384: at most 32 tiles x 2 chunks
+    lay = L.workspace_layout(512, D, 384, E, k, False, torch.bfloat16, "fused")
+    assert lay["Y"] - lay["h"] == 64 * 64 * D * 4
 
 
 def test_permute_rejects_bad_arguments_on_host():

@@ -82,9 +82,11 @@ FUSED_CASES = [
     (300, 1024, 256, 4, 2, True, "uniform"),   # widest accumulator (D = 1024)
     (513, 768, 640, 6, 2, False, "uniform"),
     (1, 384, 128, 2, 1, False, "uniform"),
-    # few tiles: F chunks split over workgroups, fp32 partials summed after
-    (200, 512, 4096, 4, 2, True, "uniform"),   # 10 tiles (+ ragged) -> 8 splits of two chunks
-    (64, 256, 2176, 3, 2, False, "zipf"),      # 2 tiles -> 8 splits of 9 chunks, the last a half chunk
+    # tiles of the last round of 256 shared out over workgroups (F chunks
+    # split, fp32 partial outputs summed after)
+    (200, 512, 4096, 4, 2, True, "uniform"),   # ~11 tiles -> 16 splits of one chunk
+    (64, 256, 2176, 3, 2, False, "zipf"),      # 2-3 tiles -> 16 splits of 9 chunks, the last a half chunk
+    (9000, 128, 640, 8, 2, False, "zipf"),     # 256 whole tiles, then ~30 tiles in 2-3 splits
 ]
 
 
