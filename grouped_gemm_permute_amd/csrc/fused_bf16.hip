@@ -293,8 +293,9 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
         for (int j = 0; j < RBW; ++j) acc_y[i][j] = f32x16_t{};
     f32x16_t acc_up[2][2];
 
-    // One up K step (16) on stage st: 2 weight frags x 2 token frags = 4 MFMAs.
-    auto compute_up = [&](const char* st) {
+    // One up K step (16) on stage st: 2 weight frags x 2 token frags = 4 MFMAs;
+    // stage s + 3 is issued into dma between the operand reads and the MFMAs.
+    auto compute_up = [&](const char* st, int s, char* dma) {
         bf16x8_t wf[2], xf[2];
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
@@ -302,14 +303,19 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
 #pragma unroll
         for (int nj = 0; nj < 2; ++nj)
             xf[nj] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + x_off + 32 * nj * X_ROW));
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s + 3, dma);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
             for (int nj = 0; nj < 2; ++nj)
                 acc_up[fb][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[fb], xf[nj], acc_up[fb][nj], 0, 0, 0);
     };
-    // One down K step (16 rows of W2) on stage st, h slice q of the chunk.
-    auto compute_down = [&](const char* st, int q) {
+    // One down K step (16 rows of W2) on stage st, h slice q of the chunk;
+    // stage s + 3 is issued once the h slice and the first weight fragment
+    // are requested.
+    auto compute_down = [&](const char* st, int q, int s, char* dma) {
         bf16x8_t hf[RBW];
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
@@ -317,9 +323,13 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
             const int c = (2 * q + (lane >> 5)) ^ swz16(row);
             hf[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(hbuf + row * H_ROW + (c << 4)));
         }
+        const bf16x8_t wf0 = cat_bf16(read_tr(st + dn_off[0]), read_tr(st + dn_off[0] + 4 * DN_ROW));
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s + 3, dma);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < CBW; ++i) {
-            const bf16x8_t wf = cat_bf16(read_tr(st + dn_off[i]), read_tr(st + dn_off[i] + 4 * DN_ROW));
+            const bf16x8_t wf = i == 0 ? wf0 : cat_bf16(read_tr(st + dn_off[i]), read_tr(st + dn_off[i] + 4 * DN_ROW));
 #pragma unroll
             for (int j = 0; j < RBW; ++j)
                 acc_y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, hf[j], acc_y[i][j], 0, 0, 0);
@@ -350,19 +360,22 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
 
     // ---- step s (buffer s % 4): wait until stage s has landed (stages s+1
     // and s+2 of this wavefront may still be in flight) and every LDS access
-    // of the previous step is done; barrier; issue stage s + 3 into the
-    // buffer of stage s - 1 (free: its last readers finished before this
-    // barrier); compute stage s.  Each chunk runs its KU up steps, writes h,
+    // of the previous step is done; barrier; read stage s's operands, then
+    // issue stage s + 3 into the buffer of stage s - 1 (free: its last
+    // readers finished before this barrier), then the MFMAs.  Issuing the
+    // loads after the operand reads rather than before them lets the reads
+    // go out while the memory pipe is still busy with earlier stages (a
+    // wavefront stalls at a load while that pipe is backed up): 8-10% off the
+    // kernel, measured.  Each chunk runs its KU up steps, writes h,
     // then its down steps (16, or 8 for a last chunk of 128 columns); every
     // count is a multiple of 4, so every phase starts in buffer 0 and the
     // buffers are named statically.  The barrier of the first down step
     // orders the h writes before the down steps' reads, and the barriers of
     // the next chunk's up phase order those reads before the next write.
-    auto begin_step = [&](int s, char* dma) {
+    auto begin_step = [&](int s) {
         wait_vm(loads_of(s + 1) + loads_of(s + 2));
         __builtin_amdgcn_s_barrier();
         fence();
-        issue(s + 3, dma);
     };
     issue(0, st0);
     issue(1, st1);
@@ -372,34 +385,34 @@ __global__ __launch_bounds__(NT, 1) void fused_up_act_down_kernel(const FusedArg
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) acc_up[fb][0] = acc_up[fb][1] = f32x16_t{};
         for (int u = 0; u < KU; u += 4) {
-            begin_step(s0 + u, st3);
-            compute_up(st0);
+            begin_step(s0 + u);
+            compute_up(st0, s0 + u, st3);
             fence();
-            begin_step(s0 + u + 1, st0);
-            compute_up(st1);
+            begin_step(s0 + u + 1);
+            compute_up(st1, s0 + u + 1, st0);
             fence();
-            begin_step(s0 + u + 2, st1);
-            compute_up(st2);
+            begin_step(s0 + u + 2);
+            compute_up(st2, s0 + u + 2, st1);
             fence();
-            begin_step(s0 + u + 3, st2);
-            compute_up(st3);
+            begin_step(s0 + u + 3);
+            compute_up(st3, s0 + u + 3, st2);
             fence();
         }
         write_h();
         const int ds = half && c == NCH - 1 ? DN_STEPS / 2 : DN_STEPS;
         const int qr = rot * (ds / 8);
         for (int q = 0; q < ds; q += 4) {
-            begin_step(s0 + KU + q, st3);
-            compute_down(st0, (q + qr) % ds);
+            begin_step(s0 + KU + q);
+            compute_down(st0, (q + qr) % ds, s0 + KU + q, st3);
             fence();
-            begin_step(s0 + KU + q + 1, st0);
-            compute_down(st1, (q + 1 + qr) % ds);
+            begin_step(s0 + KU + q + 1);
+            compute_down(st1, (q + 1 + qr) % ds, s0 + KU + q + 1, st0);
             fence();
-            begin_step(s0 + KU + q + 2, st1);
-            compute_down(st2, (q + 2 + qr) % ds);
+            begin_step(s0 + KU + q + 2);
+            compute_down(st2, (q + 2 + qr) % ds, s0 + KU + q + 2, st1);
             fence();
-            begin_step(s0 + KU + q + 3, st2);
-            compute_down(st3, (q + 3 + qr) % ds);
+            begin_step(s0 + KU + q + 3);
+            compute_down(st3, (q + 3 + qr) % ds, s0 + KU + q + 3, st2);
             fence();
         }
     }
