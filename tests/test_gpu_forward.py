@@ -144,19 +144,33 @@ def test_forward_intermediates_sampled_rows():
         check_close(Ys[i], hh @ w2.astype(np.float64), "bf16", f"Y row {p}")
 
 
-def test_forward_is_bitwise_deterministic():
+DETERMINISM_CASES = [
+    # T, D, F, E, k, shared, routing, variant
+    (3000, 256, 384, 8, 2, True, "zipf", "unfused"),      # 256-row engine
+    (300, 256, 512, 8, 2, False, "uniform", "unfused"),   # small chunks, sort inside the up GEMM
+    (300, 256, 1024, 8, 2, True, "uniform", "fused"),     # every tile split over F chunks
+    (9000, 128, 640, 8, 2, False, "zipf", "fused"),       # whole rounds, then split tiles
+]
+
+
+@pytest.mark.parametrize("case", DETERMINISM_CASES, ids=lambda c: "T{}_D{}_F{}_E{}_k{}_{}_{}_{}".format(*c))
+def test_forward_is_bitwise_deterministic(case):
+    """Three calls with differently filled workspaces on fresh streams give
+    the same bits: no atomics decide an order, and partial sums (split
+    tiles, the combine) are added in a fixed order."""
     import grouped_gemm_permute_amd as gg
-    inp = make_case(3000, 256, 384, 8, 2, True, "bf16", "zipf", seed=5)
+    T, D, F, E, k, sh, routing, variant = case
+    inp = make_case(T, D, F, E, k, sh, "bf16", routing, seed=5)
     d = device_inputs(inp)
-    lay = gg.workspace_layout(3000, 256, 384, 8, 2, True, torch.bfloat16)
-    say("determinism T3000 D256 F384 E8 k2 shared")
+    lay = gg.workspace_layout(T, D, F, E, k, sh, torch.bfloat16, variant)
+    say(f"determinism {case}")
     outs = []
     for fill in (0, 255, 77):
         ws = torch.full((lay["total"],), fill, dtype=torch.uint8, device="cuda")
         s = torch.cuda.Stream()
         with torch.cuda.stream(s):
             y = gg.forward(d["x"], d["topk_idx"], d["topk_w"], d["W1"], d["W3"], d["W2"], d["shared"],
-                           workspace=ws)
+                           variant=variant, workspace=ws)
         s.synchronize()
         outs.append(y.view(torch.int16).cpu())
     for o in outs[1:]:
