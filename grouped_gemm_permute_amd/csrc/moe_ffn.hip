@@ -216,7 +216,7 @@ moe_status forward_impl(const void* x, const void* gate_w, const int32_t* topk_i
         if (e == hipSuccess) e = launch_fused_reduce(g, (const float*)h, Y, D, F, stream);
     } else if (sort_in_up) {
         e = launch_up_swiglu_bf16_slab_routed(g, L.tile_rows / 32, topk_idx, counts, offsets, tile_off,
-                                              tile_off64, perm, inv, err, x, W1, W3, Ws1, Ws3, h, D,
+                                              tile_off64, perm, inv, err, x, W1, W3, Ws1, Ws3, W2, Ws2, h, D,
                                               F, stream);
         if (e == hipSuccess) e = mark(2);
     } else if (dtype == MOE_BF16 && L.small_tiles) {

@@ -71,12 +71,15 @@ hipError_t launch_up_swiglu_bf16_slab(const GroupArgs& g, int rb, const void* x,
 // (S = T*k <= kPermuteSingleMax, E <= kRouteMaxExperts): reads the expert id of
 // every slot and writes counts, offsets, tile_off (tile rows 32 rb),
 // tile_off64, perm, inv and err exactly as launch_permute would; g's
-// offsets, tile_off and perm are not read.
+// offsets, tile_off and perm are not read.  W2 [E, F, D] and Ws2 (or null)
+// are only read, by idle CUs, to leave them in the last-level cache for the
+// down GEMM.
 hipError_t launch_up_swiglu_bf16_slab_routed(const GroupArgs& g, int rb, const int32_t* idx,
                                              int32_t* counts, int32_t* offsets, int32_t* tile_off,
                                              int32_t* tile_off64, int32_t* perm, int32_t* inv,
                                              int32_t* err, const void* x, const void* W1,
                                              const void* W3, const void* Ws1, const void* Ws3,
+                                             const void* W2, const void* Ws2,
                                              void* h, int D, int F, hipStream_t s);
 hipError_t launch_up_swiglu_bf16_small(const GroupArgs& g, const void* x, const void* W1,
                                        const void* W3, const void* Ws1, const void* Ws3, void* h,
