@@ -9,7 +9,7 @@ namespace moe {
 
 // Slot blocks of the multi-block permute; a single workgroup handles
 // T*k <= kPermuteSingleMax.
-constexpr int kPermuteBlockSlots = 2048;
+constexpr int kPermuteBlockSlots = 1024;
 constexpr int64_t kPermuteSingleMax = 4096;
 constexpr int kMaxExperts = 1024;
 

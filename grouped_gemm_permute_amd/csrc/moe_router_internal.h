@@ -14,7 +14,7 @@ constexpr int kRouterMaxGateElems = 16384;     // D * E
 // Histogram columns the router writes per permute block of
 // kPermuteBlockSlots slots (each router workgroup counts the slots of one
 // column).
-constexpr int kRouterSub = 8;
+constexpr int kRouterSub = 4;
 
 // logits[t] = x[t] gate_w (fp32 accumulation); topk_idx[t] = the k largest
 // logits' experts in descending order (equal logits: lower expert first);
