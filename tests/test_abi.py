@@ -129,7 +129,7 @@ def test_permute_rejects_bad_arguments_on_host():
     big = list(args); big[1] = 10000                     # needs scratch for the multi-block path
     assert lib.moe_ffn_forward is not None
     assert lib.moe_expert_permute(*big) == L.MOE_ERR_WORKSPACE
-    assert lib.moe_expert_permute_scratch_size(10000, 2, 4) == 5 * ((20000 + 2047) // 2048) * 4
+    assert lib.moe_expert_permute_scratch_size(10000, 2, 4) == 5 * ((20000 + 1023) // 1024) * 4
     assert lib.moe_expert_permute_scratch_size(100, 2, 4) == 0
 
 
