@@ -118,8 +118,9 @@ __host__ __device__ inline FusedPlan fused_plan(int W, int chunks) {
 // most kFusedUnits split workgroups, 64 x D floats each.
 size_t fused_partial_bytes(int64_t R, int G, int D, int F);
 // Y [R, D] bf16 for whole tiles; split tiles write P and need
-// launch_fused_reduce afterwards (on the same stream; it returns at once
-// when the call splits nothing).
+// launch_fused_reduce afterwards, on the same stream (always launched: the
+// split tiles are known on the device only; with none, its workgroups exit
+// at once).
 hipError_t launch_fused_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
                              const void* W2, const void* Ws1, const void* Ws3, const void* Ws2,
                              void* Y, float* P, int D, int F, hipStream_t s);
