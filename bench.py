@@ -612,11 +612,41 @@ def clock_record(m, value_tflops):
             "peak_bf16_tflops_at_2p4ghz": round(cus * 2.4e9 * 4096 / 1e12, 1)}
 
 
+def measured_read_gbs(nbytes=2 << 30, blocks=(128, 192, 256), launches=10):
+    """HBM read rate of a plain streaming kernel (moe_stream_read) over a
+    buffer of nbytes (larger than the on-die caches): the best over the
+    launch shapes `blocks` of the median over launches."""
+    import numpy as np
+    import torch
+
+    import grouped_gemm_permute_amd as gg
+    if isinstance(blocks, int):
+        blocks = (blocks,)
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    best = 0.0
+    for nb in blocks:
+        sink = torch.empty(nb, dtype=torch.int32, device="cuda")
+        gg.stream_read(buf, sink)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+        torch.cuda.synchronize()
+        for i in range(launches):
+            ev[i].record()
+            gg.stream_read(buf, sink)
+        ev[launches].record()
+        torch.cuda.synchronize()
+        ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(launches)]))
+        best = max(best, nbytes / (ms * 1e-3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return round(best, 1)
+
+
 def small_chunk_record(args):
     """The small-chunk workload (512 tokens, 8 experts of ~128 rows) in the
     same run: it is bound by streaming the experts' weights, so it is priced
     in HBM bytes (x, y, routing and the weights of every active expert) per
-    forward, against 8 TB/s."""
+    forward, against 8 TB/s and against the read rate a plain streaming
+    kernel measures on the same GPU."""
     import numpy as np
     m = measure_forward(3, "unfused", steps=max(args.steps, 200), warmup=max(args.warmup, 20),
                         rotate_bytes=args.rotate_bytes)
@@ -625,10 +655,12 @@ def small_chunk_record(args):
     pc = percentiles(m["per_call"])
     roof, stage_ms = dominant_roofline(m, "unfused")
     gbs = nbytes / (pc["median"] * 1e-3) / 1e9
+    read_gbs = measured_read_gbs()
     return {"workload": w.name, "T": w.T, "D": w.D, "F": w.F, "E": w.E, "k": w.k,
             "steps": max(args.steps, 200), "rotated_sets": m["R"],
             "ms_per_call": pc, "ms_per_step_host_clock": round(m["ms_per_step"], 5),
             "bytes_alg": nbytes, "gbs": round(gbs, 1), "frac_of_8tbs": round(gbs / PEAK_HBM_GBS, 4),
+            "stream_read_gbs_measured": read_gbs, "frac_of_measured_read": round(gbs / read_gbs, 4),
             "stage_ms_mean_with_events": {k: round(v, 5) for k, v in stage_ms.items()},
             "dominant": roof}
 

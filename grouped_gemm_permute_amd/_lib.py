@@ -27,6 +27,7 @@ EXPORTS = (
     "moe_ffn_get_device_error", "moe_ffn_backward_workspace_layout", "moe_ffn_backward_workspace_size",
     "moe_ffn_backward", "moe_ffn_backward_timed", "moe_router_topk", "moe_ffn_forward_routed",
     "moe_ffn_forward_routed_timed", "moe_device_clock_sample", "moe_ffn_forward_noalloc",
+    "moe_stream_read",
 )
 
 # Bytes of the per-device workspace array behind moe_ffn_forward_noalloc.
@@ -109,6 +110,8 @@ def lib():
         L.moe_ffn_forward_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, i64, ci, ci, ci, ci, ci, ci, P]
         L.moe_device_clock_sample.restype = ci
         L.moe_device_clock_sample.argtypes = [P, ci, P]
+        L.moe_stream_read.restype = ci
+        L.moe_stream_read.argtypes = [P, ctypes.c_size_t, P, ci, P]
         L.moe_ffn_get_device_error.restype = ci
         L.moe_ffn_get_device_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32)]
         _lib = L
@@ -316,6 +319,15 @@ def device_clock_sample(blocks=1024, stream=None):
     out = torch.empty((blocks, 3), dtype=torch.int64, device="cuda")
     _check(lib().moe_device_clock_sample(_ptr(out), blocks, _stream(stream)), "moe_device_clock_sample")
     return out
+
+
+def stream_read(buf, sink, stream=None):
+    """Read every byte of the device tensor buf once (moe_stream_read) with
+    sink.numel() workgroups; sink is a device int32 tensor."""
+    if not (buf.is_cuda and sink.is_cuda and sink.dtype == torch.int32 and buf.is_contiguous()):
+        raise TypeError("stream_read: buf and sink must be contiguous GPU tensors, sink int32")
+    _check(lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), sink.numel(),
+                                 _stream(stream)), "moe_stream_read")
 
 
 def engine_clock_ghz(before, after):

@@ -262,6 +262,25 @@ moe_status moe_ffn_get_device_error(const void *workspace, hipStream_t stream, i
  */
 moe_status moe_device_clock_sample(int64_t *out, int blocks, hipStream_t stream);
 
+/*
+ * Measurement helper (not part of the layer): read `bytes` of device memory
+ * once with a plain streaming kernel of `blocks` workgroups of 512 threads
+ * on `stream` (each thread 16 bytes at a time, eight in flight,
+ * non-temporal), so that the
+ * read rate it reaches, timed by the caller, prices kernels bound by
+ * reading their operands once against what this part delivers rather than
+ * against the nominal 8 TB/s.  Workgroup b writes the xor of what it read
+ * to sink[b].
+ *
+ *   src    device pointer, 16-byte aligned; bytes a positive multiple of 16
+ *   sink   device uint32 [blocks], 4-byte aligned, caller-owned
+ *   blocks 1 .. 65536
+ *
+ * Returns MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_HIP.
+ */
+moe_status moe_stream_read(const void *src, size_t bytes, uint32_t *sink, int blocks,
+                           hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Router in front of the layer.
  *

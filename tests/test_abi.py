@@ -117,6 +117,15 @@ def test_fused_layout_64_row_tiles_and_partial_outputs():
     assert lay["Y"] - lay["h"] == 64 * 64 * D * 4
 
 
+def test_stream_read_rejects_bad_arguments_on_host():
+    lib = L.lib()
+    assert lib.moe_stream_read(None, 1024, FAKE, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_read(FAKE, 1000, FAKE, 8, None) == L.MOE_ERR_INVALID_ARG   # not 16-byte sized
+    assert lib.moe_stream_read(FAKE, 0, FAKE, 8, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_read(FAKE, 1024, FAKE, 0, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_read(FAKE + 8, 1024, FAKE, 8, None) == L.MOE_ERR_INVALID_ARG  # misaligned
+
+
 def test_permute_rejects_bad_arguments_on_host():
     lib = L.lib()
     args = [FAKE, 10, 2, 4, 256, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None]

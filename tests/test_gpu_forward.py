@@ -212,3 +212,19 @@ def test_forward_edge_cases():
     inp = make_case(0, 64, 64, 2, 1, False, "bf16")
     y, _ = gpu_forward(inp)
     assert y.shape == (0, 64)
+
+
+def test_stream_read_reads_every_word_once():
+    """The measurement helper behind the small-chunk record's read peak: each
+    16-byte chunk is read by exactly one thread, so the xor over all
+    workgroups' sinks is the xor of every word of the buffer."""
+    import grouped_gemm_permute_amd as gg
+    n = (1 << 20) + 4 * 37                         # a tail past the unrolled passes
+    host = np.random.default_rng(3).integers(-2**31, 2**31 - 1, size=n, dtype=np.int64).astype(np.int32)
+    buf = torch.from_numpy(host).cuda()
+    for blocks in (1, 64, 1000):
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        say(f"stream_read blocks={blocks}")
+        gg.stream_read(buf, sink)
+        got = np.bitwise_xor.reduce(sink.cpu().numpy())
+        assert got == np.bitwise_xor.reduce(host)
