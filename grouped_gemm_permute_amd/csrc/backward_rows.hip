@@ -1,6 +1,8 @@
 // backward_rows.hip -- the backward pass of the routed SwiGLU MoE layer as
 // plain kernels: one thread per output element, fp32 accumulation, for both
-// storage types (fp32, and bf16 with fp32 arithmetic).
+// storage types (fp32, and bf16 with fp32 arithmetic).  Their reduction
+// loops are unrolled so that a thread's loads go out together (the FMA
+// order, and so every result, is that of the plain loop).
 //
 // The vector-Jacobian product follows the autograd contract of "Triton MoE
 // Kernels & Memory Checkpointing" (Part A, section 8): the gate and up
@@ -73,6 +75,7 @@ __global__ __launch_bounds__(NT) void gate_up_kernel(BwdArgs a, const T* __restr
     const T* w3 = sh ? Ws3 : W3 + (int64_t)grp * D * F;
     const int64_t xo = token_of(a.g, grp, p) * D;
     float g = 0.f, u = 0.f;
+#pragma unroll 16
     for (int d = 0; d < D; ++d) {
         const float xv = ld(x, xo + d);
         g = fmaf(xv, ld(w1, (int64_t)d * F + f), g);
@@ -101,6 +104,7 @@ __global__ __launch_bounds__(kBwdDwBlock) void dh_kernel(BwdArgs a, const T* __r
     const int64_t yo = token_of(a.g, grp, p) * D;
     float dhp = 0.f;
     if (valid)
+#pragma unroll 16
         for (int d = 0; d < D; ++d) dhp = fmaf(ld(dy, yo + d), ld(w2, (int64_t)f * D + d), dhp);
     const float w = sh ? 1.f : a.topk_w[a.g.perm[p]];
     float prod = 0.f;
@@ -136,7 +140,9 @@ __global__ __launch_bounds__(NT) void dx_rows_kernel(BwdArgs a, const T* __restr
     const T* w3 = (sh ? Ws3 : W3 + (int64_t)grp * D * F) + (int64_t)d * F;
     const int64_t ro = p * 2 * F;
     float acc = 0.f;
+#pragma unroll 16
     for (int f = 0; f < F; ++f) acc = fmaf(ld(dgu, ro + f), ld(w1, f), acc);
+#pragma unroll 16
     for (int f = 0; f < F; ++f) acc = fmaf(ld(dgu, ro + F + f), ld(w3, f), acc);
     st(dxr, p * D + d, acc);
 }
@@ -160,6 +166,7 @@ __global__ __launch_bounds__(NT) void dw13_kernel(BwdArgs a, const T* __restrict
     int64_t p0, p1;
     group_rows(a.g, grp, p0, p1);
     float acc = 0.f;
+#pragma unroll 8
     for (int64_t p = p0; p < p1; ++p)
         acc = fmaf(ld(x, token_of(a.g, grp, p) * D + d), ld(dgu, p * 2 * F + c), acc);
     const bool sh = grp == a.g.E;
@@ -179,6 +186,7 @@ __global__ __launch_bounds__(NT) void dw2_kernel(BwdArgs a, const T* __restrict_
     int64_t p0, p1;
     group_rows(a.g, grp, p0, p1);
     float acc = 0.f;
+#pragma unroll 8
     for (int64_t p = p0; p < p1; ++p)
         acc = fmaf(ld(hw, p * F + f), ld(dy, token_of(a.g, grp, p) * D + d), acc);
     (grp == a.g.E ? dWs2 : dW2 + (int64_t)grp * F * D)[i] = acc;
