@@ -161,8 +161,10 @@ __global__ __launch_bounds__(RT) void router_kernel(const void* __restrict__ xv,
 // bf16 path on MFMA.  A wavefront takes 32 tokens: the MFMA's A operand is
 // 32 token rows x 16 features (lane l: token l%32, features 8 (l/32) .. +7 of
 // the step, read straight from x), its B operand 16 features x 32 experts
-// from the gate matrix staged in LDS as bf16 [32 experts, D] (rows past E
-// are zero; rows padded by 16 bytes against bank conflicts).  The 32 x 32
+// from the gate matrix staged in LDS as bf16 [32 experts, D] (rows padded
+// by 16 bytes against bank conflicts).  Rows E .. 31 are left as they are:
+// they only feed the logit columns of experts E .. 31, which are never read
+// (zeroing them cost 4.5 us of the 24 us kernel on 32768 tokens).  The 32 x 32
 // fp32 logits go through LDS so that lane j < 32 holds token j's logits and
 // selects its k experts serially.
 constexpr int MT = 256;                            // 4 wavefronts
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(MT) void router_mfma_kernel(const uint16_t* __restr
     int32_t* cnt = (int32_t*)(lg + 4 * 32 * 33);       // [E + 1]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // stage: 16-byte loads of gate [D, E] (D * E is a multiple of 16),
-    // each element stored to its expert row; rows E .. 31 are zero
+    // each element stored to its expert row
     for (int i = tid; i < D * E / 8; i += MT) {
         const uint4 q = *(const uint4*)(gate + 8 * (int64_t)i);
         const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -193,10 +195,6 @@ __global__ __launch_bounds__(MT) void router_mfma_kernel(const uint16_t* __restr
             const int f = 8 * i + j, d = f / E, e = f - d * E;
             *(uint16_t*)(gw + e * rowb + 2 * d) = (uint16_t)(j & 1 ? w[j >> 1] >> 16 : w[j >> 1] & 0xffff);
         }
-    }
-    for (int i = tid; i < (32 - E) * D; i += MT) {
-        const int e = E + i / D, d = i - (e - E) * D;
-        *(uint16_t*)(gw + e * rowb + 2 * d) = 0;
     }
     for (int e = tid; e <= E; e += MT) cnt[e] = 0;
     __syncthreads();
