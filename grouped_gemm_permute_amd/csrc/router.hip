@@ -185,6 +185,27 @@ __global__ __launch_bounds__(MT) void router_mfma_kernel(const uint16_t* __restr
     float* lg = (float*)(smem + 32 * rowb);            // [4 waves][32 tokens][33]
     int32_t* cnt = (int32_t*)(lg + 4 * 32 * 33);       // [E + 1]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t S = T * k;
+    int64_t s_lo = 0, s_hi = 0, t0, t1;
+    if (hist) {
+        s_lo = (int64_t)blockIdx.x * slots_per_col;
+        s_hi = min(S, s_lo + slots_per_col);
+        t0 = s_lo / k;
+        t1 = s_hi > s_lo ? (s_hi + k - 1) / k : t0;
+    } else {
+        t0 = (int64_t)blockIdx.x * 128;
+        t1 = min(T, t0 + 128);
+    }
+    // The first 256 features of this wavefront's first token block do not
+    // depend on the gate matrix: their loads go out before it is staged.
+    u32x4_t pre[16];
+    const bool has_pre = t0 + 32 * wave < t1 && D >= 256;
+    if (has_pre) {
+        const int64_t tr = min(t0 + 32 * wave + (lane & 31), T - 1);
+        const uint16_t* xr = x + tr * D + 8 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pre[i] = *(const u32x4_t*)(xr + 16 * i);
+    }
     // stage: 16-byte loads of gate [D, E] (D * E is a multiple of 16),
     // each element stored to its expert row
     for (int i = tid; i < D * E / 8; i += MT) {
@@ -199,17 +220,6 @@ __global__ __launch_bounds__(MT) void router_mfma_kernel(const uint16_t* __restr
     for (int e = tid; e <= E; e += MT) cnt[e] = 0;
     __syncthreads();
 
-    const int64_t S = T * k;
-    int64_t s_lo = 0, s_hi = 0, t0, t1;
-    if (hist) {
-        s_lo = (int64_t)blockIdx.x * slots_per_col;
-        s_hi = min(S, s_lo + slots_per_col);
-        t0 = s_lo / k;
-        t1 = s_hi > s_lo ? (s_hi + k - 1) / k : t0;
-    } else {
-        t0 = (int64_t)blockIdx.x * 128;
-        t1 = min(T, t0 + 128);
-    }
     float* mylg = lg + wave * 32 * 33;
     for (int64_t tb = t0 + 32 * wave; tb < t1; tb += 128) {
         const int64_t tr = min(tb + (lane & 31), T - 1);
@@ -220,8 +230,9 @@ __global__ __launch_bounds__(MT) void router_mfma_kernel(const uint16_t* __restr
         // 16 steps at a time: all 16 row loads in flight before the MFMAs
         for (; k0 + 256 <= D; k0 += 256) {
             u32x4_t a[16];
+            const bool first = has_pre && k0 == 0 && tb == t0 + 32 * wave;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) a[i] = *(const u32x4_t*)(xr + k0 + 16 * i);
+            for (int i = 0; i < 16; ++i) a[i] = first ? pre[i] : *(const u32x4_t*)(xr + k0 + 16 * i);
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
