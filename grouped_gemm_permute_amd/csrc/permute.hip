@@ -35,6 +35,8 @@ using namespace permute_dev;
 constexpr int kSingleThreads = 512;
 constexpr int kScatterThreads = 256;
 constexpr int kScanThreads = 1024;
+constexpr int kBlockChunks = kPermuteBlockSlots / kScatterThreads;   // scatter chunks per block
+static_assert(kBlockChunks * kScatterThreads == kPermuteBlockSlots, "whole chunks per block");
 // Largest histogram table, (E+1) x nblocks entries, that every scatter block
 // re-reads itself instead of a separate scan launch.
 constexpr int64_t kFusedScanEntries = 8192;
@@ -115,14 +117,20 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
     __shared__ int32_t run[kMaxExperts];
     __shared__ int32_t wcnt[(kScatterThreads / 64) * kMaxExperts];
     const int tid = threadIdx.x, b = blockIdx.x, nb = gridDim.x;
+    const int64_t lo = (int64_t)b * kPermuteBlockSlots;
+    const int64_t hi = min(S, lo + kPermuteBlockSlots);
+    int keys[kBlockChunks];
+#pragma unroll
+    for (int q = 0; q < kBlockChunks; ++q) keys[q] = key_of(idx, lo + q * kScatterThreads + tid, hi, E);
     for (int e = tid; e < E; e += kScatterThreads) run[e] = hist[(int64_t)e * nb + b];
     for (int i = tid; i < (kScatterThreads / 64) * E; i += kScatterThreads) wcnt[i] = 0;
     __syncthreads();
     const int nbits = key_bits(E);
-    const int64_t lo = (int64_t)b * kPermuteBlockSlots;
-    const int64_t hi = min(S, lo + kPermuteBlockSlots);
-    for (int64_t c0 = lo; c0 < hi; c0 += kScatterThreads)
-        scatter_chunk<kScatterThreads>(idx, c0, hi, S, E, nbits, run, wcnt, perm, inv);
+#pragma unroll
+    for (int q = 0; q < kBlockChunks; ++q)
+        if (lo + q * kScatterThreads < hi)
+            scatter_chunk<kScatterThreads>(keys[q], lo + q * kScatterThreads, hi, S, E, nbits, run,
+                                           wcnt, perm, inv);
 }
 
 // Scan and scatter in one launch.  Block b reads the histogram table
@@ -143,6 +151,12 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scan_scatter_kernel(
     __shared__ int32_t run[kMaxExperts + 1];
     __shared__ int32_t wcnt[(kScatterThreads / 64) * kMaxExperts];
     const int tid = threadIdx.x, b = blockIdx.x, nb = gridDim.x;
+    // this block's keys first: their loads overlap the table scan below
+    const int64_t lo = (int64_t)b * kPermuteBlockSlots;
+    const int64_t hi = min(S, lo + kPermuteBlockSlots);
+    int keys[kBlockChunks];
+#pragma unroll
+    for (int q = 0; q < kBlockChunks; ++q) keys[q] = key_of(idx, lo + q * kScatterThreads + tid, hi, E);
     for (int e = tid; e <= E; e += kScatterThreads) tot[e] = run[e] = 0;
     for (int i = tid; i < (kScatterThreads / 64) * E; i += kScatterThreads) wcnt[i] = 0;
     __syncthreads();
@@ -171,10 +185,11 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scan_scatter_kernel(
         for (int64_t p = valid + tid; p < S; p += kScatterThreads) perm[p] = -1;
     }
     const int nbits = key_bits(E);
-    const int64_t lo = (int64_t)b * kPermuteBlockSlots;
-    const int64_t hi = min(S, lo + kPermuteBlockSlots);
-    for (int64_t c0 = lo; c0 < hi; c0 += kScatterThreads)
-        scatter_chunk<kScatterThreads>(idx, c0, hi, S, E, nbits, run, wcnt, perm, inv);
+#pragma unroll
+    for (int q = 0; q < kBlockChunks; ++q)
+        if (lo + q * kScatterThreads < hi)
+            scatter_chunk<kScatterThreads>(keys[q], lo + q * kScatterThreads, hi, S, E, nbits, run,
+                                           wcnt, perm, inv);
 }
 
 }  // namespace

@@ -61,17 +61,18 @@ __device__ inline void finish_scan(const int32_t* cnt, int E, TileSpec ta, TileS
     err[0] = cnt[E];
 }
 
-// Rank the slots [c0, c0 + blockDim) of one chunk and scatter them.
+// Rank the slots [c0, c0 + blockDim) of one chunk and scatter them; key is
+// this thread's key_of(idx, c0 + threadIdx.x, end, E), loaded by the caller
+// (so that a block's loads can all be in flight at once).
 // run[e]: next free position of expert e; wcnt [nwaves][E] zeroed on entry
 // and on exit.
 // Slots at or past `end` are not part of this chunk; S bounds every write.
 template <int NT>
-__device__ inline void scatter_chunk(const int32_t* idx, int64_t c0, int64_t end, int64_t S, int E,
-                              int nbits, int32_t* run, int32_t* wcnt, int32_t* perm, int32_t* inv) {
+__device__ inline void scatter_chunk(int key, int64_t c0, int64_t end, int64_t S, int E, int nbits,
+                                     int32_t* run, int32_t* wcnt, int32_t* perm, int32_t* inv) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
     const int64_t s = c0 + tid;
-    const int key = key_of(idx, s, end, E);
     const uint64_t peers = match_peers(key, nbits);
     const int rank = __popcll(peers & ((1ull << lane) - 1ull));
     if (rank == 0 && key < E) wcnt[wave * E + key] = __popcll(peers);
@@ -110,17 +111,27 @@ __device__ void permute_one_workgroup(const int32_t* idx, int64_t S, int E, Tile
                                       int64_t shared_rows, int32_t* counts, int32_t* offsets,
                                       int32_t* perm, int32_t* inv, int32_t* err, int32_t* cnt,
                                       int32_t* run, int32_t* wcnt) {
+    constexpr int KPT = (int)(kPermuteSingleMax / NT);   // slots per thread (S <= kPermuteSingleMax)
+    static_assert(KPT * NT == kPermuteSingleMax, "whole chunks");
     const int tid = threadIdx.x;
+    // every key of this thread, loaded once, all in flight together
+    int keys[KPT];
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) keys[q] = key_of(idx, (int64_t)q * NT + tid, S, E);
     for (int e = tid; e <= E; e += NT) cnt[e] = 0;
     for (int i = tid; i < (NT / 64) * E; i += NT) wcnt[i] = 0;
     __syncthreads();
-    for (int64_t s = tid; s < S; s += NT) atomicAdd(&cnt[key_of(idx, s, S, E)], 1);
+#pragma unroll
+    for (int q = 0; q < KPT; ++q)
+        if (keys[q] <= E) atomicAdd(&cnt[keys[q]], 1);
     __syncthreads();
     if (tid == 0) finish_scan(cnt, E, ta, tb, shared_rows, counts, offsets, err, run);
     __syncthreads();
     const int nbits = key_bits(E);
-    for (int64_t c0 = 0; c0 < S; c0 += NT)
-        scatter_chunk<NT>(idx, c0, S, S, E, nbits, run, wcnt, perm, inv);
+#pragma unroll
+    for (int q = 0; q < KPT; ++q)
+        if ((int64_t)q * NT < S)
+            scatter_chunk<NT>(keys[q], (int64_t)q * NT, S, S, E, nbits, run, wcnt, perm, inv);
     const int32_t valid = (int32_t)(S - cnt[E]);
     for (int64_t p = valid + tid; p < S; p += NT) perm[p] = -1;
 }
