@@ -51,9 +51,11 @@
 //        a row tile (2 x 4 accumulators, a ring of three 24 KiB stages,
 //        72 KiB), so two workgroups share a CU and one's prologue and SiLU
 //        epilogue run under the other's MFMAs;
-//      - dh: 4 wavefronts on a whole tile, wavefront w owning features
-//        64 w .. +63 of all 256 rows (2 x 8 accumulators), its epilogue using
-//        all four stage buffers;
+//      - dh: half tiles as well (4 wavefronts, two workgroups per CU),
+//        wavefront w owning features 64 w .. +63 of the half's 128 rows
+//        (2 x 4 accumulators); its store-heavy epilogue runs under the other
+//        workgroup's MFMAs and is staged through the ring's buffers plus
+//        8 KiB (80 KiB per workgroup);
 //    spreading the wavefronts over the features rather than 2 x 2 halves the
 //    slow transposed weight reads per MFMA;
 //  * K step 32; both tiles go global -> LDS with global_load_lds (16 bytes
@@ -104,17 +106,19 @@ enum : int {
 //  * whole tiles (HALF = false): 8 wavefronts, two per SIMD, on a 256-row
 //    tile, one workgroup per CU (a 4-stage ring of 32 KiB), so one
 //    wavefront's MFMAs cover the other's stalls issuing loads;
-//  * half tiles (HALF = true, up only): 4 wavefronts on one 128-row half of
-//    a tile (a 3-stage ring of 24 KiB), two workgroups per CU, so the SiLU
+//  * half tiles (HALF = true, up and dh): 4 wavefronts on one 128-row half
+//    of a tile (a 3-stage ring of 24 KiB), two workgroups per CU, so the
 //    epilogue and the prologue of one overlap the other's MFMAs and the
 //    last round is finer.  It stages 1.5x the bytes per MFMA: the up GEMM
 //    takes it when its whole-tile grid is short (up_half_tiles), where it
 //    measured 3-9% faster; on long grids it is even to 1% slower, and for
-//    gate/up and down 4-10% slower;
-//  * dh: 4 wavefronts on a whole tile, its epilogue using all the LDS.
+//    gate/up and down 4-10% slower.  dh, whose epilogue moves 640 KiB per
+//    256-row tile, always takes it: 522 -> 487 us at 32768 tokens and
+//    110 -> 83 us at 4096 (D = 768, F = 1536, E = 8; before, 4 wavefronts
+//    on a whole tile, one workgroup per CU).
 template <int MODE, bool HALF>
 constexpr int waves_of() {
-    return HALF || MODE == M_DH ? 4 : 8;
+    return HALF ? 4 : 8;
 }
 
 struct GemmArgs {
@@ -143,7 +147,7 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
     const GemmArgs a) {
     constexpr bool UP = MODE != M_DOWN;         // A gathered by token, K = D, N = F
     constexpr bool PAIR = MODE == M_UP || MODE == M_GU;   // g / u column pairs from W1, W3
-    static_assert(!HALF || MODE == M_UP, "half tiles are built for the up GEMM");
+    static_assert(!HALF || MODE == M_UP || MODE == M_DH, "half tiles are built for the up and dh GEMMs");
     constexpr int NW = waves_of<MODE, HALF>();
     constexpr int NT = 64 * NW;
     constexpr int ROWS = HALF ? TT / 2 : TT;   // rows of the workgroup's tile
@@ -159,7 +163,8 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
     __shared__ __attribute__((aligned(1024))) char st0[SBYTES];
     __shared__ __attribute__((aligned(1024))) char st1[SBYTES];
     __shared__ __attribute__((aligned(1024))) char st2[SBYTES];
-    __shared__ __attribute__((aligned(1024))) char st3[NS == 4 ? SBYTES : 16];
+    // (dh: an 8 KiB fourth buffer for its epilogue's g/u scratch)
+    __shared__ __attribute__((aligned(1024))) char st3[NS == 4 ? SBYTES : MODE == M_DH ? 8192 : 16];
 
     const int K = UP ? a.D : a.F;      // reduction length
     const int N = UP ? a.F : a.D;      // output columns
@@ -463,34 +468,36 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
     // output column = MFMA feature.  The tile's rows are staged RPS to a
     // stage buffer, 16-byte chunks XOR-swizzled by the row's low 4 bits.
     if constexpr (MODE == M_DH) {
-        static_assert(!HALF && NW == 4, "the dh epilogue lays out one wavefront per 64 columns of all 256 rows");
+        static_assert(HALF && NW == 4 && NJ == 4 && NS == 3,
+                      "the dh epilogue lays out one wavefront per 64 columns of a 128-row half tile");
         // Element v of acc[mi][nj] on lane l: token 32 nj + l%32, column
         // nt*256 + 64 w + 32 mi + 8 (v/4) + 4 (l/32) + v%4; each lane handles
         // four consecutive columns at a time.  The wavefront's 64 columns are
         // one dwpart block; the two lane halves holding a token's columns are
-        // added with one cross-lane exchange.  g and u are loaded a token
-        // block ahead; dg, du and w h go through LDS (two
-        // buffers of 32 rows, 16-byte chunks XOR-swizzled by the row) so that
-        // the stores write whole 512-byte row segments.
+        // added with one cross-lane exchange.  g and u of the next 32-row
+        // block are loaded while this block is stored; dg, du and w h go
+        // through LDS (one block at a time: dg in the lower 16 KiB of st0,
+        // du of st1, w h of st2, 512-byte rows, 16-byte chunks XOR-swizzled
+        // by the row) so that the stores write whole 512-byte row segments.
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
         __syncthreads();                         // every wavefront is done with the stage buffers
         const int F = a.F;
         const int nbk = F / 64;
         const int blk = nt * 4 + wave;
         const bool cols_ok = nt * TF + 64 * wave < F;   // F % 64 == 0: all or none of a wavefront's
-        int64_t prow[8];
-        float wrow[8];
+        int64_t prow[NJ];
+        float wrow[NJ];
 #pragma unroll
-        for (int nj = 0; nj < 8; ++nj) prow[nj] = tile_r0 + min(32 * nj + (lane & 31), valid_rows - 1);
+        for (int nj = 0; nj < NJ; ++nj) prow[nj] = tile_r0 + min(32 * nj + (lane & 31), valid_rows - 1);
         if (shared) {
 #pragma unroll
-            for (int nj = 0; nj < 8; ++nj) wrow[nj] = 1.f;
+            for (int nj = 0; nj < NJ; ++nj) wrow[nj] = 1.f;
         } else {
-            int32_t slot[8];
+            int32_t slot[NJ];
 #pragma unroll
-            for (int nj = 0; nj < 8; ++nj) slot[nj] = a.g.perm[prow[nj]];
+            for (int nj = 0; nj < NJ; ++nj) slot[nj] = a.g.perm[prow[nj]];
 #pragma unroll
-            for (int nj = 0; nj < 8; ++nj) wrow[nj] = a.topk_w[slot[nj]];
+            for (int nj = 0; nj < NJ; ++nj) wrow[nj] = a.topk_w[slot[nj]];
         }
         // g, u of the lane's 4 columns nt*256 + 64 w + 32 mi + 8 vg + 4 (l/32) + 0..3
         struct GU {
@@ -500,13 +507,13 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
         // (instruction j: rows 8 (j%4) .. +7 of the block, g for j < 4 else u;
         // lane: row + lane/8, 16-byte chunk lane%8 of the wavefront's 64
         // columns), then rearranged into the accumulator layout through an
-        // 8 KiB LDS scratch of the wavefront's own (upper halves of stage
-        // buffers 1 and 3; w h is staged in the lower halves), 16-byte chunks
-        // XOR-swizzled by row / 2.
+        // 8 KiB LDS scratch of the wavefront's own (the upper 8 KiB of stage
+        // buffer w, or st3 for w = 3), 16-byte chunks XOR-swizzled by row / 2.
         struct Raw {
             u32x4_t v[8];
         };
-        char* const gus = (wave < 2 ? st1 : st3) + 16384 + (wave & 1) * 8192;
+        char* const gus = wave == 0 ? st0 + 16384 : wave == 1 ? st1 + 16384
+                        : wave == 2 ? st2 + 16384 : st3;
         const int fc0 = cols_ok ? nt * TF + 64 * wave : 0;   // the wavefront's first column (readable)
         auto swz_gu = [](int r) { return (r >> 1) & 7; };
         auto load_raw = [&](int nj, Raw& R) {
@@ -533,14 +540,11 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
                     b.u[mi][vg] = *(const uint2*)(gus + 4096 + off);
                 }
         };
-        // staging: buffer q holds [dg 256 | du 256] (1 KiB rows) in stage
-        // buffer 2q and w h (512-byte rows) in stage buffer 2q + 1
-        auto stage_dgdu = [&](int q) -> char* { return q ? st2 : st0; };
-        auto stage_hw = [&](int q) -> char* { return q ? st3 : st1; };
         const int r_l = lane & 31;
         auto finish_block = [&](int nj, const GU& b) {
-            char* sdg = stage_dgdu(nj & 1) + r_l * 1024;
-            char* shw = stage_hw(nj & 1) + r_l * 512;
+            char* sdg = st0 + r_l * 512;
+            char* sdu = st1 + r_l * 512;
+            char* shw = st2 + r_l * 512;
             const float w = wrow[nj];
             float part = 0.f;
 #pragma unroll
@@ -571,7 +575,7 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
                     const int off = 8 * (lane >> 5);
                     *(uint2*)(sdg + ((ch ^ r_l) << 4) + off) =
                         make_uint2(pack_bf16(dg[0], dg[1]), pack_bf16(dg[2], dg[3]));
-                    *(uint2*)(sdg + (((32 + ch) ^ r_l) << 4) + off) =
+                    *(uint2*)(sdu + ((ch ^ r_l) << 4) + off) =
                         make_uint2(pack_bf16(du[0], du[1]), pack_bf16(du[2], du[3]));
                     *(uint2*)(shw + ((ch ^ r_l) << 4) + off) =
                         make_uint2(pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3]));
@@ -583,14 +587,13 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
             *(ok ? a.dwpart + prow[nj] * nbk + blk : (float*)dh_trash) = part;
         };
         // rows 32 nj .. 32 nj + 31 of the staged block go out as whole 16-byte
-        // chunks: [dg | du] 64 chunks per row, w h 32 chunks per row
-        // Every thread issues the same 12 stores per block whatever the
-        // tile's valid rows and columns (the others go to a 16-byte trash
-        // slot), so that the compiler can count the stores issued after a
-        // block's g/u loads and wait for those loads alone.
+        // chunks: dg and du 32 chunks per row each (chunk c < 32 of dg, else
+        // of du), w h 32 chunks per row.  Every thread issues the same 12
+        // stores per block whatever the tile's valid rows and columns (the
+        // others go to a 16-byte trash slot), so that the compiler can count
+        // the stores issued after a block's g/u loads and wait for those
+        // loads alone.
         auto store_block = [&](int nj) {
-            const char* sdg = stage_dgdu(nj & 1);
-            const char* shw = stage_hw(nj & 1);
             const int c = tid & 63;
             const int col = nt * TF + 8 * (c & 31);
 #pragma unroll
@@ -598,7 +601,7 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
                 const int r = (tid >> 6) + 4 * i;
                 const bool ok = col < F && 32 * nj + r < valid_rows;
                 const int64_t p = tile_r0 + 32 * nj + r;
-                const u32x4_t v = *(const u32x4_t*)(sdg + r * 1024 + ((c ^ r) << 4));
+                const u32x4_t v = *(const u32x4_t*)((c < 32 ? st0 : st1) + r * 512 + (((c & 31) ^ r) << 4));
                 *(ok ? (u32x4_t*)((uint16_t*)a.out + p * 2 * F + (c < 32 ? 0 : F) + col) : dh_trash) = v;
             }
             const int c2 = tid & 31;
@@ -608,23 +611,29 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
                 const int r = (tid >> 5) + 8 * i;
                 const bool ok = col2 < F && 32 * nj + r < valid_rows;
                 const int64_t p = tile_r0 + 32 * nj + r;
-                const u32x4_t v = *(const u32x4_t*)(shw + r * 512 + ((c2 ^ r) << 4));
+                const u32x4_t v = *(const u32x4_t*)(st2 + r * 512 + ((c2 ^ r) << 4));
                 *(ok ? (u32x4_t*)(a.hw + p * F + col2) : dh_trash) = v;
             }
         };
         Raw raw;
         load_raw(0, raw);
 #pragma unroll
-        for (int nj = 0; nj < 8; ++nj) {
+        for (int nj = 0; nj < NJ; ++nj) {
             GU cur;
             unpack(raw, cur);
-            if (nj + 1 < 8) load_raw(nj + 1, raw);
             finish_block(nj, cur);
+            // the next block's g and u go out now, into the registers cur
+            // held (at two workgroups per CU registers are short)
+            if (nj + 1 < NJ) load_raw(nj + 1, raw);
             // the staged block is complete in LDS; a barrier that waits on
             // LDS only, so block nj + 1's loads stay in flight
             __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
             __builtin_amdgcn_s_barrier();
             store_block(nj);
+            // one staging buffer: every wavefront has read it out before the
+            // next block overwrites it
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+            __builtin_amdgcn_s_barrier();
         }
         return;
     }
@@ -764,7 +773,8 @@ hipError_t launch_bwd_dh_bf16(const GroupArgs& g, const float* topk_w, const voi
                dgu, D, F, (F + TF - 1) / TF, 1, topk_w, (const uint16_t*)gu, (uint16_t*)hw, dwpart};
     a.col_groups = column_groups(a.n_tiles, D);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<M_DH, false><<<grid_for_work(blocks), 64 * waves_of<M_DH, false>(), 0, s>>>(a);
+    // half tiles: two 128-row workgroups per 256-row tile
+    grouped_gemm_bf16_kernel<M_DH, true><<<grid_for_work(2 * blocks), 64 * waves_of<M_DH, true>(), 0, s>>>(a);
     return hipGetLastError();
 }
 
