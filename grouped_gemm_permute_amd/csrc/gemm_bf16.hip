@@ -37,7 +37,7 @@
 //    rows, so each lane ends with 4 consecutive output features of one token
 //    and stores 8 bytes at a time;
 //  * row tiles of 256 tokens x 256 MFMA features (up: 128 W1 + 128 W3
-//    columns of the same 128 outputs), in one of three workgroup shapes
+//    columns of the same 128 outputs), in one of two workgroup shapes
 //    (waves_of below), each chosen by interleaved A/Bs with bitwise-equal
 //    results:
 //      - whole tiles, 8 wavefronts (up on long grids, gate_up, down): two
@@ -47,15 +47,12 @@
 //        stages; one wavefront's MFMAs run while its partner is held issuing
 //        a load into a busy memory pipe;
 //      - half tiles, 4 wavefronts (up when its whole-tile grid is under
-//        twelve rounds of the CUs): a workgroup takes one 128-token half of
-//        a row tile (2 x 4 accumulators, a ring of three 24 KiB stages,
-//        72 KiB), so two workgroups share a CU and one's prologue and SiLU
-//        epilogue run under the other's MFMAs;
-//      - dh: half tiles as well (4 wavefronts, two workgroups per CU),
-//        wavefront w owning features 64 w .. +63 of the half's 128 rows
-//        (2 x 4 accumulators); its store-heavy epilogue runs under the other
-//        workgroup's MFMAs and is staged through the ring's buffers plus
-//        8 KiB (80 KiB per workgroup);
+//        twelve rounds of the CUs, and dh always): a workgroup takes one
+//        128-token half of a row tile, wavefront w owning features
+//        64 w .. +63 of its 128 rows (2 x 4 accumulators, a ring of three
+//        24 KiB stages, 72 KiB; dh adds 8 KiB for its epilogue), so two
+//        workgroups share a CU and one's prologue and epilogue (the SiLU,
+//        or dh's store-heavy one) run under the other's MFMAs;
 //    spreading the wavefronts over the features rather than 2 x 2 halves the
 //    slow transposed weight reads per MFMA;
 //  * K step 32; both tiles go global -> LDS with global_load_lds (16 bytes
@@ -358,8 +355,6 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
         // lands before the next step's wait.  Eight wavefronts (16 MFMAs, 4
         // loads, 16 reads): one load per 4 MFMAs over the whole step (the
         // front-loaded and the compiler's own orders measured 1-4% slower).
-        // dh (32 MFMAs, 8 loads, 24 reads): one load per 2 MFMAs in the
-        // first half of the step.
         if constexpr (NW == 8) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -373,7 +368,8 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-        } else if constexpr (HALF) {
+        } else {
+            static_assert(HALF, "four wavefronts run half tiles");
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
@@ -394,21 +390,6 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
         }
         fence();
