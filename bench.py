@@ -451,7 +451,8 @@ def percentiles(xs):
             "p90": round(float(np.percentile(a, 90)), 5), "mean": round(float(a.mean()), 5)}
 
 
-def measure_forward(wid, variant="unfused", steps=50, warmup=10, rotate_bytes=512e6, routed=False):
+def measure_forward(wid, variant="unfused", steps=50, warmup=10, rotate_bytes=512e6, routed=False,
+                    sustained_ms=0.0):
     """Time moe_ffn_forward (or the routed forward) on workload wid with its
     inputs resident in HBM and rotated over enough copies to exceed the
     on-die caches.
@@ -462,7 +463,14 @@ def measure_forward(wid, variant="unfused", steps=50, warmup=10, rotate_bytes=51
     each side.  Region 2: the same calls with HIP events recorded between the
     kernels (moe_ffn_forward_timed) for per-kernel durations; each record
     costs a few microseconds of GPU time, so whole-call figures come from
-    region 1 only."""
+    region 1 only.
+
+    With sustained_ms > 0, a third region follows: the same calls, untimed,
+    until the GPU has been kept busy for sustained_ms, then `steps` calls
+    timed with no event inside (host clock and engine clock around them).
+    The engine clock takes tens of milliseconds of sustained load to settle,
+    so regions 1 and 2 right after a short warmup run partly on a rising
+    clock; region 3 gives the settled rate beside them."""
     import numpy as np
     import torch
 
@@ -538,6 +546,28 @@ def measure_forward(wid, variant="unfused", steps=50, warmup=10, rotate_bytes=51
     stage_samples = {st: [hip.elapsed_ms(e[j], e[j + 1]) for e in evs] for j, st in enumerate(STAGES)}
     for e in evs:
         hip.destroy(e)
+
+    # Region 3 (optional): settled clock
+    sustained = None
+    if sustained_ms > 0:
+        t_end = time.perf_counter() + sustained_ms * 1e-3
+        i = 0
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                step(i)
+                i += 1
+            torch.cuda.synchronize()
+        s_clk0 = gg.device_clock_sample()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for j in range(steps):
+            step(i + j)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        s_clk1 = gg.device_clock_sample()
+        torch.cuda.synchronize()
+        sustained = {"ms_per_step": (t1 - t0) * 1e3 / steps, "calls_before": i,
+                     "clocks": gg.engine_clock_ghz(s_clk0.cpu(), s_clk1.cpu())}
     if routed:
         sidx, _ = gg.router_topk(sets[0]["x"], sets[0]["gate_w"], w.k)
         counts = np.bincount(sidx.cpu().numpy().reshape(-1), minlength=w.E)
@@ -548,7 +578,8 @@ def measure_forward(wid, variant="unfused", steps=50, warmup=10, rotate_bytes=51
     del sets, ws, y
     torch.cuda.empty_cache()
     return {"w": w, "inp": inp, "counts": counts, "R": R, "ms_per_step": ms_per_step,
-            "per_call": per_call, "stage_samples": stage_samples, "clocks": clocks, "small": small}
+            "per_call": per_call, "stage_samples": stage_samples, "clocks": clocks, "small": small,
+            "sustained": sustained}
 
 
 def dominant_roofline(m, variant):
@@ -610,6 +641,23 @@ def clock_record(m, value_tflops):
             "peak_bf16_tflops_at_measured_clock": round(peak, 1),
             "frac_of_peak_at_measured_clock": round(value_tflops / peak, 4),
             "peak_bf16_tflops_at_2p4ghz": round(cus * 2.4e9 * 4096 / 1e12, 1)}
+
+
+def sustained_record(m, w):
+    """Region 3 of measure_forward: the same steps timed after the GPU has
+    been kept busy (value is region 1, right after the warmup steps)."""
+    import numpy as np
+    s = m.get("sustained")
+    if not s:
+        return None
+    c = s["clocks"]
+    tf = w.flops() / (s["ms_per_step"] * 1e-3) / 1e12
+    return {"ms_per_step": round(s["ms_per_step"], 5), "tflops": round(tf, 3),
+            "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "calls_before": s["calls_before"],
+            "sclk_ghz_median": round(float(np.median(list(c.values()))), 4) if c else None,
+            "note": "the same steps timed again (host clock, no events inside) after the "
+                    "timed regions and calls_before further untimed calls; not the headline value"}
 
 
 def measured_read_gbs(nbytes=2 << 30, blocks=(128, 192, 256), launches=10):
@@ -689,6 +737,9 @@ def main():
     ap.add_argument("--sweep-point", type=int, default=None,
                     help="with --sweep: run only this point (index) and variant --variant, for "
                          "counter collection under rocprofv3")
+    ap.add_argument("--sustained-ms", type=float, default=150.0,
+                    help="after the timed regions, keep the GPU busy this long, then time the same "
+                         "steps again (reported as 'sustained', beside value; 0 skips it)")
     ap.add_argument("--copy-bytes", type=float, default=0,
                     help="only run a plain device-to-device copy of this many bytes --steps times "
                          "(the reference kernel for scaling HBM byte counters); prints its timing")
@@ -712,7 +763,7 @@ def main():
     import moe_inputs
     torch.cuda.set_device(0)
     m = measure_forward(args.workload, args.variant, args.steps, args.warmup, args.rotate_bytes,
-                        args.routed)
+                        args.routed, sustained_ms=args.sustained_ms)
     w, inp, counts = m["w"], m["inp"], m["counts"]
     value = w.flops() / (m["ms_per_step"] * 1e-3) / 1e12
     roof, stage_ms = dominant_roofline(m, args.variant)
@@ -745,6 +796,7 @@ def main():
         "ms_per_call": pc,
         "tflops_at_median_call": round(w.flops() / (pc["median"] * 1e-3) / 1e12, 3),
         "clock": clock_record(m, value),
+        "sustained": sustained_record(m, w),
         "hbm_gbs_path": round(path_bytes(w, counts) / (m["ms_per_step"] * 1e-3) / 1e9, 1),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stage_ms_median": {k: round(float(percentiles(v)["median"]), 5)
