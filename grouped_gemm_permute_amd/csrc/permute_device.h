@@ -78,8 +78,13 @@ __device__ inline void scatter_chunk(int key, int64_t c0, int64_t end, int64_t S
     if (rank == 0 && key < E) wcnt[wave * E + key] = __popcll(peers);
     __syncthreads();
     if (key < E) {
+        // the counts of the wavefronts below: all loads issued at once
         int32_t pos = run[key] + rank;
-        for (int w = 0; w < wave; ++w) pos += wcnt[w * E + key];
+#pragma unroll
+        for (int w = 0; w < NW - 1; ++w) {
+            const int32_t c = wcnt[w * E + key];
+            pos += w < wave ? c : 0;
+        }
         if (pos >= 0 && pos < S) {     // always true for a consistent histogram
             perm[pos] = (int32_t)s;
             inv[s] = pos;
