@@ -60,7 +60,9 @@ def source_hash(stage: str, variant: str = "unfused", small: bool = False) -> st
     src = SMALL_SOURCES.get(stage, KERNEL_SOURCES[stage]) if small else KERNEL_SOURCES[stage]
     if variant == "fused" and stage == "up_swiglu":
         src = "grouped_gemm_permute_amd/csrc/fused_bf16.hip"
-    for rel in (src, "grouped_gemm_permute_amd/csrc/mfma_common.h",
+    extra = {"grouped_gemm_permute_amd/csrc/gemm_bf16_slab.hip":     # its sort workgroup
+             ("grouped_gemm_permute_amd/csrc/permute_device.h",)}
+    for rel in (src, *extra.get(src, ()), "grouped_gemm_permute_amd/csrc/mfma_common.h",
                 "grouped_gemm_permute_amd/csrc/moe_internal.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
