@@ -21,6 +21,7 @@ namespace moe {
 namespace {
 
 constexpr int NT = 256;
+constexpr int KPRE = 4;   // top-k up to this many: all loads issued up front
 
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -45,6 +46,14 @@ __global__ __launch_bounds__(NT) void combine_bf16_kernel(const uint16_t* __rest
     const int c = (int)(gid - t * cg) * 8;
     const int64_t S = T * k;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto add4 = [&](const uint4 v, float wt) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(wt, bf16_lo(w[i]), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(wt, bf16_hi(w[i]), acc[2 * i + 1]);
+        }
+    };
     auto add = [&](const uint16_t* src, float wt) {
         const uint4 v = *(const uint4*)src;
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -54,11 +63,34 @@ __global__ __launch_bounds__(NT) void combine_bf16_kernel(const uint16_t* __rest
             acc[2 * i + 1] = fmaf(wt, bf16_hi(w[i]), acc[2 * i + 1]);
         }
     };
-    if (has_shared) add(Y + (S + t) * D + c, 1.f);
-    for (int j = 0; j < k; ++j) {
-        const int32_t p = inv[t * k + j];
-        if (p < 0 || p >= S) continue;      // invalid slot (p == -1)
-        add(Y + (int64_t)p * D + c, topk_w ? topk_w[t * k + j] : 1.f);
+    if (k <= KPRE) {
+        // every slot's row index and weight first, then every row, all in
+        // flight at once; the sum runs in the same order as below
+        int32_t p[KPRE];
+        float wt[KPRE];
+#pragma unroll
+        for (int j = 0; j < KPRE; ++j) {
+            p[j] = j < k ? inv[t * k + j] : -1;
+            wt[j] = j < k && topk_w ? topk_w[t * k + j] : 1.f;
+        }
+        uint4 v[KPRE];
+        const uint4 vs = has_shared ? *(const uint4*)(Y + (S + t) * D + c) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < KPRE; ++j) {
+            const bool ok = p[j] >= 0 && p[j] < S;      // invalid slot (p == -1) adds nothing
+            v[j] = ok ? *(const uint4*)(Y + (int64_t)p[j] * D + c) : make_uint4(0, 0, 0, 0);
+        }
+        if (has_shared) add4(vs, 1.f);
+#pragma unroll
+        for (int j = 0; j < KPRE; ++j)
+            if (p[j] >= 0 && p[j] < S) add4(v[j], wt[j]);
+    } else {
+        if (has_shared) add(Y + (S + t) * D + c, 1.f);
+        for (int j = 0; j < k; ++j) {
+            const int32_t p = inv[t * k + j];
+            if (p < 0 || p >= S) continue;      // invalid slot (p == -1)
+            add(Y + (int64_t)p * D + c, topk_w ? topk_w[t * k + j] : 1.f);
+        }
     }
     *(uint4*)(y + t * D + c) = make_uint4(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
                                           pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7]));
