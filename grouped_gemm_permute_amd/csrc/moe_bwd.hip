@@ -140,16 +140,13 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
         uint16_t* w2t = (uint16_t*)(ws + L.w2t);
         uint16_t* w13t = (uint16_t*)(ws + L.w13t);
         const int64_t df = (int64_t)D * F;
-        if (e == hipSuccess) e = launch_transpose_bf16(W2, E, F, D, w2t, df, F, 0, stream);
-        if (e == hipSuccess) e = launch_transpose_bf16(W1, E, D, F, w13t, 2 * df, D, 0, stream);
-        if (e == hipSuccess) e = launch_transpose_bf16(W3, E, D, F, w13t, 2 * df, D, F, stream);
-        if (has_shared) {
-            if (e == hipSuccess) e = launch_transpose_bf16(Ws2, 1, F, D, w2t + E * df, df, F, 0, stream);
-            if (e == hipSuccess)
-                e = launch_transpose_bf16(Ws1, 1, D, F, w13t + 2 * E * df, 2 * df, D, 0, stream);
-            if (e == hipSuccess)
-                e = launch_transpose_bf16(Ws3, 1, D, F, w13t + 2 * E * df, 2 * df, D, F, stream);
-        }
+        // the shared expert's matrix, when there is one, as batch E of the same launch
+        if (e == hipSuccess)
+            e = launch_transpose_bf16(W2, E, F, D, w2t, df, F, 0, stream, has_shared ? Ws2 : nullptr);
+        if (e == hipSuccess)
+            e = launch_transpose_bf16(W1, E, D, F, w13t, 2 * df, D, 0, stream, has_shared ? Ws1 : nullptr);
+        if (e == hipSuccess)
+            e = launch_transpose_bf16(W3, E, D, F, w13t, 2 * df, D, F, stream, has_shared ? Ws3 : nullptr);
         if (e == hipSuccess) e = launch_zero_fill(ws + L.zeros, 256, stream);
         if (e == hipSuccess) e = mark(2);
         if (e == hipSuccess) e = launch_bwd_gate_up_bf16(a.g, x, W1, W3, Ws1, Ws3, gu, D, F, stream);

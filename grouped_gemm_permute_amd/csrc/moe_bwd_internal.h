@@ -88,8 +88,10 @@ hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t s);
 
 // dst[b][dst_row0 + c][r] = src[b][r][c] for b < batches, r < rows, c < cols
 // (bf16, rows and cols multiples of 64); dst rows hold dst_ld elements and
-// dst batches are dst_batch_stride elements apart.
+// dst batches are dst_batch_stride elements apart.  With src_extra, batch
+// `batches` (one more) is read from that matrix instead.
 hipError_t launch_transpose_bf16(const void* src, int64_t batches, int rows, int cols, void* dst,
-                                 int64_t dst_batch_stride, int dst_ld, int dst_row0, hipStream_t s);
+                                 int64_t dst_batch_stride, int dst_ld, int dst_row0, hipStream_t s,
+                                 const void* src_extra = nullptr);
 
 }  // namespace moe
