@@ -54,15 +54,7 @@ __global__ __launch_bounds__(NT) void combine_bf16_kernel(const uint16_t* __rest
             acc[2 * i + 1] = fmaf(wt, bf16_hi(w[i]), acc[2 * i + 1]);
         }
     };
-    auto add = [&](const uint16_t* src, float wt) {
-        const uint4 v = *(const uint4*)src;
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = fmaf(wt, bf16_lo(w[i]), acc[2 * i]);
-            acc[2 * i + 1] = fmaf(wt, bf16_hi(w[i]), acc[2 * i + 1]);
-        }
-    };
+    auto add = [&](const uint16_t* src, float wt) { add4(*(const uint4*)src, wt); };
     if (k <= KPRE) {
         // every slot's row index and weight first, then every row, all in
         // flight at once; the sum runs in the same order as below
