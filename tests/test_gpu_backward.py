@@ -59,6 +59,7 @@ CASES = [
     (9000, 64, 128, 4, 2, True, "bf16", "zipf"),        # groups over one 4096-row gradient chunk
     (3000, 64, 128, 70, 2, True, "bf16", "uniform"),    # 71 groups: lookups over two 64-group blocks
     (2000, 64, 128, 1024, 8, False, "bf16", "uniform"), # the expert limit
+    (600, 64, 128, 8, 6, True, "bf16", "zipf"),         # top-k above 4 with a shared expert
     (400, 1024, 1600, 2, 1, True, "bf16", "uniform"),   # wide D and F (F = 25 * 64)
 ]
 

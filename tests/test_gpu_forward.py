@@ -56,6 +56,11 @@ FULL_CASES = [
     # more than 64 groups: the tile -> group lookup spans several 64-group blocks
     (3000, 128, 192, 100, 4, True, "bf16", "zipf"),      # small-chunk kernels, many empty experts
     (20000, 64, 128, 70, 2, True, "bf16", "uniform"),    # 256-row engine
+    # top-k above 4: the combine's plain per-slot loop (up to 4 slots it
+    # loads every slot's row up front)
+    (400, 128, 256, 12, 6, True, "bf16", "uniform"),     # small-chunk kernels + shared
+    (1500, 64, 128, 8, 8, False, "bf16", "uniform"),     # k = E: every token to every expert
+    (64, 64, 128, 6, 5, True, "f32", "uniform"),
     # over twelve rounds of up tiles: whole 256-row tiles, two column groups
     # (12 x 448 x 256 weights per XCD outgrow its L2 share), D tail of 192
     (24000, 448, 1536, 8, 2, True, "bf16", "zipf"),
