@@ -40,14 +40,14 @@
 //    columns of the same 128 outputs), in one of two workgroup shapes
 //    (waves_of below), each chosen by interleaved A/Bs with bitwise-equal
 //    results:
-//      - whole tiles, 8 wavefronts (up on long grids, gate_up, down): two
+//      - whole tiles, 8 wavefronts (up and gate_up on long grids, down): two
 //        wavefronts per SIMD, wavefront w owning features 64 (w % 4) .. +63
 //        of rows 128 (w / 4) .. +127 (2 x 4 v_mfma_f32_32x32x16_bf16
 //        accumulators), one workgroup per CU and a ring of four 32 KiB
 //        stages; one wavefront's MFMAs run while its partner is held issuing
 //        a load into a busy memory pipe;
-//      - half tiles, 4 wavefronts (up when its whole-tile grid is under
-//        twelve rounds of the CUs, and dh always): a workgroup takes one
+//      - half tiles, 4 wavefronts (up and gate_up when the whole-tile grid
+//        is under twelve rounds of the CUs, dh always): a workgroup takes one
 //        128-token half of a row tile, wavefront w owning features
 //        64 w .. +63 of its 128 rows (2 x 4 accumulators, a ring of three
 //        24 KiB stages, 72 KiB; dh adds 8 KiB for its epilogue), so two
@@ -103,13 +103,14 @@ enum : int {
 //  * whole tiles (HALF = false): 8 wavefronts, two per SIMD, on a 256-row
 //    tile, one workgroup per CU (a 4-stage ring of 32 KiB), so one
 //    wavefront's MFMAs cover the other's stalls issuing loads;
-//  * half tiles (HALF = true, up and dh): 4 wavefronts on one 128-row half
+//  * half tiles (HALF = true; up, gate/up and dh): 4 wavefronts on one 128-row half
 //    of a tile (a 3-stage ring of 24 KiB), two workgroups per CU, so the
 //    epilogue and the prologue of one overlap the other's MFMAs and the
 //    last round is finer.  It stages 1.5x the bytes per MFMA: the up GEMM
 //    takes it when its whole-tile grid is short (up_half_tiles), where it
-//    measured 3-9% faster; on long grids it is even to 1% slower, and for
-//    gate/up and down 4-10% slower.  dh, whose epilogue moves 640 KiB per
+//    measured 3-9% faster; on long grids it is even to 1% slower.  gate/up
+//    follows the same rule (4% faster at 4096 tokens, 4% slower at 32768);
+//    the down GEMM is slower on it at every size.  dh, whose epilogue moves 640 KiB per
 //    256-row tile, always takes it: 522 -> 487 us at 32768 tokens and
 //    110 -> 83 us at 4096 (D = 768, F = 1536, E = 8; before, 4 wavefronts
 //    on a whole tile, one workgroup per CU).
@@ -144,7 +145,7 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
     const GemmArgs a) {
     constexpr bool UP = MODE != M_DOWN;         // A gathered by token, K = D, N = F
     constexpr bool PAIR = MODE == M_UP || MODE == M_GU;   // g / u column pairs from W1, W3
-    static_assert(!HALF || MODE == M_UP || MODE == M_DH, "half tiles are built for the up and dh GEMMs");
+    static_assert(!HALF || MODE != M_DOWN, "half tiles are built for the up, gate/up and dh GEMMs");
     constexpr int NW = waves_of<MODE, HALF>();
     constexpr int NT = 64 * NW;
     constexpr int ROWS = HALF ? TT / 2 : TT;   // rows of the workgroup's tile
@@ -743,7 +744,12 @@ hipError_t launch_bwd_gate_up_bf16(const GroupArgs& g, const void* x, const void
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, gu, D, F, (F + TF / 2 - 1) / (TF / 2)};
     a.col_groups = column_groups(a.n_tiles, D);
     const int64_t blocks = (int64_t)m_tiles_upper(g) * a.n_tiles;
-    grouped_gemm_bf16_kernel<M_GU, false><<<grid_for_work(blocks), 64 * waves_of<M_GU, false>(), 0, s>>>(a);
+    // half tiles on short grids, as the forward's up GEMM (gate/up measured
+    // 4% faster on them at 4096 tokens, 4% slower at 32768)
+    if (up_half_tiles(blocks))
+        grouped_gemm_bf16_kernel<M_GU, true><<<grid_for_work(2 * blocks), 64 * waves_of<M_GU, true>(), 0, s>>>(a);
+    else
+        grouped_gemm_bf16_kernel<M_GU, false><<<grid_for_work(blocks), 64 * waves_of<M_GU, false>(), 0, s>>>(a);
     return hipGetLastError();
 }
 
