@@ -699,7 +699,7 @@ def small_chunk_record(args):
     kernel measures on the same GPU."""
     import numpy as np
     m = measure_forward(3, "unfused", steps=max(args.steps, 200), warmup=max(args.warmup, 20),
-                        rotate_bytes=args.rotate_bytes)
+                        rotate_bytes=args.rotate_bytes, sustained_ms=args.sustained_ms)
     w, counts = m["w"], m["counts"]
     nbytes = path_bytes(w, counts)
     pc = percentiles(m["per_call"])
@@ -711,8 +711,25 @@ def small_chunk_record(args):
             "ms_per_call": pc, "ms_per_step_host_clock": round(m["ms_per_step"], 5),
             "bytes_alg": nbytes, "gbs": round(gbs, 1), "frac_of_8tbs": round(gbs / PEAK_HBM_GBS, 4),
             "stream_read_gbs_measured": read_gbs, "frac_of_measured_read": round(gbs / read_gbs, 4),
+            "back_to_back": back_to_back_record(m, nbytes),
             "stage_ms_mean_with_events": {k: round(v, 5) for k, v in stage_ms.items()},
             "dominant": roof}
+
+
+def back_to_back_record(m, nbytes):
+    """Region 3 of measure_forward priced in bytes: the same calls issued
+    back to back with no event between them, after the GPU has been kept
+    busy.  At µs-scale calls each event record between calls costs GPU time
+    of its own, so ms_per_call (one event between consecutive calls) sits
+    above this figure."""
+    s = m.get("sustained")
+    if not s:
+        return None
+    gbs = nbytes / (s["ms_per_step"] * 1e-3) / 1e9
+    return {"ms_per_call": round(s["ms_per_step"], 5), "gbs": round(gbs, 1),
+            "frac_of_8tbs": round(gbs / PEAK_HBM_GBS, 4), "calls_before": s["calls_before"],
+            "note": "host clock over the calls issued back to back (no event between them), "
+                    "after calls_before untimed calls"}
 
 
 def main():

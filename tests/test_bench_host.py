@@ -89,3 +89,12 @@ def test_source_hash_covers_the_kernels_headers():
             h.update(f.read())
     assert bench.source_hash("up_swiglu", "unfused", True) == h.hexdigest()[:16]
     assert bench.source_hash("up_swiglu", "unfused", False) != bench.source_hash("up_swiglu", "unfused", True)
+
+
+def test_back_to_back_record():
+    assert bench.back_to_back_record({"sustained": None}, 58_204_160) is None
+    m = {"sustained": {"ms_per_step": 0.0291, "calls_before": 5000, "clocks": {}}}
+    r = bench.back_to_back_record(m, 58_204_160)
+    assert r["ms_per_call"] == 0.0291 and r["calls_before"] == 5000
+    assert r["gbs"] == pytest.approx(58_204_160 / 29.1e-6 / 1e9, abs=0.05)
+    assert r["frac_of_8tbs"] == pytest.approx(r["gbs"] / 8000.0, abs=1e-4)
