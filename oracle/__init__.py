@@ -65,7 +65,7 @@ def _load():
         lib.moe_oracle_backward_groups.argtypes = [P] * 10 + [i64, i64, i64, ci, ci, P, ci] + [P] * 6 + [ci]
         lib.moe_oracle_forward_permuted.restype = i64
         lib.moe_oracle_forward_permuted.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i64, ci,
-                                                    ci, P, P, P, P, P, P, P, ci]
+                                                    ci, P, P, P, P, P, P, P, P, ci]
         _lib = lib
     return _lib
 
@@ -123,9 +123,12 @@ def forward_dense(x, topk_idx, topk_w, W1, W3, W2, shared=None, tokens=None, nth
     return y
 
 
-def forward_permuted(x, topk_idx, topk_w, W1, W3, W2, shared=None, nthreads=1) -> dict:
+def forward_permuted(x, topk_idx, topk_w, W1, W3, W2, shared=None, nthreads=1,
+                     with_gu=False) -> dict:
     """Path (ii): returns y [T,D], the sorted-row intermediates h [R,F] and
-    Y [R,D] (R = T*k plus T shared rows), and counts/offsets/perm/inv."""
+    Y [R,D] (R = T*k plus T shared rows), and counts/offsets/perm/inv; with
+    with_gu also gu [R, 2F], each row's gate product g = v W1 (columns
+    0..F-1) and up product u = v W3 (columns F..2F-1)."""
     x = _f64(x)
     T, D = x.shape
     E, _, F = W1.shape
@@ -139,18 +142,22 @@ def forward_permuted(x, topk_idx, topk_w, W1, W3, W2, shared=None, nthreads=1) -
     y = np.empty((T, D), np.float64)
     h = np.empty((max(R, 1), F), np.float64)
     Y = np.empty((max(R, 1), D), np.float64)
+    gu = np.empty((max(R, 1), 2 * F), np.float64) if with_gu else None
     counts = np.empty(E, np.int32)
     offsets = np.empty(E + 1, np.int32)
     perm = np.empty(max(S, 1), np.int32)
     inv = np.empty(max(S, 1), np.int32)
     bad = _load().moe_oracle_forward_permuted(
         _ptr(x), _ptr(idx), _ptr(w), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1), _ptr(Ws3),
-        _ptr(Ws2), T, D, F, E, k, _ptr(y), _ptr(h), _ptr(Y), _ptr(counts), _ptr(offsets),
-        _ptr(perm), _ptr(inv), nthreads)
+        _ptr(Ws2), T, D, F, E, k, _ptr(y), _ptr(h), _ptr(Y), _ptr(gu), _ptr(counts),
+        _ptr(offsets), _ptr(perm), _ptr(inv), nthreads)
     if bad < 0:
         raise MemoryError("oracle allocation failed")
-    return dict(y=y, h=h[:R], Y=Y[:R], counts=counts, offsets=offsets, perm=perm[:S],
-                inv=inv[:S], bad=int(bad))
+    out = dict(y=y, h=h[:R], Y=Y[:R], counts=counts, offsets=offsets, perm=perm[:S],
+               inv=inv[:S], bad=int(bad))
+    if with_gu:
+        out["gu"] = gu[:R]
+    return out
 
 
 def backward(x, topk_idx, topk_w, W1, W3, W2, shared, dy, nthreads=1) -> dict:

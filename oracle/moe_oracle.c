@@ -174,6 +174,7 @@ typedef struct {
     const int32_t *perm, *offsets;
     int64_t S;
     double *h_out, *Y_out;     /* sorted-row results [S(+T), F] and [S(+T), D] */
+    double *gu_out;            /* optional [S(+T), 2F]: g in columns 0..F-1, u in F..2F-1 */
     /* backward */
     const int32_t *groups;
     const double *dy;
@@ -285,6 +286,10 @@ static void *sorted_worker(void *arg)
             t = p - J->S;
         }
         swiglu_row(J->x + t * D, A1, A3, A2, D, F, g, u, J->h_out + p * F, J->Y_out + p * D);
+        if (J->gu_out) {
+            double *r = J->gu_out + p * 2 * F;
+            for (int64_t f = 0; f < F; ++f) { r[f] = g[f]; r[F + f] = u[f]; }
+        }
     }
 done:
     free(g); free(u);
@@ -296,7 +301,10 @@ done:
  * per-expert loop over sorted rows (empty experts do nothing), shared rows
  * appended after the S routed rows, then unpermute through inv and combine
  * in j order.  h_out [S + T*sh, F] and Y_out [S + T*sh, D] receive every
- * sorted row's h and W2 output (rows of invalid slots are left as zero).
+ * sorted row's h and W2 output (rows of invalid slots are left as zero);
+ * gu_out [S + T*sh, 2F], when not NULL, receives the row's gate and up
+ * products g = v W1, u = v W3 (columns 0..F-1 and F..2F-1), the values a
+ * backward that caches them instead of recomputing them would keep.
  * perm/inv/counts/offsets are written to the caller's arrays
  * (sizes S, S, E, E+1).  Returns the number of invalid slots, or -1 on
  * allocation failure.
@@ -305,7 +313,7 @@ int64_t moe_oracle_forward_permuted(const double *x, const int32_t *idx, const d
                                     const double *W1, const double *W3, const double *W2,
                                     const double *Ws1, const double *Ws3, const double *Ws2,
                                     int64_t T, int64_t D, int64_t F, int E, int k,
-                                    double *y, double *h_out, double *Y_out,
+                                    double *y, double *h_out, double *Y_out, double *gu_out,
                                     int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
                                     int nthreads)
 {
@@ -319,6 +327,7 @@ int64_t moe_oracle_forward_permuted(const double *x, const int32_t *idx, const d
     free(tile_off);
     memset(h_out, 0, sizeof(double) * (size_t)(rows * F));
     memset(Y_out, 0, sizeof(double) * (size_t)(rows * D));
+    if (gu_out) memset(gu_out, 0, sizeof(double) * (size_t)(rows * 2 * F));
 
     job_t J;
     memset(&J, 0, sizeof J);
@@ -326,6 +335,7 @@ int64_t moe_oracle_forward_permuted(const double *x, const int32_t *idx, const d
     J.Ws1 = Ws1; J.Ws3 = Ws3; J.Ws2 = Ws2;
     J.T = T; J.D = D; J.F = F; J.E = E; J.k = k;
     J.perm = perm; J.offsets = offsets; J.S = S; J.h_out = h_out; J.Y_out = Y_out;
+    J.gu_out = gu_out;
     if (run_jobs(&J, rows, nthreads, sorted_worker)) return -1;
 
     /* Unpermute and combine: y[t] = Ysh[t] + sum_j w[t,j] * Y[inv[t*k+j]]. */

@@ -196,6 +196,41 @@ def test_permuted_intermediates_are_per_row_swiglu():
                                    atol=1e-13)
 
 
+def test_permuted_gate_up_products_per_row():
+    """The sorted-row gate and up products a caching backward keeps
+    ("Triton MoE Kernels & Memory Checkpointing", Part A section 8: g = v W1,
+    u = v W3): against numpy's products of the row's token with its
+    expert's matrices, h = silu(g) u to the last bit, zero rows for invalid
+    slots."""
+    rng = np.random.default_rng(21)
+    T, D, F, E, k = 13, 8, 12, 4, 2
+    x, idx, w, W1, W3, W2, sh = _rand_problem(rng, T, D, F, E, k, shared=True)
+    idx[3, 1] = E + 2                                   # one invalid slot
+    r = oracle.forward_permuted(x, idx, w, W1, W3, W2, sh, with_gu=True)
+    S = T * k
+    gu = r["gu"]
+    assert gu.shape == (S + T, 2 * F)
+    valid = r["offsets"][E]
+    for p in range(S):
+        if p >= valid:
+            assert not gu[p].any()
+            continue
+        s = r["perm"][p]
+        t, e = s // k, idx.reshape(-1)[s]
+        np.testing.assert_allclose(gu[p, :F], x[t] @ W1[e], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(gu[p, F:], x[t] @ W3[e], rtol=1e-12, atol=1e-13)
+    for t in range(T):
+        np.testing.assert_allclose(gu[S + t, :F], x[t] @ sh[0], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(gu[S + t, F:], x[t] @ sh[1], rtol=1e-12, atol=1e-13)
+    g, u = gu[:, :F], gu[:, F:]
+    # (numpy's exp and the C library's may differ in the last bit)
+    np.testing.assert_allclose(r["h"], g / (1 + np.exp(-g)) * u, rtol=1e-15, atol=1e-300)
+    # asking for them changes nothing else
+    plain = oracle.forward_permuted(x, idx, w, W1, W3, W2, sh)
+    for key in ("y", "h", "Y", "perm", "inv"):
+        np.testing.assert_array_equal(plain[key], r[key])
+
+
 def test_invalid_ids_contribute_nothing():
     rng = np.random.default_rng(13)
     x, idx, w, W1, W3, W2, _ = _rand_problem(rng, 10, 8, 8, 3, 2)

@@ -34,6 +34,8 @@ MUTANTS = {
     "tile_round_down": ("(counts[e] + BM - 1) / BM", "(counts[e]) / BM"),
     "offsets_off_by_one": ("offsets[e + 1] = offsets[e] + counts[e];",
                            "offsets[e + 1] = offsets[e] + counts[e] + (e == 0);"),
+    "gu_columns_swapped": ("r[f] = g[f]; r[F + f] = u[f];", "r[f] = u[f]; r[F + f] = g[f];"),
+    "gu_row_stride": ("double *r = J->gu_out + p * 2 * F;", "double *r = J->gu_out + p * F;"),
 }
 
 
@@ -66,6 +68,17 @@ def _pins_pass(golden_dir) -> bool:
                       oracle.forward_permuted(x, tidx, w, W1, W3, W2, s)["y"]):
                 if not np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()):
                     return False
+        # the sorted rows' gate and up products against numpy's
+        r = oracle.forward_permuted(x, tidx, w, W1, W3, W2, sh, with_gu=True)
+        for p in range(T * k + T):
+            if p < T * k:
+                sl = r["perm"][p]
+                v, A1, A3 = x[sl // k], W1[tidx.reshape(-1)[sl]], W3[tidx.reshape(-1)[sl]]
+            else:
+                v, A1, A3 = x[p - T * k], sh[0], sh[1]
+            if not (np.allclose(r["gu"][p, :F], v @ A1, rtol=1e-12, atol=1e-12)
+                    and np.allclose(r["gu"][p, F:], v @ A3, rtol=1e-12, atol=1e-12)):
+                return False
         # closed forms
         cases = json.load(open(os.path.join(golden_dir, "closed_form_cases.json")))["cases"]
         for c in cases:
