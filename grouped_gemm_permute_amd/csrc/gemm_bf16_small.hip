@@ -1,14 +1,15 @@
-// gemm_bf16_small.hip -- grouped GEMMs for small per-expert chunks.
+// gemm_bf16_small.hip -- the down grouped GEMM for small per-expert chunks.
 //
-// Same products as gemm_bf16.hip (up: h = bf16(silu(x . W1) * (x . W3));
-// down: Y = bf16(h . W2)), shaped for the regime where each expert
-// sees only tens to a few hundred rows and the weights dominate the traffic
-// (the "small chunks" that "Triton MoE Kernels & Memory Checkpointing",
-// Part A sections 2 and 6.1, calls the pathological regime).  There the
-// product is bound by streaming each expert's weights once, so the tile is
-// small in both directions to spread the weights over many workgroups:
+// The same product as gemm_bf16.hip's down mode, Y = bf16(h . W2), shaped
+// for the regime where each expert sees only tens to a few hundred rows and
+// the weights dominate the traffic (the "small chunks" that "Triton MoE
+// Kernels & Memory Checkpointing", Part A sections 2 and 6.1, calls the
+// pathological regime).  There the product is bound by streaming each
+// expert's weights once, so the tile is small in both directions to spread
+// the weights over many workgroups (the up product of this regime is
+// gemm_bf16_slab.hip):
 //
-//  * tile 64 rows x 64 MFMA features (up: 32 g + 32 u), K step 64;
+//  * tile 64 rows x 64 output columns, K step 64;
 //  * 256 threads = 4 wavefronts (2 feature x 2 row), one 32 x 32
 //    v_mfma_f32_32x32x16_bf16 block each; two workgroups per CU;
 //  * a 4-deep ring of LDS stages (16 KiB each) filled with global_load_lds
@@ -17,10 +18,7 @@
 //  * tiles run m-major (all column tiles of one row tile back to back), so
 //    an XCD works through one group's whole weight matrix with neighbouring
 //    workgroups reading neighbouring parts of each weight row, and the
-//    group's next row tile finds the weights in that XCD's L2;
-//  * up: a wavefront's 32 MFMA rows are 16 g columns followed by the same 16
-//    u columns, so accumulator element v (g) and v + 8 (u) of a lane belong
-//    to the same (row, column).
+//    group's next row tile finds the weights in that XCD's L2.
 #include "mfma_common.h"
 
 namespace moe {
@@ -29,13 +27,13 @@ namespace {
 using namespace mfma;
 
 constexpr int TT = kSmallTileRows;   // 64 rows per tile
-constexpr int TF = 64;               // MFMA features per tile (up: 32 g + 32 u)
+constexpr int TF = 64;               // output columns per tile
 constexpr int BK = 64;
 constexpr int NT = 256;
 constexpr int NSTAGE = 4;
 constexpr int X_ROW = BK * 2;                  // 128 B
 constexpr int X_BYTES = TT * X_ROW;            // 8 KiB
-constexpr int W_ROW = TF * 2;                  // 128 B (64 features of one k row)
+constexpr int W_ROW = TF * 2;                  // 128 B (64 columns of one k row)
 constexpr int W_BYTES = BK * W_ROW;            // 8 KiB
 constexpr int STAGE_BYTES = X_BYTES + W_BYTES; // 16 KiB
 
@@ -47,25 +45,22 @@ __device__ __forceinline__ int swz_tr128(int k) { return 4 * ((k >> 1) & 1); }
 
 struct SmallArgs {
     GroupArgs g;
-    const uint16_t* a;        // up: x [T, D]; down: h [R, F]
-    const uint16_t* b0;       // up: W1; down: W2
-    const uint16_t* b1;       // up: W3
-    const uint16_t* bs0;      // shared: up Ws1, down Ws2
-    const uint16_t* bs1;      // shared: up Ws3
-    uint16_t* out;            // up: h [R, F]; down: Y [R, D]
+    const uint16_t* a;        // h [R, F]
+    const uint16_t* b0;       // W2 [E, F, D]
+    const uint16_t* bs0;      // shared expert's Ws2 [F, D]
+    uint16_t* out;            // Y [R, D]
     int D, F;
     int n_tiles;
 };
 
-template <bool UP>
-__global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallArgs a) {
+__global__ __launch_bounds__(NT, 2) void grouped_gemm_small_down_kernel(const SmallArgs a) {
     __shared__ __attribute__((aligned(1024))) char st0[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st3[STAGE_BYTES];
 
-    const int K = UP ? a.D : a.F;
-    const int N = UP ? a.F : a.D;
+    const int K = a.F;
+    const int N = a.D;
     // the group lookup's loads go out with the tile count's (one round trip)
     const GroupBlock gblock = load_group_block(a.g, 0, threadIdx.x & 63);
     const int total = a.g.tile_off[a.g.G];
@@ -82,48 +77,27 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallAr
     const int valid_rows = tg.valid_rows;
     if (valid_rows <= 0) return;
 
-    // ---- row tile: DMA instruction j (0, 1) of wavefront w fills rows 16 w + 8 j .. +7.
+    // ---- row tile: DMA instruction j (0, 1) of wavefront w fills rows 16 w +
+    // 8 j .. +7 (rows past the group's end re-read its last row, never stored).
     const char* x_src[2];
-    {
-        int64_t src_row[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            src_row[j] = tile_r0 + min(16 * wave + 8 * j + (lane >> 3), valid_rows - 1);
-        if (UP && !shared) {
-            const int32_t s0 = a.g.perm[src_row[0]], s1 = a.g.perm[src_row[1]];
-            src_row[0] = s0 / a.g.k;
-            src_row[1] = s1 / a.g.k;
-        } else if (UP) {
-            src_row[0] -= a.g.S;
-            src_row[1] -= a.g.S;
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = 16 * wave + 8 * j + (lane >> 3);
-            x_src[j] = (const char*)(a.a + src_row[j] * (int64_t)K + 8 * ((lane & 7) ^ swz8(row)));
-        }
+    for (int j = 0; j < 2; ++j) {
+        const int row = 16 * wave + 8 * j + (lane >> 3);
+        const int64_t src_row = tile_r0 + min(row, valid_rows - 1);
+        x_src[j] = (const char*)(a.a + src_row * (int64_t)K + 8 * ((lane & 7) ^ swz8(row)));
     }
-    // ---- weight tile [64 k][64 features]: DMA instruction j (0, 1) of
+    // ---- weight tile [64 k][64 columns]: DMA instruction j (0, 1) of
     // wavefront w fills k rows 16 w + 8 j .. +7; lane -> k row 16 w + 8 j +
-    // lane/8, physical chunk lane%8 holding logical chunk lc = phys ^ swz(k).
-    // Up: logical chunk lc -> wavefront wb = lc / 4, g when (lc / 2) is even,
-    // h column 16 wb + 8 (lc % 2) of the tile.
+    // lane/8, physical chunk lane%8 holding logical chunk lc = phys ^ swz(k),
+    // output columns 8 lc .. 8 lc + 7 of the tile.
     const int64_t gstride = (int64_t)a.D * a.F;
     const char* w_src[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int kr = 16 * wave + 8 * j + (lane >> 3);
         const int lc = (lane & 7) ^ swz_tr128(kr);
-        int col;
-        const uint16_t* base;
-        if (UP) {
-            const int kind = (lc >> 1) & 1;
-            col = nt * (TF / 2) + 16 * (lc >> 2) + 8 * (lc & 1);
-            base = shared ? (kind ? a.bs1 : a.bs0) : (kind ? a.b1 : a.b0) + grp * gstride;
-        } else {
-            col = nt * TF + 8 * lc;
-            base = shared ? a.bs0 : a.b0 + grp * gstride;
-        }
+        int col = nt * TF + 8 * lc;
+        const uint16_t* base = shared ? a.bs0 : a.b0 + grp * gstride;
         if (col >= N) col = 0;                 // past the last column: a valid chunk, never stored
         w_src[j] = (const char*)(base + (int64_t)kr * N + col);
     }
@@ -227,26 +201,13 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_small_kernel(const SmallAr
     const int t = xrow;
     if (t >= valid_rows) return;
     uint16_t* out = a.out + (tile_r0 + t) * (int64_t)N;
-    if (UP) {
-        // g: v = 0..7 (features 0..15 of the block), u: v + 8 (features 16..31)
 #pragma unroll
-        for (int vg = 0; vg < 2; ++vg) {
-            const int col = nt * (TF / 2) + 16 * wf + 8 * vg + 4 * (lane >> 5);
-            if (col >= N) continue;
-            const int v = 4 * vg;
-            *(uint2*)(out + col) =
-                make_uint2(pack_bf16(silu_mul(acc[v], acc[v + 8]), silu_mul(acc[v + 1], acc[v + 9])),
-                           pack_bf16(silu_mul(acc[v + 2], acc[v + 10]), silu_mul(acc[v + 3], acc[v + 11])));
-        }
-    } else {
-#pragma unroll
-        for (int vg = 0; vg < 4; ++vg) {
-            const int col = nt * TF + 32 * wf + 8 * vg + 4 * (lane >> 5);
-            if (col >= N) continue;
-            const int v = 4 * vg;
-            *(uint2*)(out + col) = make_uint2(pack_bf16(acc[v], acc[v + 1]),
-                                              pack_bf16(acc[v + 2], acc[v + 3]));
-        }
+    for (int vg = 0; vg < 4; ++vg) {
+        const int col = nt * TF + 32 * wf + 8 * vg + 4 * (lane >> 5);
+        if (col >= N) continue;
+        const int v = 4 * vg;
+        *(uint2*)(out + col) = make_uint2(pack_bf16(acc[v], acc[v + 1]),
+                                          pack_bf16(acc[v + 2], acc[v + 3]));
     }
 }
 
@@ -257,23 +218,12 @@ int m_tiles_upper_small(const GroupArgs& g) {
 
 }  // namespace
 
-hipError_t launch_up_swiglu_bf16_small(const GroupArgs& g, const void* x, const void* W1,
-                                       const void* W3, const void* Ws1, const void* Ws3, void* h,
-                                       int D, int F, hipStream_t s) {
-    SmallArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
-                (const uint16_t*)Ws1, (const uint16_t*)Ws3, (uint16_t*)h, D, F,
-                (F + TF / 2 - 1) / (TF / 2)};
-    const int64_t blocks = (int64_t)m_tiles_upper_small(g) * a.n_tiles;
-    grouped_gemm_small_kernel<true><<<grid_for_work(blocks), NT, 0, s>>>(a);
-    return hipGetLastError();
-}
-
 hipError_t launch_down_bf16_small(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
                                   void* Y, int D, int F, hipStream_t s) {
-    SmallArgs a{g, (const uint16_t*)h, (const uint16_t*)W2, nullptr, (const uint16_t*)Ws2, nullptr,
-                (uint16_t*)Y, D, F, (D + TF - 1) / TF};
+    SmallArgs a{g, (const uint16_t*)h, (const uint16_t*)W2, (const uint16_t*)Ws2, (uint16_t*)Y, D, F,
+                (D + TF - 1) / TF};
     const int64_t blocks = (int64_t)m_tiles_upper_small(g) * a.n_tiles;
-    grouped_gemm_small_kernel<false><<<grid_for_work(blocks), NT, 0, s>>>(a);
+    grouped_gemm_small_down_kernel<<<grid_for_work(blocks), NT, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -81,9 +81,6 @@ hipError_t launch_up_swiglu_bf16_slab_routed(const GroupArgs& g, int rb, const i
                                              const void* W3, const void* Ws1, const void* Ws3,
                                              const void* W2, const void* Ws2,
                                              void* h, int D, int F, hipStream_t s);
-hipError_t launch_up_swiglu_bf16_small(const GroupArgs& g, const void* x, const void* W1,
-                                       const void* W3, const void* Ws1, const void* Ws3, void* h,
-                                       int D, int F, hipStream_t s);
 hipError_t launch_down_bf16_small(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
                                   void* Y, int D, int F, hipStream_t s);
 
