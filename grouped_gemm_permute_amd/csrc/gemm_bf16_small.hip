@@ -10,7 +10,7 @@
 // gemm_bf16_slab.hip):
 //
 //  * tile 64 rows x 64 output columns, K step 64;
-//  * 256 threads = 4 wavefronts (2 feature x 2 row), one 32 x 32
+//  * 256 threads = 4 wavefronts (2 column x 2 row blocks), one 32 x 32
 //    v_mfma_f32_32x32x16_bf16 block each; two workgroups per CU;
 //  * a 4-deep ring of LDS stages (16 KiB each) filled with global_load_lds
 //    (two stages in flight while one computes), and the next stage's
@@ -30,7 +30,6 @@ constexpr int TT = kSmallTileRows;   // 64 rows per tile
 constexpr int TF = 64;               // output columns per tile
 constexpr int BK = 64;
 constexpr int NT = 256;
-constexpr int NSTAGE = 4;
 constexpr int X_ROW = BK * 2;                  // 128 B
 constexpr int X_BYTES = TT * X_ROW;            // 8 KiB
 constexpr int W_ROW = TF * 2;                  // 128 B (64 columns of one k row)

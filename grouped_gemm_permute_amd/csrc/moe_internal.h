@@ -54,7 +54,7 @@ hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, c
 // Small-chunk grouped GEMMs (bf16), for groups too small to fill the GPU
 // with 256-row tiles.  The up GEMM runs on row tiles of 32 * rb rows that hold
 // a whole typical group (rb from slab_row_blocks), each weight slab streamed
-// once; the down GEMM on 64-row x 64-feature tiles with a 4-deep load ring.
+// once; the down GEMM on 64-row x 64-column tiles with a 4-deep load ring.
 constexpr int kSmallTileRows = 64;
 constexpr int kSlabMaxRowBlocks = 8;
 // Workgroups of one round of the slab kernel (one per compute unit).
