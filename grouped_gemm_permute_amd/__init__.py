@@ -8,5 +8,5 @@ torch supplies device memory and streams, nothing else.
 """
 from ._lib import (MoeError, alloc_workspace, backward, backward_workspace_layout,  # noqa: F401
                    device_clock_sample, device_error, engine_clock_ghz, expert_permute, forward,
-                   forward_noalloc, forward_routed, lib, router_topk, status_string, stream_read, tile_rows,
+                   forward_noalloc, forward_routed, forward_save_gu, lib, router_topk, status_string, stream_read, tile_rows,
                    workspace_layout, workspace_size, EXPORTS, LIB_PATH, NOALLOC_SCRATCH_BYTES)

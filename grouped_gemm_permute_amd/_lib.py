@@ -27,7 +27,8 @@ EXPORTS = (
     "moe_ffn_get_device_error", "moe_ffn_backward_workspace_layout", "moe_ffn_backward_workspace_size",
     "moe_ffn_backward", "moe_ffn_backward_timed", "moe_router_topk", "moe_ffn_forward_routed",
     "moe_ffn_forward_routed_timed", "moe_device_clock_sample", "moe_ffn_forward_noalloc",
-    "moe_stream_read",
+    "moe_stream_read", "moe_ffn_forward_save_gu", "moe_ffn_backward_cached",
+    "moe_ffn_backward_cached_timed",
 )
 
 # Bytes of the per-device workspace array behind moe_ffn_forward_noalloc.
@@ -82,6 +83,8 @@ def lib():
         L.moe_ffn_workspace_size.argtypes = [i64, ci, ci, ci, ci, ci, ci, ci]
         L.moe_ffn_forward.restype = ci
         L.moe_ffn_forward.argtypes = [P, P, P, P, P, P, P, P, P, P, i64, ci, ci, ci, ci, ci, ci, P, sz, P]
+        L.moe_ffn_forward_save_gu.restype = ci
+        L.moe_ffn_forward_save_gu.argtypes = [P] * 11 + [i64, ci, ci, ci, ci, ci, ci, P, sz, P]
         L.moe_ffn_forward_timed.restype = ci
         L.moe_ffn_forward_timed.argtypes = [P, P, P, P, P, P, P, P, P, P, i64, ci, ci, ci, ci, ci, ci,
                                             P, sz, P, P]
@@ -99,6 +102,11 @@ def lib():
         L.moe_ffn_backward.argtypes = bwd_args
         L.moe_ffn_backward_timed.restype = ci
         L.moe_ffn_backward_timed.argtypes = bwd_args + [P]
+        cached_args = [P] * 19 + [i64, ci, ci, ci, ci, ci, P, sz, P]
+        L.moe_ffn_backward_cached.restype = ci
+        L.moe_ffn_backward_cached.argtypes = cached_args
+        L.moe_ffn_backward_cached_timed.restype = ci
+        L.moe_ffn_backward_cached_timed.argtypes = cached_args + [P]
         L.moe_router_topk.restype = ci
         L.moe_router_topk.argtypes = [P, P, i64, ci, ci, ci, ci, P, P, P]
         routed = [P] * 11 + [i64, ci, ci, ci, ci, ci, ci, P, sz, P]
@@ -262,6 +270,34 @@ def forward(x, topk_idx, topk_w, W1, W3, W2, shared=None, y=None, variant="unfus
     return y
 
 
+def forward_save_gu(x, topk_idx, topk_w, W1, W3, W2, shared=None, y=None, gu=None, workspace=None,
+                    stream=None):
+    """(y, gu) = moe_ffn_forward_save_gu(...): the unfused bf16 forward that
+    also returns each sorted row's gate and up products, gu [R, 2F] bf16
+    (R = T*k + T with a shared expert), for backward(..., gu=gu)."""
+    T, D, F, E = _check_layer(x, W1, W3, W2, shared, y)
+    k = _check_routing(x, topk_idx, topk_w, T)
+    R = T * k + (T if shared is not None else 0)
+    if gu is None:
+        gu = torch.empty((R, 2 * F), dtype=x.dtype, device=x.device)
+    _expect("gu", gu, (R, 2 * F), x.dtype)
+    _same_device(x, dict(topk_idx=topk_idx, topk_w=topk_w, gu=gu,
+                         **_layer_tensors(W1, W3, W2, shared, y)))
+    Ws1, Ws3, Ws2 = shared if shared is not None else (None, None, None)
+    if y is None:
+        y = torch.empty((T, D), dtype=x.dtype, device=x.device)
+    n = workspace_size(T, D, F, E, k, shared is not None, x.dtype, "unfused")
+    if workspace is None:
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    _check_workspace(x, workspace, n)
+    _check(lib().moe_ffn_forward_save_gu(_ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W1), _ptr(W3),
+                                         _ptr(W2), _ptr(Ws1), _ptr(Ws3), _ptr(Ws2), _ptr(y), _ptr(gu),
+                                         T, D, F, E, k, _dtype_enum(x.dtype), MOE_VARIANT_UNFUSED,
+                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_ffn_forward_save_gu")
+    return y, gu
+
+
 def forward_noalloc(x, topk_idx, topk_w, W1, W3, W2, shared=None, y=None, variant="unfused",
                     stream=None):
     """y = moe_ffn_forward_noalloc(...): the forward on the library's own
@@ -352,15 +388,21 @@ def backward_workspace_layout(T, D, F, E, k, has_shared, dtype) -> dict:
 
 
 def backward(x, topk_idx, topk_w, W1, W3, W2, shared, dy, out=None, workspace=None, stream=None,
-             events=None) -> dict:
+             events=None, gu=None) -> dict:
     """moe_ffn_backward(...): gradients of the layer for the incoming dy [T,D].
     Returns dx [T,D] (x's dtype), dW1/dW3 [E,D,F], dW2 [E,F,D], dWs1/dWs3
     [D,F], dWs2 [F,D] (None without a shared expert) and dtopk_w [T,k], all
     fp32 except dx.  ``out`` may supply any of these tensors.  ``events``: a
-    ctypes array of nine hipEvent_t handles (moe_ffn_backward_timed)."""
+    ctypes array of nine hipEvent_t handles (moe_ffn_backward_timed).
+    ``gu``: the gate and up products forward_save_gu returned for the same
+    inputs; the call then goes to moe_ffn_backward_cached(_timed), which
+    skips their recompute."""
     T, D, F, E = _check_layer(x, W1, W3, W2, shared, None)
     k = _check_routing(x, topk_idx, topk_w, T)
     _expect("dy", dy, (T, D), x.dtype)
+    if gu is not None:
+        _expect("gu", gu, (T * k + (T if shared is not None else 0), 2 * F), x.dtype)
+        _same_device(x, dict(gu=gu))
     dev = x.device
     f32 = dict(dtype=torch.float32, device=dev)
     o = dict(out or {})
@@ -394,7 +436,13 @@ def backward(x, topk_idx, topk_w, W1, W3, W2, shared, dy, out=None, workspace=No
             _ptr(Ws3), _ptr(Ws2), _ptr(dy), _ptr(o["dx"]), _ptr(o["dW1"]), _ptr(o["dW3"]),
             _ptr(o["dW2"]), _ptr(o["dWs1"]), _ptr(o["dWs3"]), _ptr(o["dWs2"]), _ptr(o["dtopk_w"]),
             T, D, F, E, k, _dtype_enum(x.dtype), _ptr(workspace), workspace.numel(), _stream(stream))
-    if events is None:
+    if gu is not None:
+        cargs = args[:9] + (_ptr(gu),) + args[9:]
+        if events is None:
+            _check(lib().moe_ffn_backward_cached(*cargs), "moe_ffn_backward_cached")
+        else:
+            _check(lib().moe_ffn_backward_cached_timed(*cargs, events), "moe_ffn_backward_cached_timed")
+    elif events is None:
         _check(lib().moe_ffn_backward(*args), "moe_ffn_backward")
     else:
         _check(lib().moe_ffn_backward_timed(*args, events), "moe_ffn_backward_timed")

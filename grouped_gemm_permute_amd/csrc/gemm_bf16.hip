@@ -73,6 +73,8 @@
 // to their group's last row on load and never stored.
 #include "mfma_common.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -97,6 +99,7 @@ enum : int {
     M_DOWN = 1,    // rows . W2 -> Y (also the backward's dx rows)
     M_GU = 2,      // x gathered . [W1 | W3] -> [g | u]
     M_DH = 3,      // dy gathered . W2t -> dgu, hw, dwpart
+    M_UPGU = 4,    // x gathered . [W1 | W3] -> [g | u] and h = silu(g) u
 };
 
 // Workgroup shapes, each chosen by measurement (interleaved A/Bs):
@@ -135,6 +138,8 @@ struct GemmArgs {
     const uint16_t* gu;       // [R, 2F] recomputed g and u
     uint16_t* hw;             // [R, F] w * h
     float* dwpart;            // [R, F / 64] partial sums of dh' * h
+    // up with the gate and up products kept (M_UPGU) only
+    void* gu_out;             // [R, 2F] g and u, as the gate/up mode stores them
 };
 
 // Target of the dh epilogue's stores for rows and columns outside the tile.
@@ -144,7 +149,7 @@ template <int MODE, bool HALF>
 __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void grouped_gemm_bf16_kernel(
     const GemmArgs a) {
     constexpr bool UP = MODE != M_DOWN;         // A gathered by token, K = D, N = F
-    constexpr bool PAIR = MODE == M_UP || MODE == M_GU;   // g / u column pairs from W1, W3
+    constexpr bool PAIR = MODE == M_UP || MODE == M_GU || MODE == M_UPGU;   // g / u column pairs from W1, W3
     static_assert(!HALF || MODE != M_DOWN, "half tiles are built for the up, gate/up and dh GEMMs");
     constexpr int NW = waves_of<MODE, HALF>();
     constexpr int NT = 64 * NW;
@@ -619,6 +624,73 @@ __global__ __launch_bounds__((64 * waves_of<MODE, HALF>()), (HALF ? 2 : 1)) void
         }
         return;
     }
+    if constexpr (MODE == M_UPGU) {
+        // Two passes through the stage buffers: [g | u] as the gate/up mode
+        // stages and stores it (staged columns 0..127 g, 128..255 u, to
+        // gu_out [R, 2F]), then h as the up mode does (to out [R, F]).
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        __syncthreads();
+        auto pass = [&](auto GUc) {
+            constexpr bool GU = decltype(GUc)::value;
+            constexpr int OCOLS = GU ? TF : TF / 2;
+            constexpr int OROW = OCOLS * 2;
+            constexpr int OCH = OROW / 16;
+            constexpr int RPS = SBYTES / OROW;
+            static_assert(RPS % 16 == 0 && NS * RPS >= ROWS, "the stage buffers hold the staged tile");
+            auto orow = [&](int r) -> char* {
+                const int q = r / RPS;
+                char* b = q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3;
+                return b + (r - q * RPS) * OROW;
+            };
+#pragma unroll
+            for (int nj = 0; nj < NJ; ++nj) {
+                const int t = 32 * NJ * rw + 32 * nj + (lane & 31);
+                char* rowp = orow(t);
+                const int sw = t & 15;
+                if constexpr (GU) {
+#pragma unroll
+                    for (int mi = 0; mi < 2; ++mi) {
+                        const f32x16_t& c = acc[mi][nj];
+#pragma unroll
+                        for (int vg = 0; vg < 4; ++vg) {
+                            const int v = 4 * vg;
+                            const int ch = 16 * mi + 4 * fw + vg;
+                            *(uint2*)(rowp + ((ch ^ sw) << 4) + 8 * (lane >> 5)) =
+                                make_uint2(pack_bf16(c[v], c[v + 1]), pack_bf16(c[v + 2], c[v + 3]));
+                        }
+                    }
+                } else {
+                    const f32x16_t& g = acc[0][nj];
+                    const f32x16_t& u = acc[1][nj];
+#pragma unroll
+                    for (int vg = 0; vg < 4; ++vg) {
+                        const int v = 4 * vg;
+                        const int c = 4 * fw + vg;
+                        *(uint2*)(rowp + ((c ^ sw) << 4) + 8 * (lane >> 5)) =
+                            make_uint2(pack_bf16(silu_mul(g[v], u[v]), silu_mul(g[v + 1], u[v + 1])),
+                                       pack_bf16(silu_mul(g[v + 2], u[v + 2]), silu_mul(g[v + 3], u[v + 3])));
+                    }
+                }
+            }
+            __syncthreads();
+            constexpr int ROWS_PER_PASS = NT / OCH;
+            const int c = tid % OCH;
+            const int col = GU ? (c < 16 ? nt * 128 + 8 * c : N + nt * 128 + 8 * (c - 16)) : nt * OCOLS + 8 * c;
+            const int ldo = GU ? 2 * N : N;
+            const bool col_ok = GU ? nt * 128 + 8 * (c & 15) < N : col < N;
+            uint16_t* out = (uint16_t*)(GU ? a.gu_out : a.out);
+#pragma unroll 4
+            for (int r = tid / OCH; r < ROWS; r += ROWS_PER_PASS) {
+                if (r >= valid_rows) break;
+                const u32x4_t v = *(const u32x4_t*)(orow(r) + ((c ^ (r & 15)) << 4));
+                if (col_ok) *(u32x4_t*)(out + (tile_r0 + r) * (int64_t)ldo + col) = v;
+            }
+        };
+        pass(std::true_type{});
+        __syncthreads();          // every wavefront has read the [g | u] pass out of LDS
+        pass(std::false_type{});
+        return;
+    }
     constexpr int OCOLS = MODE == M_UP ? TF / 2 : TF;   // output columns of the tile
     constexpr int OROW = OCOLS * 2;             // bytes per staged row
     constexpr int OCH = OROW / 16;              // 16-byte chunks per row
@@ -724,6 +796,21 @@ hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* 
         grouped_gemm_bf16_kernel<M_UP, true><<<grid_for_work(2 * tiles), 64 * waves_of<M_UP, true>(), 0, s>>>(a);
     else
         grouped_gemm_bf16_kernel<M_UP, false><<<grid_for_work(tiles), 64 * waves_of<M_UP, false>(), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_up_swiglu_gu_bf16(const GroupArgs& g, const void* x, const void* W1,
+                                    const void* W3, const void* Ws1, const void* Ws3, void* h,
+                                    void* gu, int D, int F, hipStream_t s) {
+    GemmArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
+               (const uint16_t*)Ws1, (const uint16_t*)Ws3, h, D, F, (F + TF / 2 - 1) / (TF / 2)};
+    a.col_groups = column_groups(a.n_tiles, D);
+    a.gu_out = gu;
+    const int64_t tiles = (int64_t)m_tiles_upper(g) * a.n_tiles;
+    if (up_half_tiles(tiles))
+        grouped_gemm_bf16_kernel<M_UPGU, true><<<grid_for_work(2 * tiles), 64 * waves_of<M_UPGU, true>(), 0, s>>>(a);
+    else
+        grouped_gemm_bf16_kernel<M_UPGU, false><<<grid_for_work(tiles), 64 * waves_of<M_UPGU, false>(), 0, s>>>(a);
     return hipGetLastError();
 }
 

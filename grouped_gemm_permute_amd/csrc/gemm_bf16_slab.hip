@@ -89,6 +89,9 @@ struct SlabArgs {
     const uint16_t* ws2;      // [F, D] or null
     int64_t w2_bytes, ws2_bytes;
     int pf_blocks;
+    // optional: each row's gate and up products [R, 2F] (g in columns
+    // 0..F-1, u in F..2F-1), rounded to bf16, for a backward that keeps them
+    uint16_t* gu;
 };
 
 constexpr int kRouteSlotsPerThread = kPermuteSingleMax / 256;
@@ -579,6 +582,12 @@ __global__ __launch_bounds__(NT, 1) void up_swiglu_slab_kernel(const SlabArgs a)
             *(uint2*)(out + col) =
                 make_uint2(pack_bf16(silu_mul(c[v], c[v + 8]), silu_mul(c[v + 1], c[v + 9])),
                            pack_bf16(silu_mul(c[v + 2], c[v + 10]), silu_mul(c[v + 3], c[v + 11])));
+            if (a.gu) {
+                uint16_t* gu = a.gu + (tile_r0 + t) * (int64_t)(2 * N);
+                *(uint2*)(gu + col) = make_uint2(pack_bf16(c[v], c[v + 1]), pack_bf16(c[v + 2], c[v + 3]));
+                *(uint2*)(gu + N + col) =
+                    make_uint2(pack_bf16(c[v + 8], c[v + 9]), pack_bf16(c[v + 10], c[v + 11]));
+            }
         }
     }
 #pragma unroll
@@ -626,10 +635,11 @@ hipError_t launch_slab(const SlabArgs& a, int rb, hipStream_t s);
 
 hipError_t launch_up_swiglu_bf16_slab(const GroupArgs& g, int rb, const void* x, const void* W1,
                                       const void* W3, const void* Ws1, const void* Ws3, void* h,
-                                      int D, int F, hipStream_t s) {
+                                      int D, int F, hipStream_t s, void* gu) {
     SlabArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, (uint16_t*)h, D, F,
                (F + TCOL - 1) / TCOL};
+    a.gu = (uint16_t*)gu;
     return launch_slab(a, rb, s);
 }
 
@@ -639,7 +649,7 @@ hipError_t launch_up_swiglu_bf16_slab_routed(const GroupArgs& g, int rb, const i
                                              int32_t* err, const void* x, const void* W1,
                                              const void* W3, const void* Ws1, const void* Ws3,
                                              const void* W2, const void* Ws2,
-                                             void* h, int D, int F, hipStream_t s) {
+                                             void* h, int D, int F, hipStream_t s, void* gu) {
     if (g.S > kPermuteSingleMax || g.S < 1 || g.E > kRouteMaxExperts) return hipErrorInvalidValue;
     SlabArgs a{g, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
                (const uint16_t*)Ws1, (const uint16_t*)Ws3, (uint16_t*)h, D, F,
@@ -653,6 +663,7 @@ hipError_t launch_up_swiglu_bf16_slab_routed(const GroupArgs& g, int rb, const i
     // prefetch workgroups only on CUs the GEMM and the sort leave idle (256
     // CUs, one workgroup each), so they never delay the GEMM's last round
     a.pf_blocks = std::max(0, std::min(64, 256 - gemm_blocks - 1));
+    a.gu = (uint16_t*)gu;
     return launch_slab(a, rb, s);
 }
 

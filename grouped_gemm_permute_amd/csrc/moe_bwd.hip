@@ -84,13 +84,19 @@ size_t moe_ffn_backward_workspace_size(int64_t T, int D, int F, int E, int k, in
     return make_bwd_layout(T, D, F, E, k, has_shared, dtype, &L) == MOE_OK ? L.total : 0;
 }
 
-moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const float* topk_w,
-                                  const void* W1, const void* W3, const void* W2, const void* Ws1,
-                                  const void* Ws3, const void* Ws2, const void* dy, void* dx,
-                                  float* dW1, float* dW3, float* dW2, float* dWs1, float* dWs3,
-                                  float* dWs2, float* dtopk_w, int64_t T, int D, int F, int E,
-                                  int k, moe_dtype dtype, void* workspace, size_t ws_bytes,
-                                  hipStream_t stream, hipEvent_t* events) {
+}  // extern "C"
+
+namespace {
+
+// The backward; with gu_in (bf16 only) the gate and up products come from
+// the caller (the forward that saved them) instead of the recompute launch.
+moe_status backward_impl(const void* x, const int32_t* topk_idx, const float* topk_w,
+                         const void* W1, const void* W3, const void* W2, const void* Ws1,
+                         const void* Ws3, const void* Ws2, const void* dy, void* dx, float* dW1,
+                         float* dW3, float* dW2, float* dWs1, float* dWs3, float* dWs2,
+                         float* dtopk_w, int64_t T, int D, int F, int E, int k, moe_dtype dtype,
+                         void* workspace, size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
+                         const void* gu_in) {
     const int nsh = (Ws1 != nullptr) + (Ws3 != nullptr) + (Ws2 != nullptr);
     const int ndsh = (dWs1 != nullptr) + (dWs3 != nullptr) + (dWs2 != nullptr);
     if ((nsh != 0 && nsh != 3) || ndsh != nsh) return MOE_ERR_INVALID_ARG;
@@ -107,6 +113,7 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
         !aligned(workspace, kAlign))
         return MOE_ERR_INVALID_ARG;
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (gu_in && !aligned(gu_in, 16)) return MOE_ERR_INVALID_ARG;
 
     char* ws = (char*)workspace;
     int32_t* err = (int32_t*)(ws + L.err);
@@ -117,7 +124,7 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
     int32_t* perm = (int32_t*)(ws + L.perm);
     int32_t* inv = (int32_t*)(ws + L.inv);
     int32_t* hist = (int32_t*)(ws + L.hist);
-    void* gu = ws + L.gu;
+    const void* gu = gu_in ? gu_in : ws + L.gu;
     void* dgu = ws + L.dgu;
     void* hw = ws + L.hw;
     void* dxr = ws + L.dxr;
@@ -149,7 +156,8 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
             e = launch_transpose_bf16(W3, E, D, F, w13t, 2 * df, D, F, stream, has_shared ? Ws3 : nullptr);
         if (e == hipSuccess) e = launch_zero_fill(ws + L.zeros, 256, stream);
         if (e == hipSuccess) e = mark(2);
-        if (e == hipSuccess) e = launch_bwd_gate_up_bf16(a.g, x, W1, W3, Ws1, Ws3, gu, D, F, stream);
+        if (e == hipSuccess && !gu_in)
+            e = launch_bwd_gate_up_bf16(a.g, x, W1, W3, Ws1, Ws3, ws + L.gu, D, F, stream);
         if (e == hipSuccess) e = mark(3);
         if (e == hipSuccess)
             e = launch_bwd_dh_bf16(a.g, topk_w, dy, w2t, has_shared ? w2t + E * df : nullptr, gu, dgu,
@@ -161,7 +169,7 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
         if (e == hipSuccess) e = mark(5);
     } else if (T > 0) {
         if (e == hipSuccess) e = mark(2);
-        if (e == hipSuccess) e = launch_bwd_gate_up(a, x, W1, W3, Ws1, Ws3, gu, stream);
+        if (e == hipSuccess) e = launch_bwd_gate_up(a, x, W1, W3, Ws1, Ws3, ws + L.gu, stream);
         if (e == hipSuccess) e = mark(3);
         if (e == hipSuccess) e = launch_bwd_dh(a, dy, W2, Ws2, gu, dgu, hw, dwpart, stream);
         if (e == hipSuccess) e = mark(4);
@@ -204,6 +212,54 @@ moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const 
     }
     if (e == hipSuccess) e = mark(8);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_ffn_backward_timed(const void* x, const int32_t* topk_idx, const float* topk_w,
+                                  const void* W1, const void* W3, const void* W2, const void* Ws1,
+                                  const void* Ws3, const void* Ws2, const void* dy, void* dx,
+                                  float* dW1, float* dW3, float* dW2, float* dWs1, float* dWs3,
+                                  float* dWs2, float* dtopk_w, int64_t T, int D, int F, int E,
+                                  int k, moe_dtype dtype, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream, hipEvent_t* events) {
+    return backward_impl(x, topk_idx, topk_w, W1, W3, W2, Ws1, Ws3, Ws2, dy, dx, dW1, dW3, dW2, dWs1,
+                         dWs3, dWs2, dtopk_w, T, D, F, E, k, dtype, workspace, ws_bytes, stream,
+                         events, nullptr);
+}
+
+moe_status moe_ffn_backward_cached_timed(const void* x, const int32_t* topk_idx,
+                                         const float* topk_w, const void* W1, const void* W3,
+                                         const void* W2, const void* Ws1, const void* Ws3,
+                                         const void* Ws2, const void* gu, const void* dy, void* dx,
+                                         float* dW1, float* dW3, float* dW2, float* dWs1,
+                                         float* dWs3, float* dWs2, float* dtopk_w, int64_t T, int D,
+                                         int F, int E, int k, moe_dtype dtype, void* workspace,
+                                         size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+    if (dtype != MOE_BF16) {
+        const int nsh = (Ws1 != nullptr) + (Ws3 != nullptr) + (Ws2 != nullptr);
+        moe_bwd_ws_layout L;
+        const moe_status st = make_bwd_layout(T, D, F, E, k, nsh == 3, dtype, &L);
+        return st != MOE_OK ? st : MOE_ERR_UNSUPPORTED;
+    }
+    if (T > 0 && !gu) return MOE_ERR_INVALID_ARG;
+    return backward_impl(x, topk_idx, topk_w, W1, W3, W2, Ws1, Ws3, Ws2, dy, dx, dW1, dW3, dW2, dWs1,
+                         dWs3, dWs2, dtopk_w, T, D, F, E, k, dtype, workspace, ws_bytes, stream,
+                         events, T > 0 ? gu : nullptr);
+}
+
+moe_status moe_ffn_backward_cached(const void* x, const int32_t* topk_idx, const float* topk_w,
+                                   const void* W1, const void* W3, const void* W2, const void* Ws1,
+                                   const void* Ws3, const void* Ws2, const void* gu, const void* dy,
+                                   void* dx, float* dW1, float* dW3, float* dW2, float* dWs1,
+                                   float* dWs3, float* dWs2, float* dtopk_w, int64_t T, int D, int F,
+                                   int E, int k, moe_dtype dtype, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
+    return moe_ffn_backward_cached_timed(x, topk_idx, topk_w, W1, W3, W2, Ws1, Ws3, Ws2, gu, dy, dx,
+                                         dW1, dW3, dW2, dWs1, dWs3, dWs2, dtopk_w, T, D, F, E, k,
+                                         dtype, workspace, ws_bytes, stream, nullptr);
 }
 
 moe_status moe_ffn_backward(const void* x, const int32_t* topk_idx, const float* topk_w,

@@ -143,7 +143,7 @@ moe_status forward_impl(const void* x, const void* gate_w, const int32_t* topk_i
                         const float* topk_w, const void* W1, const void* W3, const void* W2,
                         const void* Ws1, const void* Ws3, const void* Ws2, void* y, int64_t T, int D,
                         int F, int E, int k, moe_dtype dtype, moe_variant variant, void* workspace,
-                        size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+                        size_t ws_bytes, hipStream_t stream, hipEvent_t* events, void* gu = nullptr) {
     const int nsh = (Ws1 != nullptr) + (Ws3 != nullptr) + (Ws2 != nullptr);
     if (nsh != 0 && nsh != 3) return MOE_ERR_INVALID_ARG;
     const bool has_shared = nsh == 3;
@@ -159,6 +159,7 @@ moe_status forward_impl(const void* x, const void* gate_w, const int32_t* topk_i
         return MOE_ERR_INVALID_ARG;
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     if (T == 0) return MOE_OK;
+    if (gu && !aligned(gu, 16)) return MOE_ERR_INVALID_ARG;
 
     char* ws = (char*)workspace;
     int32_t* err = (int32_t*)(ws + L.err);
@@ -217,13 +218,14 @@ moe_status forward_impl(const void* x, const void* gate_w, const int32_t* topk_i
     } else if (sort_in_up) {
         e = launch_up_swiglu_bf16_slab_routed(g, L.tile_rows / 32, topk_idx, counts, offsets, tile_off,
                                               tile_off64, perm, inv, err, x, W1, W3, Ws1, Ws3, W2, Ws2, h, D,
-                                              F, stream);
+                                              F, stream, gu);
         if (e == hipSuccess) e = mark(2);
     } else if (dtype == MOE_BF16 && L.small_tiles) {
-        e = launch_up_swiglu_bf16_slab(g, L.tile_rows / 32, x, W1, W3, Ws1, Ws3, h, D, F, stream);
+        e = launch_up_swiglu_bf16_slab(g, L.tile_rows / 32, x, W1, W3, Ws1, Ws3, h, D, F, stream, gu);
         if (e == hipSuccess) e = mark(2);
     } else if (dtype == MOE_BF16) {
-        e = launch_up_swiglu_bf16(g, x, W1, W3, Ws1, Ws3, h, D, F, stream);
+        e = gu ? launch_up_swiglu_gu_bf16(g, x, W1, W3, Ws1, Ws3, h, gu, D, F, stream)
+               : launch_up_swiglu_bf16(g, x, W1, W3, Ws1, Ws3, h, D, F, stream);
         if (e == hipSuccess) e = mark(2);
     } else {
         e = launch_up_swiglu_f32(g, (const float*)x, (const float*)W1, (const float*)W3,
@@ -304,6 +306,23 @@ moe_status moe_ffn_forward_routed(const void* x, const void* gate_w, const void*
     return moe_ffn_forward_routed_timed(x, gate_w, W1, W3, W2, Ws1, Ws3, Ws2, y, topk_idx, topk_w, T,
                                         D, F, E, k, dtype, variant, workspace, ws_bytes, stream,
                                         nullptr);
+}
+
+moe_status moe_ffn_forward_save_gu(const void* x, const int32_t* topk_idx, const float* topk_w,
+                                   const void* W1, const void* W3, const void* W2, const void* Ws1,
+                                   const void* Ws3, const void* Ws2, void* y, void* gu, int64_t T,
+                                   int D, int F, int E, int k, moe_dtype dtype, moe_variant variant,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+    // the gate and up products exist as bf16 tiles only on the unfused bf16 path
+    if (dtype != MOE_BF16 || variant != MOE_VARIANT_UNFUSED) {
+        moe_ws_layout L;
+        const int nsh = (Ws1 != nullptr) + (Ws3 != nullptr) + (Ws2 != nullptr);
+        const moe_status st = make_layout(T, D, F, E, k, nsh == 3, dtype, variant, &L);
+        return st != MOE_OK ? st : MOE_ERR_UNSUPPORTED;
+    }
+    if (T > 0 && !gu) return MOE_ERR_INVALID_ARG;
+    return forward_impl(x, nullptr, topk_idx, topk_w, W1, W3, W2, Ws1, Ws3, Ws2, y, T, D, F, E, k,
+                        dtype, variant, workspace, ws_bytes, stream, nullptr, gu);
 }
 
 moe_status moe_ffn_forward(const void* x, const int32_t* topk_idx, const float* topk_w,

@@ -46,6 +46,11 @@ constexpr int kBf16TileRows = 256;
 hipError_t launch_up_swiglu_bf16(const GroupArgs& g, const void* x, const void* W1, const void* W3,
                                  const void* Ws1, const void* Ws3, void* h, int D, int F,
                                  hipStream_t s);
+// The same, also storing each row's gate and up products gu[p] = [g | u]
+// rounded to bf16 ([R, 2F], the layout of the backward's gate/up recompute).
+hipError_t launch_up_swiglu_gu_bf16(const GroupArgs& g, const void* x, const void* W1,
+                                    const void* W3, const void* Ws1, const void* Ws3, void* h,
+                                    void* gu, int D, int F, hipStream_t s);
 // Down GEMM output: Y[p] = h[p] . W2[grp] rounded to bf16 (the routing
 // weight is applied by the combine).
 hipError_t launch_down_bf16(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
@@ -64,9 +69,10 @@ constexpr int kRouteMaxExperts = 512;
 // rb for S routed rows over E experts, shared_rows shared-expert rows (0:
 // none) and F output columns.
 int slab_row_blocks(int64_t S, int64_t shared_rows, int E, int F);
+// gu (optional, may be null): each row's [g | u] rounded to bf16, [R, 2F].
 hipError_t launch_up_swiglu_bf16_slab(const GroupArgs& g, int rb, const void* x, const void* W1,
                                       const void* W3, const void* Ws1, const void* Ws3, void* h,
-                                      int D, int F, hipStream_t s);
+                                      int D, int F, hipStream_t s, void* gu = nullptr);
 // The same with the counting sort of the permute done inside the kernel
 // (S = T*k <= kPermuteSingleMax, E <= kRouteMaxExperts): reads the expert id of
 // every slot and writes counts, offsets, tile_off (tile rows 32 rb),
@@ -80,7 +86,8 @@ hipError_t launch_up_swiglu_bf16_slab_routed(const GroupArgs& g, int rb, const i
                                              int32_t* err, const void* x, const void* W1,
                                              const void* W3, const void* Ws1, const void* Ws3,
                                              const void* W2, const void* Ws2,
-                                             void* h, int D, int F, hipStream_t s);
+                                             void* h, int D, int F, hipStream_t s,
+                                             void* gu = nullptr);
 hipError_t launch_down_bf16_small(const GroupArgs& g, const void* h, const void* W2, const void* Ws2,
                                   void* Y, int D, int F, hipStream_t s);
 

@@ -180,6 +180,34 @@ moe_status moe_ffn_forward_timed(const void *x, const int32_t *topk_idx, const f
                                  hipEvent_t events[5]);
 
 /*
+ * moe_ffn_forward that also keeps, for the backward, each sorted row's gate
+ * and up products: the "Triton MoE Kernels & Memory Checkpointing" autograd
+ * contract (Part A, section 8) recomputes g = v W1 and u = v W3 in the
+ * backward; keeping them instead trades their storage for that recompute
+ * (moe_ffn_backward_cached takes them back).
+ *
+ *   gu  [R, 2F] dtype, caller-owned, 16-byte aligned, R = T*k (+ T with a
+ *       shared expert): row p is sorted row p of the layer (the rows in the
+ *       order of moe_expert_permute's perm, then the T shared rows), g in
+ *       columns 0..F-1, u in F..2F-1, each the fp32 product rounded once to
+ *       bf16 -- bitwise what the backward's own recompute produces.  Rows of
+ *       invalid slots (positions >= offsets[E] among the routed rows) are not
+ *       written.
+ *
+ * y is bitwise the y of moe_ffn_forward.  Only bf16 with
+ * MOE_VARIANT_UNFUSED keeps g and u (the fused variant never stores the
+ * up product, and the fp32 path has no bf16 rows): other dtypes or variants
+ * return MOE_ERR_UNSUPPORTED.  Other arguments and errors as
+ * moe_ffn_forward; gu NULL with T > 0 is MOE_ERR_INVALID_ARG.
+ */
+moe_status moe_ffn_forward_save_gu(const void *x, const int32_t *topk_idx, const float *topk_w,
+                                   const void *W1, const void *W3, const void *W2,
+                                   const void *Ws1, const void *Ws3, const void *Ws2,
+                                   void *y, void *gu, int64_t T, int D, int F, int E, int k,
+                                   moe_dtype dtype, moe_variant variant,
+                                   void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * moe_ffn_forward without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  The library keeps one workspace of
@@ -440,6 +468,41 @@ moe_status moe_ffn_backward_timed(const void *x, const int32_t *topk_idx, const 
                                   int64_t T, int D, int F, int E, int k, moe_dtype dtype,
                                   void *workspace, size_t ws_bytes, hipStream_t stream,
                                   hipEvent_t events[9]);
+
+/*
+ * moe_ffn_backward with the gate and up products taken from the forward
+ * instead of recomputed ("Triton MoE Kernels & Memory Checkpointing",
+ * Part A section 8: the recompute-versus-keep trade-off of the autograd
+ * contract): gu is the [R, 2F] array moe_ffn_forward_save_gu wrote for the
+ * same x, topk_idx, W1 and W3 (caller-owned, 16-byte aligned, read only).
+ * The gate/up recompute launch is skipped; every other step is that of
+ * moe_ffn_backward, and since gu holds bitwise what the recompute would
+ * store, every gradient is bitwise the one moe_ffn_backward returns.  The
+ * workspace is moe_ffn_backward_workspace_size() bytes, as for
+ * moe_ffn_backward (its gate/up slot stays unused).  bf16 only (other
+ * dtypes return MOE_ERR_UNSUPPORTED); gu NULL with T > 0 is
+ * MOE_ERR_INVALID_ARG; other errors as moe_ffn_backward.
+ */
+moe_status moe_ffn_backward_cached(const void *x, const int32_t *topk_idx, const float *topk_w,
+                                   const void *W1, const void *W3, const void *W2,
+                                   const void *Ws1, const void *Ws3, const void *Ws2,
+                                   const void *gu, const void *dy, void *dx, float *dW1,
+                                   float *dW3, float *dW2, float *dWs1, float *dWs3, float *dWs2,
+                                   float *dtopk_w, int64_t T, int D, int F, int E, int k,
+                                   moe_dtype dtype, void *workspace, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* moe_ffn_backward_cached plus the nine events of moe_ffn_backward_timed
+ * (events[2] and [3] back to back: no recompute launch between them). */
+moe_status moe_ffn_backward_cached_timed(const void *x, const int32_t *topk_idx,
+                                         const float *topk_w, const void *W1, const void *W3,
+                                         const void *W2, const void *Ws1, const void *Ws3,
+                                         const void *Ws2, const void *gu, const void *dy,
+                                         void *dx, float *dW1, float *dW3, float *dW2,
+                                         float *dWs1, float *dWs3, float *dWs2, float *dtopk_w,
+                                         int64_t T, int D, int F, int E, int k, moe_dtype dtype,
+                                         void *workspace, size_t ws_bytes, hipStream_t stream,
+                                         hipEvent_t events[9]);
 
 #ifdef __cplusplus
 }
