@@ -334,6 +334,102 @@ def run_backward(args):
     print(json.dumps(res), flush=True)
 
 
+def run_train_step(args):
+    """The recompute-versus-keep trade-off of the gate and up products
+    ("Triton MoE Kernels & Memory Checkpointing", Part A section 8), timed on
+    one workload: a training step's forward and backward either as
+    moe_ffn_forward + moe_ffn_backward (g and u recomputed by the backward)
+    or as moe_ffn_forward_save_gu + moe_ffn_backward_cached (g and u kept
+    from the forward, R x 2F values of the storage dtype).  Each of the four
+    calls is timed alone over the rotated input sets (host clock between two
+    synchronisations), and the whole step both ways; one JSON line."""
+    import numpy as np
+    import torch
+
+    import grouped_gemm_permute_amd as gg
+    import moe_inputs
+
+    w = moe_inputs.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        raise SystemExit("--train-step: the kept gate/up products exist on the bf16 path only")
+    log(f"train-step workload {w.name}: drawing inputs")
+    inp = moe_inputs.add_output_grad(moe_inputs.make_inputs(args.workload))
+    torch.cuda.set_device(0)
+
+    def dev(name):
+        return torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+
+    base = {n: dev(n) for n in ("x", "W1", "W3", "W2", "dy")}
+    if w.shared:
+        base.update({n: dev(n) for n in ("Ws1", "Ws3", "Ws2")})
+    base["idx"] = torch.from_numpy(inp["topk_idx"]).cuda()
+    base["w"] = torch.from_numpy(inp["topk_w"]).cuda()
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    R = max(2, math.ceil(args.rotate_bytes / set_bytes))
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(R - 1)]
+    rows = w.T * w.k + (w.T if w.shared else 0)
+    gus = [torch.empty((rows, 2 * w.F), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    fws = gg.alloc_workspace(w.T, w.D, w.F, w.E, w.k, w.shared, torch.bfloat16)
+    lay = gg.backward_workspace_layout(w.T, w.D, w.F, w.E, w.k, w.shared, torch.bfloat16)
+    bws = torch.empty(lay["total"], dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.T, w.D), dtype=torch.bfloat16, device="cuda")
+    out = None
+    log(f"{R} rotated input sets of {set_bytes / 1e6:.1f} MB, kept g/u {rows * 2 * w.F * 2 / 1e6:.1f} MB each")
+
+    def args_of(s):
+        sh = (s["Ws1"], s["Ws3"], s["Ws2"]) if w.shared else None
+        return (s["x"], s["idx"], s["w"], s["W1"], s["W3"], s["W2"], sh)
+
+    def fwd(i):
+        gg.forward(*args_of(sets[i % R]), y=y, workspace=fws)
+
+    def fwd_keep(i):
+        gg.forward_save_gu(*args_of(sets[i % R]), y=y, gu=gus[i % R], workspace=fws)
+
+    def bwd(i, gu=False):
+        nonlocal out
+        s = sets[i % R]
+        out = gg.backward(*args_of(s), s["dy"], out=out, workspace=bws, gu=gus[i % R] if gu else None)
+
+    calls = {
+        "forward": fwd,
+        "forward_save_gu": fwd_keep,
+        "backward_recompute": lambda i: bwd(i),
+        "backward_cached": lambda i: bwd(i, gu=True),
+        "step_recompute": lambda i: (fwd(i), bwd(i)),
+        "step_keep": lambda i: (fwd_keep(i), bwd(i, gu=True)),
+    }
+    for i in range(R):                   # every set's g/u, for the cached calls
+        fwd_keep(i)
+    ms = {}
+    for name, f in calls.items():
+        for i in range(args.warmup):
+            f(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            f(i)
+        torch.cuda.synchronize()
+        ms[name] = (time.perf_counter() - t0) * 1e3 / args.steps
+        log(f"{name}: {ms[name]:.4f} ms per call")
+    flop = 22 * w.D * w.F * rows          # 6 D F forward + 16 D F backward per row
+    flop_keep = 18 * w.D * w.F * rows     # the backward's 4 D F gate/up recompute left out
+    res = {
+        "metric": "MoE FFN training step ms, gate/up recomputed vs kept", "unit": "ms",
+        "value": round(ms["step_keep"], 5), "higher_is_better": False, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "F": w.F, "E": w.E, "k": w.k,
+                   "shared_expert": w.shared, "routing": w.routing, "rotated_sets": R},
+        "ms_per_call": {k: round(v, 5) for k, v in ms.items()},
+        "step_tflops": {"recompute": round(flop / (ms["step_recompute"] * 1e-3) / 1e12, 2),
+                        "keep": round(flop_keep / (ms["step_keep"] * 1e-3) / 1e12, 2),
+                        "note": "FLOP executed per row: 22 D F recomputing, 18 D F keeping"},
+        "kept_bytes": rows * 2 * w.F * 2,
+        "saving_ms": round(ms["step_recompute"] - ms["step_keep"], 5),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def time_forward(w, variant, steps, warmup, rotate_bytes=512e6):
     """Wall time per forward call of workload w (inputs rotated as in the
     main bench), in ms."""
@@ -747,6 +843,9 @@ def main():
                     help="skip the same-run small-chunk (512-token) record")
     ap.add_argument("--backward", action="store_true",
                     help="time moe_ffn_backward (dx, weight gradients, dtopk_w) instead of the forward")
+    ap.add_argument("--train-step", action="store_true",
+                    help="time a training step's forward and backward with the gate/up products "
+                         "recomputed by the backward or kept from the forward (bf16 workloads)")
     ap.add_argument("--routed", action="store_true",
                     help="time moe_ffn_forward_routed: the top-k router (x @ gate_w, top-k, softmax) "
                          "feeding the permute, then the same forward")
@@ -772,6 +871,9 @@ def main():
         sys.exit(2)
     if args.backward:
         run_backward(args)
+        return
+    if args.train_step:
+        run_train_step(args)
         return
     if args.sweep:
         run_sweep(args)

@@ -124,3 +124,20 @@ def test_backward_gradient_buffers():
 def test_permute_index_dtype():
     with pytest.raises(TypeError, match="topk_idx"):
         gg.expert_permute(torch.zeros((T, K), dtype=torch.int64), E)
+
+
+def test_kept_gate_up_shape_and_dtype():
+    """forward_save_gu's gu and backward's gu are [T*k + T (shared), 2F] in
+    x's dtype: a smaller array would let the kernels write or read past it."""
+    a = layer()
+    R = T * K + T
+    args = (a["x"], a["idx"], a["w"], a["W1"], a["W3"], a["W2"], a["shared"])
+    with pytest.raises(ValueError, match="gu"):
+        gg.forward_save_gu(*args, gu=torch.zeros((R - 1, 2 * F), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="gu"):
+        gg.forward_save_gu(*args, gu=torch.zeros((R, F), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="gu"):
+        gg.forward_save_gu(*args, gu=torch.zeros((R, 2 * F), dtype=torch.float32))
+    dy = torch.zeros((T, D), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="gu"):
+        gg.backward(*args, dy, gu=torch.zeros((T * K, 2 * F), dtype=torch.bfloat16))
