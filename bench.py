@@ -334,7 +334,7 @@ def run_backward(args):
     print(json.dumps(res), flush=True)
 
 
-def run_train_step(args):
+def train_step_record(workload, steps, warmup, rotate_bytes):
     """The recompute-versus-keep trade-off of the gate and up products
     ("Triton MoE Kernels & Memory Checkpointing", Part A section 8), timed on
     one workload: a training step's forward and backward either as
@@ -349,11 +349,11 @@ def run_train_step(args):
     import grouped_gemm_permute_amd as gg
     import moe_inputs
 
-    w = moe_inputs.WORKLOADS[args.workload]
+    w = moe_inputs.WORKLOADS[workload]
     if w.dtype != "bf16":
         raise SystemExit("--train-step: the kept gate/up products exist on the bf16 path only")
     log(f"train-step workload {w.name}: drawing inputs")
-    inp = moe_inputs.add_output_grad(moe_inputs.make_inputs(args.workload))
+    inp = moe_inputs.add_output_grad(moe_inputs.make_inputs(workload))
     torch.cuda.set_device(0)
 
     def dev(name):
@@ -365,7 +365,7 @@ def run_train_step(args):
     base["idx"] = torch.from_numpy(inp["topk_idx"]).cuda()
     base["w"] = torch.from_numpy(inp["topk_w"]).cuda()
     set_bytes = sum(t.numel() * t.element_size() for t in base.values())
-    R = max(2, math.ceil(args.rotate_bytes / set_bytes))
+    R = max(2, math.ceil(rotate_bytes / set_bytes))
     sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(R - 1)]
     rows = w.T * w.k + (w.T if w.shared else 0)
     gus = [torch.empty((rows, 2 * w.F), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
@@ -403,21 +403,21 @@ def run_train_step(args):
         fwd_keep(i)
     ms = {}
     for name, f in calls.items():
-        for i in range(args.warmup):
+        for i in range(warmup):
             f(i)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             f(i)
         torch.cuda.synchronize()
-        ms[name] = (time.perf_counter() - t0) * 1e3 / args.steps
+        ms[name] = (time.perf_counter() - t0) * 1e3 / steps
         log(f"{name}: {ms[name]:.4f} ms per call")
     flop = 22 * w.D * w.F * rows          # 6 D F forward + 16 D F backward per row
     flop_keep = 18 * w.D * w.F * rows     # the backward's 4 D F gate/up recompute left out
     res = {
         "metric": "MoE FFN training step ms, gate/up recomputed vs kept", "unit": "ms",
         "value": round(ms["step_keep"], 5), "higher_is_better": False, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "dtype": w.dtype, "data": "synthetic",
+        "steps": steps, "warmup": warmup, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "D": w.D, "F": w.F, "E": w.E, "k": w.k,
                    "shared_expert": w.shared, "routing": w.routing, "rotated_sets": R},
         "ms_per_call": {k: round(v, 5) for k, v in ms.items()},
@@ -427,7 +427,14 @@ def run_train_step(args):
         "kept_bytes": rows * 2 * w.F * 2,
         "saving_ms": round(ms["step_recompute"] - ms["step_keep"], 5),
     }
-    print(json.dumps(res), flush=True)
+    del sets, gus, fws, bws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_train_step(args):
+    print(json.dumps(train_step_record(args.workload, args.steps, args.warmup, args.rotate_bytes)),
+          flush=True)
 
 
 def time_forward(w, variant, steps, warmup, rotate_bytes=512e6):
@@ -843,6 +850,9 @@ def main():
                     help="skip the same-run small-chunk (512-token) record")
     ap.add_argument("--backward", action="store_true",
                     help="time moe_ffn_backward (dx, weight gradients, dtopk_w) instead of the forward")
+    ap.add_argument("--no-train-step", action="store_true",
+                    help="skip the same-run training-step record (forward + backward, gate/up "
+                         "recomputed vs kept)")
     ap.add_argument("--train-step", action="store_true",
                     help="time a training step's forward and backward with the gate/up products "
                          "recomputed by the backward or kept from the forward (bf16 workloads)")
@@ -897,6 +907,13 @@ def main():
         log("same-run small-chunk record")
         small = small_chunk_record(args)
 
+    train = None
+    if args.workload == 2 and args.variant == "unfused" and not args.routed and not args.no_train_step:
+        log("same-run training-step record (gate/up recomputed vs kept)")
+        train = train_step_record(args.workload, args.steps, args.warmup, args.rotate_bytes)
+        train = {k: train[k] for k in ("ms_per_call", "step_tflops", "kept_bytes", "saving_ms",
+                                       "steps", "warmup")}
+
     cpu = None
     if args.cpu_seconds > 0 and not args.routed:
         log("timing the CPU oracle baseline")
@@ -926,6 +943,7 @@ def main():
         "input_sha256": moe_inputs.input_digest(inp),
         "roofline": roof,
         "small_chunk": small,
+        "train_step": train,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

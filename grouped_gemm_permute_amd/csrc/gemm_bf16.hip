@@ -22,6 +22,9 @@
 //
 //  gate_up:    gu[p] = [g | u] rounded to bf16 (g in columns 0..F-1, u in
 //              F..2F-1): the up GEMM with the activation left out.
+//  up_gu:      up_swiglu that also stores gate_up's [g | u] (the forward
+//              that keeps the gate and up products for the backward instead
+//              of their recompute; the same K loop, two epilogue passes).
 //  dh:         dh' = dy[tok(p)] . W2t[grp] with W2t[grp] = W2[grp]^T ([D, F]),
 //              then per element, with g, u read back from gu and w the row's
 //              routing weight (1 on shared rows):

@@ -4,7 +4,9 @@
 // (x . W3)) on the rows of each group), shaped for the regime where every
 // expert sees at most a few hundred rows and streaming the weights is the
 // cost (the "small chunks" that "Triton MoE Kernels & Memory Checkpointing",
-// Part A sections 2 and 6.1, calls the pathological regime).
+// Part A sections 2 and 6.1, calls the pathological regime).  Given a gu
+// array it also stores each row's [g | u] rounded to bf16 beside h, for the
+// forward that keeps the gate and up products for the backward.
 //
 // Every byte a workgroup stages passes through its CU's memory pipe, which
 // moves a few tens of bytes per clock; the kernel is bound by the total
