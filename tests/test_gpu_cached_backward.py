@@ -110,6 +110,18 @@ def test_cached_backward_invalid_ids():
     assert torch.equal(_rows_written(gu, inp), _rows_written(gu_re, inp))
     _assert_same_grads(g_re, g_ca, "invalid ids")
     assert float(g_ca["dtopk_w"][10, 1]) == 0.0 and float(g_ca["dtopk_w"][11, 0]) == 0.0
+    # T = 0: nothing kept, weight gradients come back as zeros
+    import grouped_gemm_permute_amd as gg
+    inp0 = moe_inputs.add_output_grad(make_case(0, 64, 128, 3, 2, True, "bf16", seed=9))
+    d0 = device_inputs(inp0)
+    args0 = (d0["x"], d0["topk_idx"], d0["topk_w"], d0["W1"], d0["W3"], d0["W2"], d0["shared"])
+    say("cached backward T0")
+    y0, gu0 = gg.forward_save_gu(*args0)
+    assert y0.shape == (0, 64) and gu0.shape == (0, 256)
+    g0 = gg.backward(*args0, dev(inp0, "dy", "bf16"), gu=gu0)
+    torch.cuda.synchronize()
+    for n in ("dW1", "dW3", "dW2", "dWs1", "dWs3", "dWs2"):
+        assert torch.count_nonzero(g0[n]).item() == 0, n
 
 
 def test_cached_backward_step_workload():
